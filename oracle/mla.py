@@ -1,0 +1,186 @@
+"""Reference decode step of Multi-head Latent Attention — TEST INFRASTRUCTURE ONLY.
+
+Plain numpy in float64. The oracle does NOT use the absorption trick: it rebuilds every past
+token's per-head content key and value from the cached latent and runs ordinary multi-head
+attention with the decoupled rotary part, exactly as the pages write the method out:
+
+  [Scratch] = "DeepSeek-V2 from Scratch: Multi-head Latent Attention and DeepSeekMoE"
+              (prathamp.com), sections 1-7;
+  [Visual]  = "DeepSeek-V2" (sghael visual-learn), "Why position needs separate handling";
+  [Summary] = noblerworks summary of the DeepSeek-V2 paper, "The matrix-absorption trick".
+
+Where the pages are silent the oracle takes these readings (each is listed with its reason in
+the design notes of the repository):
+  * rotary embedding: consecutive pairs (x_2m, x_2m+1) rotated by pos * base^(-2m/d_r), base
+    10000; applied to every head's d_h^R slice of the rotary query and to the shared rotary key;
+  * positions are 0-based, cache row j holds position j, the current token sits at T_b - 1 and
+    attends to itself (the pages' sums run to j = t inclusive);
+  * head i owns row block i of W^UQ, W^QR, W^UK, W^UV and column block i of W^O;
+  * the attention weight carries a head index (it depends on the head's query);
+  * the softmax scale is 1/sqrt(d_h + d_h^R) in every formulation, including the absorbed one;
+  * the appended row is rounded to the storage type before attention reads it.
+
+Pins (tests/test_oracle_pins.py): the absorbed formulation below agrees to 1e-10; a special case
+reduces to torch's scaled-dot-product attention; T = 1 closed form; hand-derived tiny case
+(tests/golden); rotary invariants and a complex-number formulation; decode step by step equals
+causal attention over the whole prefix; the pages' printed softmax example.
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+from .encodings import store_rows, load_rows
+
+
+@dataclass(frozen=True)
+class OracleDims:
+    d: int
+    n_h: int
+    d_h: int
+    d_c: int
+    d_cq: int
+    d_r: int
+    rope_base: float = 10000.0
+
+    @classmethod
+    def of(cls, dims) -> "OracleDims":
+        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base))
+
+
+def softmax(z, axis=-1):
+    """Softmax with the maximum subtracted first (same value, no overflow)."""
+    z = np.asarray(z, dtype=np.float64)
+    m = np.max(z, axis=axis, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def rope(x, pos, base=10000.0):
+    """Rotary embedding of the last axis of x (even length) at integer position `pos`.
+
+    [Scratch] section 3.1 defines RoPE only as a position-dependent rotation whose query-key dot
+    product depends on the position difference; the pair layout and frequencies are the
+    textbook ones (see the module docstring)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % 2 == 0
+    m = np.arange(n // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * m / n)
+    ang = float(pos) * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def head_slices(W, dims: OracleDims):
+    """Per-head blocks of the weights, [Scratch] sections 2.2, 4.1 and 5.1-5.2.
+    Returns (W_uq[i]: d_h x d_cq, W_qr[i]: d_r x d_cq, W_uk[i]: d_h x d_c, W_uv[i]: d_h x d_c,
+    W_o[i]: d x d_h)."""
+    n, dh, dr = dims.n_h, dims.d_h, dims.d_r
+    return (W["W_uq"].reshape(n, dh, dims.d_cq),
+            W["W_qr"].reshape(n, dr, dims.d_cq),
+            W["W_uk"].reshape(n, dh, dims.d_c),
+            W["W_uv"].reshape(n, dh, dims.d_c),
+            W["W_o"].reshape(dims.d, n, dh).transpose(1, 0, 2))
+
+
+def new_token(W, h, pos, dims: OracleDims, cdtype):
+    """Query and KV pathways for the current token ([Scratch] section 6).
+
+    Returns q^C [n_h, d_h], q^R [n_h, d_r] (rotated), the cache row [c^KV ; k^R] exactly as
+    computed (float64), and the row as stored (payload, scale) and as read back (float64)."""
+    cQ = W["W_dq"] @ h                                         # c^Q = W^DQ h
+    qC = (W["W_uq"] @ cQ).reshape(dims.n_h, dims.d_h)          # q^C = W^UQ c^Q, split by head
+    qR = rope((W["W_qr"] @ cQ).reshape(dims.n_h, dims.d_r), pos, dims.rope_base)
+    cKV = W["W_dkv"] @ h                                       # c^KV = W^DKV h   (cached)
+    kR = rope(W["W_kr"] @ h, pos, dims.rope_base)             # k^R = RoPE(W^KR h) (cached)
+    row = np.concatenate([cKV, kR])                            # row layout: latent, then k^R
+    payload, scale = store_rows(row[None, :], cdtype)
+    read = load_rows(payload, cdtype, scale)[0]
+    return qC, qR, row, (payload[0], None if scale is None else scale[0]), read
+
+
+def decode_step_explicit(W, h, prefix, dims: OracleDims, cdtype, heads=None, want_u=True,
+                         chunk=4096):
+    """One decode step of one layer for one sequence, with explicit key/value reconstruction.
+
+    W: dict of float64 weights ([out, in]); h: [d] float64; prefix: [T-1, d_c + d_r] float64
+    (the stored rows of positions 0..T-2, as the attention reads them).
+    heads: optional subset of heads for the diagnostics (u needs all heads).
+    Returns dict(u [d], o [n_h, d_h], o_lat [H, d_c], lse [H], row_new, stored_new, alpha_max).
+    """
+    prefix = np.asarray(prefix, dtype=np.float64).reshape(-1, dims.d_c + dims.d_r)
+    T = prefix.shape[0] + 1
+    pos = T - 1
+    qC, qR, row, stored, read = new_token(W, h, pos, dims, cdtype)
+    rows = np.vstack([prefix, read[None, :]])                  # [T, d_c + d_r]
+    C, KR = rows[:, : dims.d_c], rows[:, dims.d_c:]
+    Wuq, Wqr, Wuk, Wuv, Wo = head_slices(W, dims)
+    heads = list(range(dims.n_h)) if heads is None else list(heads)
+    if want_u:
+        assert len(heads) == dims.n_h
+    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+
+    # pass 1: scores s[j, i] = [q^C_i ; q^R_i] . [k^C_{j,i} ; k^R_j] / sqrt(d_h + d_r)
+    S = np.empty((T, len(heads)))
+    for a in range(0, T, chunk):
+        Cc = C[a: a + chunk]
+        for n, i in enumerate(heads):
+            kC = Cc @ Wuk[i].T                                 # k^C_{j,i} = W^UK_i c_j
+            k = np.concatenate([kC, KR[a: a + chunk]], axis=1)  # k_{j,i} = [k^C_{j,i}; k^R_j]
+            q = np.concatenate([qC[i], qR[i]])                  # q_i = [q^C_i; q^R_i]
+            S[a: a + chunk, n] = (k @ q) * scale
+    alpha = softmax(S, axis=0)                                 # over the context j
+    m = S.max(axis=0)
+    lse = m + np.log(np.exp(S - m).sum(axis=0))
+
+    # pass 2: o_i = sum_j alpha_{j,i} v^C_{j,i}, v^C_{j,i} = W^UV_i c_j
+    o = np.zeros((len(heads), dims.d_h))
+    o_lat = np.zeros((len(heads), dims.d_c))
+    for a in range(0, T, chunk):
+        Cc = C[a: a + chunk]
+        for n, i in enumerate(heads):
+            vC = Cc @ Wuv[i].T
+            o[n] += alpha[a: a + chunk, n] @ vC
+            o_lat[n] += alpha[a: a + chunk, n] @ Cc            # diagnostic only
+    out = dict(o=o, o_lat=o_lat, lse=lse, row_new=row, stored_new=stored, read_new=read,
+               alpha_max=alpha.max(axis=0), score_std=float(S.std()) if T > 1 else 0.0, T=T)
+    if want_u:
+        out["u"] = W["W_o"] @ o.reshape(-1)                    # u = W^O [o_1; ...; o_nh]
+    return out
+
+
+def decode_step_absorbed(W, h, prefix, dims: OracleDims, cdtype):
+    """Second formulation, used only to pin the first: the absorbed form of [Scratch] section 5.
+
+    q~_i = (W^UK_i)^T q^C_i scores the latent directly; the attention-weighted latent is
+    up-projected afterwards by W^UV_i and then W^O_i. Different arithmetic, same exact result."""
+    prefix = np.asarray(prefix, dtype=np.float64).reshape(-1, dims.d_c + dims.d_r)
+    T = prefix.shape[0] + 1
+    qC, qR, row, stored, read = new_token(W, h, T - 1, dims, cdtype)
+    rows = np.vstack([prefix, read[None, :]])
+    C, KR = rows[:, : dims.d_c], rows[:, dims.d_c:]
+    Wuq, Wqr, Wuk, Wuv, Wo = head_slices(W, dims)
+    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    u = np.zeros(dims.d)
+    o_lat = np.zeros((dims.n_h, dims.d_c))
+    lse = np.zeros(dims.n_h)
+    for i in range(dims.n_h):
+        q_abs = Wuk[i].T @ qC[i]                               # (W^UK_i)^T q^C_i, in R^{d_c}
+        s = (C @ q_abs + KR @ qR[i]) * scale
+        a = softmax(s)
+        m = s.max()
+        lse[i] = m + np.log(np.exp(s - m).sum())
+        o_lat[i] = a @ C                                       # sum_j alpha_j c_j
+        u += Wo[i] @ (Wuv[i] @ o_lat[i])                       # W^O_i W^UV_i (sum alpha c)
+    return dict(u=u, o_lat=o_lat, lse=lse)
+
+
+def decode_batch(W, h, prefixes, dims: OracleDims, cdtype, heads=None, want_u=True):
+    """decode_step_explicit over a batch; prefixes[b] are sequence b's stored rows."""
+    return [decode_step_explicit(W, h[b], prefixes[b], dims, cdtype, heads=heads, want_u=want_u)
+            for b in range(len(prefixes))]
