@@ -1,0 +1,218 @@
+"""Benchmark: one MLA decode step (one layer) at the DeepSeek-V2 shape on one MI355X.
+
+A step is absorb_q -> rope (append) -> decode_attn -> combine -> absorb_out over one batch of
+synthetic inputs resident in HBM. Prints ONE JSON line with whole-step throughput (tokens/s),
+the latent-cache read bandwidth of the attention kernels, the roofline record of the dominant
+kernel (decode_attn) timed with HIP events on its launch stream, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Default workload: batch 64, every sequence 4096 tokens (contiguous bf16 latent cache
+[64, 4096, 576]), n_h=128, d_h=128, d_c=512, d_c'=1536, d_h^R=64, d=5120; hidden states N(0,1),
+weights N(0, 0.006). The cache is replicated `--rotate` times and the steps cycle through the
+copies so that successive steps do not find the cache in the 256 MB last-level (MALL) cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="2", help="workload key (2, 3, 4, 4f8)")
+    ap.add_argument("--splits", type=int, default=0, help="decode ranges (0 = one per CU)")
+    ap.add_argument("--rotate", type=int, default=2, help="cache copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
+    return ap.parse_args()
+
+
+def build_cache(mla, case):
+    import torch
+    cfg, dims = case.cfg, case.dims
+    if cfg.layout == "contiguous":
+        cache = mla.LatentCache.contiguous(case.B, case.t_cap, dims.row, cfg.cdtype)
+    else:
+        cache = mla.LatentCache.paged(case.num_pages, cfg.page_size, dims.row, cfg.cdtype, case.block_table)
+    if cfg.cdtype != "fp8_e4m3":
+        cache.rows.copy_(case.rows)
+    else:
+        n_rows = (case.seq_lens - 1).to(torch.int32).contiguous()
+        mla.cache_store(mla.Dims.of(dims), cache, n_rows, case.t_cap, case.rows32.contiguous(), case.t_cap)
+    return cache
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands, on whole sequences of this workload until the budget is spent."""
+    import numpy as np
+    from oracle import OracleDims, decode_step_explicit
+    W = {k: v.double().cpu().numpy() for k, v in case.weights.items()}
+    od = OracleDims.of(case.dims)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(case.B):
+        pre = case.prefix_rows(b)
+        if case.cfg.cdtype == "fp8_e4m3":
+            from oracle import e4m3_decode, quantize_rows_e4m3
+            codes, sc = quantize_rows_e4m3(pre.float().cpu().numpy())
+            pre64 = e4m3_decode(codes) * sc.astype(np.float64)[:, None]
+        else:
+            pre64 = pre.double().cpu().numpy()
+        decode_step_explicit(W, case.h[b].double().cpu().numpy(), pre64, od, case.cfg.cdtype)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    T = int(case.seq_lens[0])
+    return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {case.B} sequences (T={T} each, full decode step incl. all heads), "
+                      f"{dt:.1f} s, numpy float64 explicit K/V reconstruction"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "
+                                   "for how the path shards across GPUs"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_25_amd as mla
+    from synth import get_config, make_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mla.lib()  # fails loudly when libmla.so is missing
+    cfg = get_config(args.config)
+    dims = cfg.dims
+    case = make_case(cfg, device="cuda")
+    B = case.B
+    caches = [build_cache(mla, case) for _ in range(max(1, args.rotate))]
+    step = mla.DecodeStep(dims, B, args.splits)
+    torch.cuda.synchronize()
+    W, h, seq_lens = case.weights, case.h, case.seq_lens
+    d = step.dims
+    sigma_T = int(seq_lens.sum())
+    row_bytes = dims.row * (1 if cfg.cdtype == "fp8_e4m3" else 2) + (4 if cfg.cdtype == "fp8_e4m3" else 0)
+    cache_bytes = sigma_T * row_bytes
+    flops_attn = sigma_T * 2 * dims.n_h * (dims.row + dims.d_c)
+    wsz = {k: v.numel() * v.element_size() for k, v in case.weights.items()}
+    wq_bytes = sum(wsz[k] for k in ("W_dq", "W_uq", "W_qr", "W_dkv", "W_kr", "W_uk"))
+    wo_bytes = wsz["W_uv"] + wsz["W_o"]
+
+    def one_step(cache, ev=None):
+        if ev is not None:
+            ev[0].record()
+        mla.absorb_q(d, h, W, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+        if ev is not None:
+            ev[1].record()
+        mla.rope(d, seq_lens, step.q_pe, step.kv_new, cache)
+        if ev is not None:
+            ev[2].record()
+        mla.decode_attn(d, step.q_lat, step.q_pe, cache, seq_lens, args.splits, step.ws_d)
+        if ev is not None:
+            ev[3].record()
+        mla.combine(d, args.splits, seq_lens, step.ws_d, step.o_lat, step.lse)
+        if ev is not None:
+            ev[4].record()
+        mla.absorb_out(d, step.o_lat, W["W_uv"], W["W_o"], step.ws_o, step.u)
+        if ev is not None:
+            ev[5].record()
+
+    graphs = None
+    if args.graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in caches:
+                one_step(c)
+        torch.cuda.current_stream().wait_stream(s)
+        for c in caches:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_step(c)
+            graphs.append(g)
+
+    for i in range(args.warmup):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            one_step(caches[i % len(caches)])
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t_start = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            one_step(caches[i % len(caches)])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # decode_attn / combine launch durations, measured with events on the launch stream over the
+    # same number of eager steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        one_step(caches[i % len(caches)], evs[i])
+    torch.cuda.synchronize()
+    stage = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) * 1e-3 for k in range(5)]
+    t_dec, t_comb = stage[2], stage[3]
+
+    tok_s = B / (ms_step * 1e-3)
+    achieved = cache_bytes / t_dec / 1e9
+    out = {
+        "metric": "MLA decode latent-cache GB/s (% HBM peak) + decode tokens/s, 1 MI355X",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.cdtype == "bf16" else cfg.cdtype,
+        "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 attention shape)",
+        "config": {"workload": f"config {cfg.key}: {cfg.title}", "batch": B, "seq_len": int(seq_lens.max()),
+                   "sum_context_tokens": sigma_T, "cache_dtype": cfg.cdtype, "layout": cfg.layout,
+                   "n_h": dims.n_h, "d_c": dims.d_c, "d_r": dims.d_r, "d": dims.d,
+                   "decode_splits": args.splits or "one per CU", "cache_copies_cycled": len(caches),
+                   "hip_graph": bool(graphs)},
+        "latent_cache_gbps": cache_bytes / (t_dec + t_comb) / 1e9,
+        "latent_cache_pct_hbm_peak": 100.0 * cache_bytes / (t_dec + t_comb) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": {"absorb_q": stage[0] * 1e6, "rope_append": stage[1] * 1e6, "decode_attn": t_dec * 1e6,
+                       "combine": t_comb * 1e6, "absorb_out": stage[4] * 1e6, "step": ms_step * 1e3},
+        "weights_gbps": {"absorb_q": wq_bytes / stage[0] / 1e9, "absorb_out": wo_bytes / stage[4] / 1e9},
+        "attn_mfma_tflops": flops_attn / t_dec / 1e12,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_attn", "bytes_per_launch": cache_bytes,
+                     "per_unit": f"{row_bytes} B per cached token x {sigma_T} tokens"},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) Multi-head Latent Attention decode library (libmla.so).
+ *
+ * One decode step of one attention layer, over a cache that stores per token only the joint
+ * KV latent c^KV (d_c values) followed by the decoupled, already-rotated rotary key k^R
+ * (d_h^R values): "DeepSeek-V2 from Scratch: Multi-head Latent Attention and DeepSeekMoE",
+ * section 4.5 (what gets cached) and section 6 (the complete algorithm, boxed quantities).
+ * W^UK is absorbed into the query and W^UV into the output (same page, sections 5.1-5.3), so
+ * attention runs against the latents directly and the full keys/values are never formed.
+ *
+ * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless the comment says host. The caller owns every buffer
+ *    (inputs, outputs, workspaces); the library never allocates, frees or keeps per-call state.
+ *  - Every call only enqueues work on `stream` (may be NULL = the default stream) and returns.
+ *    Nothing synchronises. Work is ordered with the caller's other work on that stream.
+ *  - Arguments are validated on the host before anything is enqueued. On an error nothing is
+ *    launched, the call returns a non-zero mla_status and mla_last_error() describes it
+ *    (thread-local text). A failed launch returns MLA_E_HIP.
+ *  - Device-resident values (sequence lengths, block tables) are the caller's contract: lengths
+ *    must satisfy 1 <= seq_lens[b] <= capacity and block-table entries must name pages of the pool.
+ *  - Weights are row-major [out, in] so that y = W x, as the pages write them:
+ *      W_dq [d_cq, d]         W_uq [n_h*d_h, d_cq]   W_qr [n_h*d_r, d_cq]
+ *      W_dkv [d_c, d]         W_kr [d_r, d]
+ *      W_uk [n_h*d_h, d_c]    W_uv [n_h*d_h, d_c]    W_o [d, n_h*d_h]
+ *    Head i owns rows [i*d_h, (i+1)*d_h) of W_uq/W_uk/W_uv, rows [i*d_r, (i+1)*d_r) of W_qr and
+ *    columns [i*d_h, (i+1)*d_h) of W_o.
+ *  - Activations passed between calls are float32, row-major:
+ *      q_lat [B, n_h, d_c]   absorbed content query (W^UK_i)^T q^C_i
+ *      q_pe  [B, n_h, d_r]   rotary query (raw after mla_absorb_q, rotated after mla_rope)
+ *      kv_new [B, d_c + d_r] current token's [c^KV | k^R] (k^R raw, then rotated by mla_rope)
+ *      o_lat [B, n_h, d_c]   attention-weighted latent sum per head;  lse [B, n_h] natural log
+ *      u     [B, d]          layer output
+ *  - Positions are 0-based: the current token of sequence b sits at position seq_lens[b]-1,
+ *    cache row j holds position j, and attention covers rows 0..seq_lens[b]-1 inclusive.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#if defined(__GNUC__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+typedef enum {
+  MLA_F32 = 0,       /* IEEE binary32 */
+  MLA_F16 = 1,       /* IEEE binary16 */
+  MLA_BF16 = 2,      /* bfloat16 */
+  MLA_FP8_E4M3 = 3   /* OCP e4m3 (max 448, no inf) codes + one float32 scale per cached token;
+                        cache storage only */
+} mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_E_ARG = 1,          /* invalid argument (null pointer, bad size, inconsistent dims) */
+  MLA_E_UNSUPPORTED = 2,  /* valid but not implemented (dtype/dims combination) */
+  MLA_E_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
+  MLA_E_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+/* Model dimensions (the pages' notation). rope_base: rotary frequency base (10000 on the
+ * pages' configs). sm_scale <= 0 selects 1/sqrt(d_h + d_r), the scale of "DeepSeek-V2 from
+ * Scratch" section 4.4. Requirements: all dims > 0, d_r even, d_c and d_r multiples of 8. */
+typedef struct {
+  int32_t d, n_h, d_h, d_c, d_cq, d_r;
+  double rope_base;
+  float sm_scale;
+} mla_dims;
+
+/* Latent cache of one layer. Row width is d_c + d_r elements: [c^KV | k^R].
+ *  contiguous (page_size == 0): rows is [B, t_cap, d_c + d_r]; token j of sequence b at
+ *      rows + (b * t_cap + j) * (d_c + d_r).
+ *  paged (page_size > 0): rows is a pool [num_pages, page_size, d_c + d_r]; token j of sequence
+ *      b lives in page block_table[b * max_pages + j / page_size], slot j % page_size.
+ *      block_table is device int32 [B, max_pages]; unused entries may hold -1.
+ *  dtype MLA_FP8_E4M3: rows holds uint8 codes and scales holds one float32 per row with the
+ *      same indexing (scales[(b * t_cap + j)] or scales[page * page_size + slot]); value =
+ *      code * scale. scales must be NULL for the other dtypes.
+ * The struct itself is read on the host during the call; it need not outlive the call. */
+typedef struct {
+  void* rows;
+  float* scales;
+  int32_t dtype;          /* mla_dtype */
+  int32_t page_size;      /* 0 = contiguous */
+  int64_t t_cap;          /* contiguous: rows per sequence; paged: max_pages * page_size */
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t num_pages;
+} mla_cache;
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_absorb_q — query pathway with W^UK absorbed, plus the current token's KV projection.
+ * "DeepSeek-V2 from Scratch" section 4.1 (c^Q = W^DQ h, q^C = W^UQ c^Q, raw q^R = W^QR c^Q),
+ * section 2.1 (c^KV = W^DKV h), section 4.2 (raw k^R = W^KR h) and section 5.1
+ * (absorbed query q~_i = (W^UK_i)^T q^C_i, one matrix-vector product per head).
+ *   h: [B, d] in `wdtype`; weights in `wdtype` (F32, F16 or BF16).
+ *   workspace: device scratch of at least mla_absorb_q_workspace_bytes(dims, B) bytes.
+ *   Outputs (float32): q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] (NOT yet rotated),
+ *   kv_new [B, d_c + d_r] (k^R part NOT yet rotated). */
+MLA_API size_t mla_absorb_q_workspace_bytes(const mla_dims* dims, int32_t B);
+MLA_API mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h,
+                        const void* W_dq, const void* W_uq, const void* W_qr, const void* W_uk,
+                        const void* W_dkv, const void* W_kr, void* workspace, size_t ws_bytes,
+                        float* q_lat, float* q_pe, float* kv_new, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_rope — decoupled rotary embedding and cache append.
+ * "DeepSeek-V2 from Scratch" section 3.1 (a position-dependent rotation whose query-key dot
+ * product depends only on the offset), sections 4.1-4.2 (q^R per head, one k^R shared by all
+ * heads) and section 4.5 (k^R is cached already rotated). Pairs (x[2m], x[2m+1]) are rotated by
+ * angle pos * rope_base^(-2m/d_r), computed in float64.
+ *   seq_lens: device int32 [B]; pos_b = seq_lens[b] - 1.
+ *   q_pe [B, n_h, d_r] and the k^R part of kv_new [B, d_c + d_r] are rotated IN PLACE.
+ *   cache: if non-NULL, row [c^KV | k^R] of each sequence is written to slot pos_b, rounded to
+ *   the cache dtype (RNE; fp8: per-token scale amax/448 and saturating RNE codes). */
+MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, float* q_pe,
+                    float* kv_new, const mla_cache* cache, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_decode_attn — attention of the absorbed query against the cached latents.
+ * "DeepSeek-V2 from Scratch" section 4.4 (score = q^C.k^C + q^R.k^R over sqrt(d_h + d_r)),
+ * section 5.1 (q^C.k^C = q~.c^KV) and section 5.3 (steps 2-3: dot with every cached latent,
+ * softmax-weighted sum of latents). Per head i and cached row j:
+ *     s_ij = (q_lat_i . c_j + q_pe_i . k^R_j) * sm_scale
+ * and the result is the softmax-weighted latent sum plus its log-sum-exp.
+ * The batch's tokens (sum of seq_lens) are cut into `num_splits` contiguous ranges of equal
+ * length (0 = one per compute unit; at most 1024); each range is one workgroup, and a sequence
+ * is split where ranges cut it. Each (range, sequence) piece writes a partial result into the workspace;
+ * mla_combine merges them. At most num_splits + B - 1 pieces exist.
+ *   q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] (rotated): float32.
+ *   seq_lens: device int32 [B] (including the current token, already appended).
+ *   workspace: at least mla_decode_workspace_bytes(dims, B, num_splits) bytes. */
+MLA_API size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t num_splits);
+MLA_API mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, const float* q_pe,
+                           const mla_cache* cache, const int32_t* seq_lens, int32_t num_splits,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_combine — merge the split-sequence partial results of mla_decode_attn.
+ * Regroups the softmax sum of "DeepSeek-V2 from Scratch" section 4.4 over the pieces of each
+ * sequence: with piece lse_s and normalised partial o_s, M = max_s lse_s, w_s = exp(lse_s - M),
+ *     o_lat = sum_s w_s o_s / sum_s w_s,   lse = M + log(sum_s w_s).
+ * Deterministic (fixed order, no atomics). Must be called with the same dims, B, num_splits,
+ * seq_lens and workspace as the preceding mla_decode_attn.
+ *   Outputs: o_lat [B, n_h, d_c] float32, lse [B, n_h] float32 (lse may be NULL). */
+MLA_API mla_status mla_combine(const mla_dims* dims, int32_t B, int32_t num_splits, const int32_t* seq_lens,
+                       const void* workspace, size_t ws_bytes, float* o_lat, float* lse,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_absorb_out — value up-projection after the weighted sum, then the output projection.
+ * "DeepSeek-V2 from Scratch" section 5.2 (o_i = W^UV_i sum_j a_j c_j) and sections 1/6
+ * (u = W^O [o_1; ...; o_nh]), applied in that two-step order.
+ *   o_lat [B, n_h, d_c] float32; W_uv, W_o in `wdtype`; u [B, d] float32.
+ *   workspace: at least mla_absorb_out_workspace_bytes(dims, B) bytes. */
+MLA_API size_t mla_absorb_out_workspace_bytes(const mla_dims* dims, int32_t B);
+MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
+                          const void* W_uv, const void* W_o, void* workspace, size_t ws_bytes,
+                          float* u, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_cache_store — write given rows into a cache (prefix fill; not part of a decode step).
+ * Rows of sequence b, j < n_rows[b], are read from src + (b * src_stride + j) * (d_c + d_r)
+ * (float32) and stored at position j exactly as mla_rope stores its appended row (same
+ * rounding / same fp8 scale rule). n_rows: device int32 [B]; n_rows[b] <= capacity.
+ * max_rows (host) bounds every n_rows[b] and sizes the launch. */
+MLA_API mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t B,
+                           const int32_t* n_rows, int32_t max_rows, const float* src,
+                           int64_t src_stride, hipStream_t stream);
+
+/* Status text, and the last error message of the calling thread ("" if none). */
+MLA_API const char* mla_status_str(mla_status s);
+MLA_API const char* mla_last_error(void);
+/* Library version string (host). */
+MLA_API const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

@@ -1,0 +1,10 @@
+"""MI355X-native Multi-head Latent Attention decode over a latent KV cache.
+
+The compute lives in libmla.so (HIP kernels for gfx950 behind the C ABI of include/mla.h);
+this package is its Python binding.
+"""
+from .binding import (  # noqa: F401
+    BF16, F16, F32, FP8_E4M3, DecodeStep, Dims, LatentCache, MLAError, absorb_out, absorb_out_workspace_bytes,
+    absorb_q, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib, rope,
+    version,
+)

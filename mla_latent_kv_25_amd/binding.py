@@ -1,0 +1,238 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Each function here has the name of a C entry point of include/mla.h (without the `mla_` prefix)
+and does nothing but check tensor placement/dtype/contiguity, pass raw pointers and the current
+HIP stream, and raise MLAError on a non-zero status. Every step of the computation runs in the
+library's kernels; there is no fallback. PyTorch is used only for device memory and streams.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+STORAGE_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "fp8_e4m3": FP8_E4M3}
+
+
+class MLAError(RuntimeError):
+    pass
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_r", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("sm_scale", ctypes.c_float)]
+
+    @classmethod
+    def of(cls, dims, sm_scale: float = 0.0) -> "Dims":
+        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base), sm_scale)
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("t_cap", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmla.so once. Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or `python mla_latent_kv_25_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, ST = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    D, C = ctypes.POINTER(Dims), ctypes.POINTER(CCache)
+    sig = {
+        "mla_absorb_q_workspace_bytes": (SZ, [D, I32]),
+        "mla_absorb_q": (I32, [D, I32, I32, P, P, P, P, P, P, P, P, SZ, P, P, P, ST]),
+        "mla_rope": (I32, [D, I32, P, P, P, C, ST]),
+        "mla_decode_workspace_bytes": (SZ, [D, I32, I32]),
+        "mla_decode_attn": (I32, [D, I32, P, P, C, P, I32, P, SZ, ST]),
+        "mla_combine": (I32, [D, I32, I32, P, P, SZ, P, P, ST]),
+        "mla_absorb_out_workspace_bytes": (SZ, [D, I32]),
+        "mla_absorb_out": (I32, [D, I32, I32, P, P, P, P, SZ, P, ST]),
+        "mla_cache_store": (I32, [D, C, I32, P, I32, P, I64, ST]),
+        "mla_status_str": (ctypes.c_char_p, [I32]),
+        "mla_last_error": (ctypes.c_char_p, []),
+        "mla_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_decode_workspace_bytes",
+           "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
+           "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise MLAError(f"{L.mla_status_str(status).decode()}: {L.mla_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MLAError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MLAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MLAError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class LatentCache:
+    """Device buffers of one layer's latent cache (see mla_cache in include/mla.h)."""
+    rows: torch.Tensor                       # [B, t_cap, row] or [P, page, row]; uint8 codes for fp8
+    dtype: str                               # "f32" | "f16" | "bf16" | "fp8_e4m3"
+    t_cap: int
+    scales: Optional[torch.Tensor] = None    # fp8: float32 per row
+    block_table: Optional[torch.Tensor] = None
+    page_size: int = 0
+
+    @classmethod
+    def contiguous(cls, B, t_cap, row, dtype, device="cuda"):
+        if dtype == "fp8_e4m3":
+            return cls(torch.zeros((B, t_cap, row), dtype=torch.uint8, device=device), dtype, t_cap,
+                       scales=torch.ones((B, t_cap), dtype=torch.float32, device=device))
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+        return cls(torch.zeros((B, t_cap, row), dtype=tdt, device=device), dtype, t_cap)
+
+    @classmethod
+    def paged(cls, num_pages, page_size, row, dtype, block_table, device="cuda"):
+        max_pages = int(block_table.shape[1])
+        if dtype == "fp8_e4m3":
+            return cls(torch.zeros((num_pages, page_size, row), dtype=torch.uint8, device=device), dtype,
+                       max_pages * page_size, scales=torch.ones((num_pages, page_size), dtype=torch.float32,
+                                                               device=device),
+                       block_table=block_table, page_size=page_size)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+        return cls(torch.zeros((num_pages, page_size, row), dtype=tdt, device=device), dtype,
+                   max_pages * page_size, block_table=block_table, page_size=page_size)
+
+    def c(self) -> CCache:
+        bt = self.block_table
+        return CCache(_ptr(self.rows, name="cache rows"), _ptr(self.scales, torch.float32, "cache scales"),
+                      STORAGE_CODE[self.dtype], self.page_size, self.t_cap,
+                      _ptr(bt, torch.int32, "block_table") if bt is not None else None,
+                      int(bt.shape[1]) if bt is not None else 0,
+                      int(self.rows.shape[0]) if self.page_size else 0)
+
+
+# ------------------------------------------------------------------------------------------------
+def absorb_q_workspace_bytes(dims: Dims, B: int) -> int:
+    return lib().mla_absorb_q_workspace_bytes(ctypes.byref(dims), B)
+
+
+def decode_workspace_bytes(dims: Dims, B: int, num_splits: int) -> int:
+    return lib().mla_decode_workspace_bytes(ctypes.byref(dims), B, num_splits)
+
+
+def absorb_out_workspace_bytes(dims: Dims, B: int) -> int:
+    return lib().mla_absorb_out_workspace_bytes(ctypes.byref(dims), B)
+
+
+def absorb_q(dims: Dims, h, W, workspace, q_lat, q_pe, kv_new):
+    """W: dict with W_dq, W_uq, W_qr, W_uk, W_dkv, W_kr (same dtype as h)."""
+    wdt = DTYPE_CODE[h.dtype]
+    _check(lib().mla_absorb_q(ctypes.byref(dims), h.shape[0], wdt, _ptr(h, name="h"),
+                              *[_ptr(W[k], h.dtype, k) for k in ("W_dq", "W_uq", "W_qr", "W_uk", "W_dkv", "W_kr")],
+                              _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                              _ptr(q_lat, torch.float32, "q_lat"), _ptr(q_pe, torch.float32, "q_pe"),
+                              _ptr(kv_new, torch.float32, "kv_new"), _stream()))
+
+
+def rope(dims: Dims, seq_lens, q_pe, kv_new, cache: Optional[LatentCache] = None):
+    cc = cache.c() if cache is not None else None
+    _check(lib().mla_rope(ctypes.byref(dims), seq_lens.shape[0], _ptr(seq_lens, torch.int32, "seq_lens"),
+                          _ptr(q_pe, torch.float32, "q_pe"), _ptr(kv_new, torch.float32, "kv_new"),
+                          ctypes.byref(cc) if cc is not None else None, _stream()))
+
+
+def decode_attn(dims: Dims, q_lat, q_pe, cache: LatentCache, seq_lens, num_splits: int, workspace):
+    cc = cache.c()
+    _check(lib().mla_decode_attn(ctypes.byref(dims), seq_lens.shape[0], _ptr(q_lat, torch.float32, "q_lat"),
+                                 _ptr(q_pe, torch.float32, "q_pe"), ctypes.byref(cc),
+                                 _ptr(seq_lens, torch.int32, "seq_lens"), num_splits,
+                                 _ptr(workspace, name="workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream()))
+
+
+def combine(dims: Dims, num_splits: int, seq_lens, workspace, o_lat, lse=None):
+    _check(lib().mla_combine(ctypes.byref(dims), seq_lens.shape[0], num_splits,
+                             _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(workspace, name="workspace"),
+                             workspace.numel() * workspace.element_size(), _ptr(o_lat, torch.float32, "o_lat"),
+                             _ptr(lse, torch.float32, "lse"), _stream()))
+
+
+def absorb_out(dims: Dims, o_lat, W_uv, W_o, workspace, u):
+    wdt = DTYPE_CODE[W_uv.dtype]
+    _check(lib().mla_absorb_out(ctypes.byref(dims), o_lat.shape[0], wdt, _ptr(o_lat, torch.float32, "o_lat"),
+                                _ptr(W_uv, name="W_uv"), _ptr(W_o, W_uv.dtype, "W_o"),
+                                _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                _ptr(u, torch.float32, "u"), _stream()))
+
+
+def cache_store(dims: Dims, cache: LatentCache, n_rows, max_rows: int, src, src_stride: int):
+    cc = cache.c()
+    _check(lib().mla_cache_store(ctypes.byref(dims), ctypes.byref(cc), n_rows.shape[0],
+                                 _ptr(n_rows, torch.int32, "n_rows"), max_rows,
+                                 _ptr(src, torch.float32, "src"), src_stride, _stream()))
+
+
+def version() -> str:
+    return lib().mla_version().decode()
+
+
+# ------------------------------------------------------------------------------------------------
+class DecodeStep:
+    """Buffers for the five calls of one decode step, allocated once (torch), reused per step."""
+
+    def __init__(self, dims, B: int, num_splits: int, device="cuda", sm_scale: float = 0.0):
+        self.dims = Dims.of(dims, sm_scale)
+        self.B = B
+        self.num_splits = num_splits
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_lat = torch.empty((B, dims.n_h, dims.d_c), **f32)
+        self.q_pe = torch.empty((B, dims.n_h, dims.d_r), **f32)
+        self.kv_new = torch.empty((B, dims.d_c + dims.d_r), **f32)
+        self.o_lat = torch.empty((B, dims.n_h, dims.d_c), **f32)
+        self.lse = torch.empty((B, dims.n_h), **f32)
+        self.u = torch.empty((B, dims.d), **f32)
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.ws_q = torch.empty(max(1, absorb_q_workspace_bytes(self.dims, B)), **u8)
+        self.ws_d = torch.empty(max(1, decode_workspace_bytes(self.dims, B, num_splits)), **u8)
+        self.ws_o = torch.empty(max(1, absorb_out_workspace_bytes(self.dims, B)), **u8)
+
+    def run(self, h, W, cache: LatentCache, seq_lens):
+        """absorb_q -> rope (append) -> decode_attn -> combine -> absorb_out; returns u [B, d]."""
+        absorb_q(self.dims, h, W, self.ws_q, self.q_lat, self.q_pe, self.kv_new)
+        rope(self.dims, seq_lens, self.q_pe, self.kv_new, cache)
+        decode_attn(self.dims, self.q_lat, self.q_pe, cache, seq_lens, self.num_splits, self.ws_d)
+        combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
+        absorb_out(self.dims, self.o_lat, W["W_uv"], W["W_o"], self.ws_o, self.u)
+        return self.u

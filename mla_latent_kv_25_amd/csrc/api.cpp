@@ -1,0 +1,230 @@
+// C ABI of libmla: host-side validation, workspace sizing and dispatch. Every entry point checks
+// its arguments before enqueueing anything; no entry point allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mla.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status ok() {
+  g_err[0] = 0;
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorNotSupported) return fail(MLA_E_UNSUPPORTED, "%s: no kernel for these dims/dtype", what);
+  return fail(MLA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_wdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16; }
+bool valid_cdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+
+mla_status check_dims(const mla_dims* d, const char* fn) {
+  if (!d) return fail(MLA_E_ARG, "%s: dims is NULL", fn);
+  if (d->d <= 0 || d->n_h <= 0 || d->d_h <= 0 || d->d_c <= 0 || d->d_cq <= 0 || d->d_r <= 0)
+    return fail(MLA_E_ARG, "%s: every dimension must be > 0", fn);
+  if (d->d_r % 8 != 0 || d->d_c % 8 != 0) return fail(MLA_E_ARG, "%s: d_c and d_r must be multiples of 8", fn);
+  if (!(d->rope_base > 1.0) || !std::isfinite(d->rope_base)) return fail(MLA_E_ARG, "%s: rope_base must be > 1", fn);
+  if (!std::isfinite(d->sm_scale)) return fail(MLA_E_ARG, "%s: sm_scale must be finite", fn);
+  return MLA_OK;
+}
+
+mla_status check_cache(const mla_cache* c, const char* fn, mla::CacheArgs* out) {
+  if (!c) return fail(MLA_E_ARG, "%s: cache is NULL", fn);
+  if (!c->rows) return fail(MLA_E_ARG, "%s: cache rows is NULL", fn);
+  if (!valid_cdtype(c->dtype)) return fail(MLA_E_ARG, "%s: bad cache dtype %d", fn, c->dtype);
+  if ((c->dtype == MLA_FP8_E4M3) != (c->scales != nullptr))
+    return fail(MLA_E_ARG, "%s: scales must be given exactly for the fp8 cache", fn);
+  if (c->page_size < 0) return fail(MLA_E_ARG, "%s: page_size < 0", fn);
+  if (c->page_size == 0) {
+    if (c->t_cap < 1) return fail(MLA_E_ARG, "%s: contiguous cache needs t_cap >= 1", fn);
+  } else {
+    if (!c->block_table) return fail(MLA_E_ARG, "%s: paged cache needs a block table", fn);
+    if (c->max_pages < 1 || c->num_pages < 1) return fail(MLA_E_ARG, "%s: paged cache needs max_pages, num_pages >= 1", fn);
+    if (c->t_cap != (int64_t)c->max_pages * c->page_size)
+      return fail(MLA_E_ARG, "%s: paged cache t_cap must equal max_pages * page_size", fn);
+  }
+  out->rows = c->rows;
+  out->scales = c->scales;
+  out->block_table = c->block_table;
+  out->t_cap = c->t_cap;
+  out->dtype = c->dtype;
+  out->page_size = c->page_size;
+  out->max_pages = c->max_pages;
+  out->num_pages = c->num_pages;
+  return MLA_OK;
+}
+
+float resolve_scale(const mla_dims* d) {
+  return d->sm_scale > 0.f ? d->sm_scale : (float)(1.0 / std::sqrt((double)(d->d_h + d->d_r)));
+}
+
+}  // namespace
+
+namespace mla {
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+}  // namespace mla
+
+static int resolve_splits(int32_t num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int n = mla::device_cu_count();
+  return n < 1024 ? n : 1024;
+}
+
+extern "C" {
+
+const char* mla_version(void) { return "mla_latent_kv_25_amd 0.1 (gfx950)"; }
+const char* mla_last_error(void) { return g_err; }
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_E_ARG: return "MLA_E_ARG";
+    case MLA_E_UNSUPPORTED: return "MLA_E_UNSUPPORTED";
+    case MLA_E_WORKSPACE: return "MLA_E_WORKSPACE";
+    case MLA_E_HIP: return "MLA_E_HIP";
+  }
+  return "MLA_E_?";
+}
+
+size_t mla_absorb_q_workspace_bytes(const mla_dims* dims, int32_t B) {
+  if (!dims || B <= 0) return 0;
+  return mla::absorb_q_layout(*dims, B).bytes;
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h, const void* W_dq,
+                        const void* W_uq, const void* W_qr, const void* W_uk, const void* W_dkv, const void* W_kr,
+                        void* workspace, size_t ws_bytes, float* q_lat, float* q_pe, float* kv_new,
+                        hipStream_t stream) {
+  const char* fn = "mla_absorb_q";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (B == 0) return ok();
+  if (!h || !W_dq || !W_uq || !W_qr || !W_uk || !W_dkv || !W_kr || !q_lat || !q_pe || !kv_new)
+    return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (!workspace || ws_bytes < mla_absorb_q_workspace_bytes(dims, B))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_q_workspace_bytes(dims, B));
+  return hip_status(mla::launch_absorb_q(*dims, B, wdtype, h, W_dq, W_uq, W_qr, W_uk, W_dkv, W_kr, workspace, q_lat,
+                                         q_pe, kv_new, stream),
+                    fn);
+}
+
+mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, float* q_pe, float* kv_new,
+                    const mla_cache* cache, hipStream_t stream) {
+  const char* fn = "mla_rope";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (B == 0) return ok();
+  if (!seq_lens || !q_pe || !kv_new) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  mla::CacheArgs c{};
+  if (cache) {
+    s = check_cache(cache, fn, &c);
+    if (s) return s;
+  }
+  return hip_status(mla::launch_rope(*dims, B, seq_lens, q_pe, kv_new, cache ? &c : nullptr, stream), fn);
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t num_splits) {
+  if (!dims || B <= 0 || num_splits < 0) return 0;
+  return mla::decode_layout(*dims, B, resolve_splits(num_splits)).bytes;
+}
+
+mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, const float* q_pe,
+                           const mla_cache* cache, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "mla_decode_attn";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (num_splits < 0 || num_splits > 1024) return fail(MLA_E_ARG, "%s: num_splits must be in [0, 1024]", fn);
+  mla::CacheArgs c{};
+  s = check_cache(cache, fn, &c);
+  if (s) return s;
+  if (B == 0) return ok();
+  if (!q_lat || !q_pe || !seq_lens) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (!mla::decode_supported(*dims, c.dtype, c.page_size))
+    return fail(MLA_E_UNSUPPORTED, "%s: no decode kernel for n_h=%d d_c=%d d_r=%d with cache dtype %d", fn,
+                dims->n_h, dims->d_c, dims->d_r, c.dtype);
+  const int G = resolve_splits(num_splits);
+  const size_t need = mla::decode_layout(*dims, B, G).bytes;
+  if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  return hip_status(mla::launch_decode(*dims, B, q_lat, q_pe, c, seq_lens, G, resolve_scale(dims), workspace, stream),
+                    fn);
+}
+
+mla_status mla_combine(const mla_dims* dims, int32_t B, int32_t num_splits, const int32_t* seq_lens,
+                       const void* workspace, size_t ws_bytes, float* o_lat, float* lse, hipStream_t stream) {
+  const char* fn = "mla_combine";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (num_splits < 0 || num_splits > 1024) return fail(MLA_E_ARG, "%s: num_splits must be in [0, 1024]", fn);
+  if (B == 0) return ok();
+  if (!seq_lens || !o_lat) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  const int G = resolve_splits(num_splits);
+  const size_t need = mla::decode_layout(*dims, B, G).bytes;
+  if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  return hip_status(mla::launch_combine(*dims, B, G, workspace, o_lat, lse, stream), fn);
+}
+
+size_t mla_absorb_out_workspace_bytes(const mla_dims* dims, int32_t B) {
+  if (!dims || B <= 0) return 0;
+  return mla::absorb_out_layout(*dims, B).bytes;
+}
+
+mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat, const void* W_uv,
+                          const void* W_o, void* workspace, size_t ws_bytes, float* u, hipStream_t stream) {
+  const char* fn = "mla_absorb_out";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (B == 0) return ok();
+  if (!o_lat || !W_uv || !W_o || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (!workspace || ws_bytes < mla_absorb_out_workspace_bytes(dims, B))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_out_workspace_bytes(dims, B));
+  return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
+}
+
+mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t B, const int32_t* n_rows,
+                           int32_t max_rows, const float* src, int64_t src_stride, hipStream_t stream) {
+  const char* fn = "mla_cache_store";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  mla::CacheArgs c{};
+  s = check_cache(cache, fn, &c);
+  if (s) return s;
+  if (B < 0 || max_rows < 0) return fail(MLA_E_ARG, "%s: B and max_rows must be >= 0", fn);
+  if (B == 0 || max_rows == 0) return ok();
+  if (!n_rows || !src) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (src_stride < max_rows) return fail(MLA_E_ARG, "%s: src_stride < max_rows", fn);
+  if (max_rows > c.t_cap) return fail(MLA_E_ARG, "%s: max_rows exceeds the cache capacity", fn);
+  return hip_status(mla::launch_cache_store(*dims, c, B, n_rows, max_rows, src, src_stride, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,676 @@
+// Latent-space decode attention and the split-sequence combine.
+//
+// "DeepSeek-V2 from Scratch" section 4.4: the score of head i against cached token j is
+// q^C_i.k^C_{j,i} + q^R_i.k^R_j over sqrt(d_h + d_h^R); section 5.1: the content part equals
+// q~_i.c_j with q~_i = (W^UK_i)^T q^C_i; section 5.3 steps 2-3: dot the absorbed query with every
+// cached latent and sum the latents under the softmax weights. Each cached row is
+// [c_j (d_c) | k^R_j (d_r)], so with q = [q~_i | q^R_i] the whole score is one dot product over
+// the row, and the weighted sum runs over the first d_c entries of the same rows.
+//
+// Work split: the batch's tokens (concatenated sequence by sequence) are cut into G equal ranges;
+// range p is one workgroup. A range may cover the end of one sequence and the start of the next;
+// each (range, sequence) piece writes a normalised partial o and its log-sum-exp into slot p + b
+// of the workspace (slots are unique: ranges and sequences both advance with the token order).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+DecodeLayout decode_layout(const mla_dims& d, int B, int G) {
+  DecodeLayout L;
+  L.n_pieces = (int64_t)G + B - 1;
+  L.off_cu = 0;
+  L.off_lse = ((size_t)(B + 1) * 8 + 255) & ~(size_t)255;
+  L.off_o = (L.off_lse + (size_t)L.n_pieces * d.n_h * 4 + 255) & ~(size_t)255;
+  L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;
+  return L;
+}
+
+__device__ __forceinline__ int64_t row_index(const CacheArgs& c, int b, int64_t j) {
+  if (c.page_size == 0) return (int64_t)b * c.t_cap + j;
+  int32_t page = c.block_table[(int64_t)b * c.max_pages + j / c.page_size];
+  return (int64_t)page * c.page_size + (j % c.page_size);
+}
+
+// ------------------------------------------------------------------------------------------------
+// cu[b] = sum_{b' < b} seq_lens[b'] (int64), one block.
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seq_lens, int B,
+                                               int64_t* __restrict__ cu) {
+  __shared__ int64_t part[1024];
+  __shared__ int64_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    int i = base + tid;
+    int64_t v = i < B ? (int64_t)seq_lens[i] : 0;
+    part[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
+      int64_t x = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += x;
+      __syncthreads();
+    }
+    if (i < B) cu[i + 1] = carry + part[tid];
+    __syncthreads();
+    if (tid == 1023) carry += part[1023];
+    __syncthreads();
+  }
+  if (tid == 0) cu[0] = 0;
+}
+
+// Range assignment: workgroups are dispatched round-robin over the 8 XCDs; consecutive ranges
+// (usually the same sequence, sharing its query in L2) are mapped onto the same XCD.
+__device__ __forceinline__ int range_for_block(int bid, int G) {
+  if (G % 8 == 0) return (bid & 7) * (G >> 3) + (bid >> 3);
+  return bid;
+}
+
+__device__ __forceinline__ int first_seq(const int64_t* cu, int B, int64_t t) {
+  int lo = 0, hi = B - 1;  // largest b with cu[b] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ================================================================================================
+// MFMA kernel for the DeepSeek-V2 shape: n_h = 128, d_c = 512, d_r = 64 (row = 576).
+// One workgroup = 4 waves; wave w owns heads [32w, 32w + 32). All heads share each latent tile,
+// staged once in LDS. Per 32-token tile and wave:
+//   S^T[32 tok x 32 heads] = K[32 x 576] Q^T            (36 MFMA 32x32x16, K rows via ds_read_b128)
+//   online softmax in float32 (base-2, scale folded into Q)
+//   O^T[512 x 32 heads] += V^T[512 x 32 tok] P^T        (32 MFMA, V^T via ds_read_b64_tr_b16)
+// The S^T accumulator layout (lane: head, registers: tokens) is exactly the B-operand layout of
+// the P^T product, so probabilities never leave registers.
+namespace v2 {
+constexpr int NH = 128, DC = 512, DR = 64, RW = 576;
+constexpr int TT = 32;                     // tokens per tile
+constexpr int ROWB = RW * 2;               // bytes of one bf16 row in LDS
+constexpr int CHUNKS = RW / 8;             // 16-byte chunks per row (72)
+constexpr int TILE_CHUNKS = TT * CHUNKS;   // 2304
+constexpr int TILEB = TT * ROWB;           // 36864
+constexpr int LOADS = TILE_CHUNKS / 256;   // chunks staged per thread per tile (9)
+constexpr int KSTEPS = RW / 16;            // 36
+constexpr int CB = DC / 32;                // 16 output column blocks
+}  // namespace v2
+
+// LDS position of chunk c of tile row t: XOR swizzle inside aligned groups of 8 chunks, so 16
+// consecutive rows read at one chunk index hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int t, int c) { return c ^ ((t >> 1) & 7); }
+
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t em = c & 0x7fu;
+  if (em >= 8u) return s | ((em + (120u << 3)) << 4);
+  float v = (float)em * 0.001953125f;  // subnormal: em * 2^-9, exact in bf16
+  return s | (__builtin_bit_cast(uint32_t, v) >> 16);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding, then barrier.
+// The memory clobber keeps the compiler from moving LDS reads above it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Cached-row locator for one sequence: contiguous [B, t_cap, row] or pages of 2^ps_shift rows.
+// Within one 32-token tile at most two pages occur (page size >= 32); their ids are read once
+// per tile with uniform (scalar) loads.
+template <bool PAGED>
+struct Rows {
+  int64_t base_row;       // contiguous: b * t_cap
+  const int32_t* bt;      // paged: block table row of sequence b
+  int ps_shift;
+  int32_t pg0, pg1;
+  int64_t tile_page0;
+  __device__ __forceinline__ void init(const CacheArgs& c, int b) {
+    if constexpr (PAGED) {
+      bt = c.block_table + (int64_t)b * c.max_pages;
+      ps_shift = __builtin_ctz((unsigned)c.page_size);
+    } else {
+      base_row = (int64_t)b * c.t_cap;
+    }
+  }
+  __device__ __forceinline__ void tile(int64_t t0, int64_t t_last) {
+    if constexpr (PAGED) {
+      tile_page0 = t0 >> ps_shift;
+      pg0 = bt[tile_page0];
+      pg1 = bt[t_last >> ps_shift];
+    }
+  }
+  __device__ __forceinline__ int64_t row(int64_t tok) const {
+    if constexpr (PAGED) {
+      const int32_t pg = (tok >> ps_shift) == tile_page0 ? pg0 : pg1;
+      return ((int64_t)pg << ps_shift) + (tok & ((1 << ps_shift) - 1));
+    } else {
+      return base_row + tok;
+    }
+  }
+};
+
+// Scores of one tile: S^T[32 tok x 32 heads] = sum over 36 k-steps of K-tile rows x Q^T.
+// The chain is written with explicit MFMA instructions so that S lives in VGPRs: the 256
+// accumulators of O^T take all AGPRs, and letting the compiler place S in AGPRs too evicts the
+// query fragments. MFMA -> MFMA accumulation into the same registers needs no wait states; the
+// 24 wait states after the last step cover the MFMA-result -> VALU-read dependency and are in
+// the same asm statement so no reader can be scheduled between them.
+__device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_t (&kq)[4],
+                                              const bf16x8 (&qf)[v2::KSTEPS]) {
+  f32x16 s;
+  bf16x8 a = *(const bf16x8*)(tile + kq[0]);
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qf[0]));
+#pragma unroll
+  for (int ks = 1; ks < v2::KSTEPS - 1; ++ks) {
+    a = *(const bf16x8*)(tile + kq[ks & 3] + 128 * (ks >> 2));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qf[ks]));
+  }
+  constexpr int KL = v2::KSTEPS - 1;
+  a = *(const bf16x8*)(tile + kq[KL & 3] + 128 * (KL >> 2));
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(s) : "v"(a), "v"(qf[KL]));
+  return s;
+}
+
+template <int CDT, bool PAGED>
+__global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ q_lat,
+                                                      const float* __restrict__ q_pe, CacheArgs cache,
+                                                      const int64_t* __restrict__ cu, int B, int G,
+                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ o_part) {
+  using namespace v2;
+  constexpr bool FP8 = CDT == MLA_FP8_E4M3;
+  constexpr int NBUF = FP8 ? 2 : 3;
+  // Softmax reference: per head, the maximum of the segment's first tile. Later probabilities are
+  // exp2(s - m_ref) <= 2^HEAD (fine in float32/bf16), so the accumulators are never rescaled. A
+  // score above m_ref + HEAD makes the workgroup run the segment once more with the segment's
+  // true maximum as the reference (exact; at most one re-run).
+  constexpr float HEAD = 64.f;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
+  __shared__ float lds_sc[NBUF][TT];
+  __shared__ int redo_flag;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int p = range_for_block(blockIdx.x, G);
+  const int64_t total = cu[B];
+  int64_t start = range_start(p, total, G);
+  const int64_t end = range_start(p + 1, total, G);
+  if (start >= end) return;
+  int b = first_seq(cu, B, start);
+  const int head = 32 * w + l32;
+
+  // Per-lane LDS byte offsets inside a tile. The swizzle only permutes the low 3 bits of a chunk
+  // index, so every read is one of a few per-lane bases plus a compile-time immediate.
+  //  K rows (scores): chunk c = 2ks + g of row l32 -> base kq[ks & 3] + 128 * (ks >> 2)
+  uint32_t kq[4];
+  {
+    const int kx = (l32 >> 1) & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kq[j] = l32 * ROWB + (((2 * j + g) ^ kx) << 4);
+  }
+  //  V^T (transposed reads): rows ta = 16kk + 4g + j16/4 and ta + 8, chunk 4cb + cst
+  //  -> base vq[kk][row a/b][cb & 1] + 128 * (cb >> 1)
+  uint32_t vq[2][2][2];
+  {
+    const int j16 = lane & 15, h2 = (lane >> 4) & 1;
+    const int cst = 2 * h2 + ((j16 & 3) >> 1);
+    const int sub = (j16 & 1) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int ab = 0; ab < 2; ++ab) {
+        const int t = 16 * kk + 4 * g + (j16 >> 2) + 8 * ab;
+        const int key = (t >> 1) & 7;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) vq[kk][ab][par] = t * ROWB + sub + (((4 * par + cst) ^ key) << 4);
+      }
+  }
+
+  while (start < end) {
+    const int64_t s0 = cu[b], s1 = cu[b + 1];
+    if (s1 <= start) { ++b; continue; }
+    const int64_t seg_end = end < s1 ? end : s1;
+    const int64_t t0 = start - s0, t1 = seg_end - s0;
+    const int64_t slot = (int64_t)p + b;
+    Rows<PAGED> rows;
+    rows.init(cache, b);
+
+    // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
+    bf16x8 qf[KSTEPS];
+    {
+      const float* ql = q_lat + ((int64_t)b * NH + head) * DC;
+      const float* qp = q_pe + ((int64_t)b * NH + head) * DR;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int f0 = 16 * ks + 8 * g;
+        const float* src = f0 < DC ? ql + f0 : qp + (f0 - DC);
+        f32x4 a = *(const f32x4*)src, c = *(const f32x4*)(src + 4);
+        bf16x8 v;
+        v[0] = (__bf16)(a[0] * qscale); v[1] = (__bf16)(a[1] * qscale);
+        v[2] = (__bf16)(a[2] * qscale); v[3] = (__bf16)(a[3] * qscale);
+        v[4] = (__bf16)(c[0] * qscale); v[5] = (__bf16)(c[1] * qscale);
+        v[6] = (__bf16)(c[2] * qscale); v[7] = (__bf16)(c[3] * qscale);
+        qf[ks] = v;
+      }
+    }
+
+    const int64_t n = t1 - t0;
+    const int ntiles = (int)((n + TT - 1) / TT);
+    auto valid_of = [&](int it) -> int {
+      const int64_t r = n - (int64_t)it * TT;
+      return r < TT ? (int)r : TT;
+    };
+
+    f32x16 O[CB];
+    float m_ref = -__builtin_inff(), m_seg = -__builtin_inff(), l_run = 0.f;
+    bool have_ref = false;
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) O[cb] = f32x16{};
+      l_run = 0.f;
+      if (tid == 0) redo_flag = 0;
+      bool over = false;
+
+      // ---- one tile: scores, probabilities against the reference, weighted latent sum
+      auto compute = [&](const uint8_t* tile, const float* sc, int valid) __attribute__((always_inline)) {
+        f32x16 s = tile_scores(tile, kq, qf);
+        // register r holds token 8(r/4) + 4g + r%4 of the tile; lane holds head `head`
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tk = 8 * (r >> 2) + 4 * g + (r & 3);
+          float v = s[r];
+          if constexpr (FP8) v *= sc[tk];
+          v = tk < valid ? v : -__builtin_inff();
+          s[r] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (!have_ref) { m_ref = mx; have_ref = true; }
+        m_seg = fmaxf(m_seg, mx);
+        over |= mx > m_ref + HEAD;
+        float rs = 0.f;
+        bf16x8 pk0, pk1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = __builtin_amdgcn_exp2f(fminf(s[r] - m_ref, HEAD));
+          rs += e;
+          if constexpr (FP8) e *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
+          if (r < 8) pk0[r] = (__bf16)e; else pk1[r - 8] = (__bf16)e;
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run += rs;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 pk = kk == 0 ? pk0 : pk1;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            // tile-dependent part in a scalar register so the per-lane part stays a few bases
+            const uint32_t sb = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 128u * (cb >> 1));
+            const uint32_t ia = vq[kk][0][cb & 1] + sb;
+            const uint32_t ib = vq[kk][1][cb & 1] + sb;
+            const u32x2 x0 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
+            const u32x2 x1 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
+            const u32x4 av = {x0.x, x0.y, x1.x, x1.y};
+            O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk, O[cb], 0, 0, 0);
+          }
+        }
+      };
+
+      if constexpr (!FP8) {
+        // bf16: 16-byte chunks go straight from HBM into LDS; two tiles stay in flight.
+        const uint8_t* rows_b = (const uint8_t*)cache.rows;
+        auto issue = [&](int it) {
+          const int64_t tt0 = t0 + (int64_t)it * TT;
+          const int64_t tlast = (tt0 + TT - 1 < t1 - 1) ? tt0 + TT - 1 : t1 - 1;
+          rows.tile(tt0, tlast);
+          uint8_t* dst = lds + (it % NBUF) * TILEB + w * 1024;
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) {
+            const int f = i * 256 + tid, t = f / CHUNKS;
+            int64_t tok = tt0 + t;
+            if (tok > t1 - 1) tok = t1 - 1;
+            const uint8_t* src = rows_b + rows.row(tok) * ROWB + (swz(t, f - t * CHUNKS) << 4);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (MLA_LDS void*)(dst + i * 4096), 16, 0, 0);
+          }
+        };
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        issue(0);
+        if (ntiles > 1) issue(1);
+        for (int it = 0; it < ntiles; ++it) {
+          if (it + 1 < ntiles) vm_wait_barrier<LOADS>(); else vm_wait_barrier<0>();
+          if (it + 2 < ntiles) issue(it + 2);
+          compute(lds + (it % NBUF) * TILEB, nullptr, valid_of(it));
+        }
+      } else {
+        // fp8: codes widened to bf16 in registers on the way into LDS; scales per token.
+        u32x2 r8[LOADS];
+        float scv = 0.f;
+        auto load = [&](int it) {
+          const int64_t tt0 = t0 + (int64_t)it * TT;
+          const int64_t tlast = (tt0 + TT - 1 < t1 - 1) ? tt0 + TT - 1 : t1 - 1;
+          rows.tile(tt0, tlast);
+          const uint8_t* rows_b = (const uint8_t*)cache.rows;
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) {
+            const int f = i * 256 + tid, t = f / CHUNKS;
+            int64_t tok = tt0 + t;
+            if (tok > t1 - 1) tok = t1 - 1;
+            r8[i] = *(const u32x2*)(rows_b + rows.row(tok) * RW + (swz(t, f - t * CHUNKS) << 3));
+          }
+          if (tid < TT) {
+            int64_t tok = tt0 + tid;
+            if (tok > t1 - 1) tok = t1 - 1;
+            scv = cache.scales[rows.row(tok)];
+          }
+        };
+        auto store = [&](int it) {
+          uint8_t* dst = lds + (it % NBUF) * TILEB;
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) {
+            u32x4 o;
+            const uint32_t lo = r8[i].x, hi = r8[i].y;
+            o.x = e4m3_to_bf16_bits(lo & 0xff) | (e4m3_to_bf16_bits((lo >> 8) & 0xff) << 16);
+            o.y = e4m3_to_bf16_bits((lo >> 16) & 0xff) | (e4m3_to_bf16_bits(lo >> 24) << 16);
+            o.z = e4m3_to_bf16_bits(hi & 0xff) | (e4m3_to_bf16_bits((hi >> 8) & 0xff) << 16);
+            o.w = e4m3_to_bf16_bits((hi >> 16) & 0xff) | (e4m3_to_bf16_bits(hi >> 24) << 16);
+            *(u32x4*)(dst + (size_t)(i * 256 + tid) * 16) = o;
+          }
+          if (tid < TT) lds_sc[it % NBUF][tid] = scv;
+        };
+        __syncthreads();
+        load(0);
+        store(0);
+        if (ntiles > 1) load(1);
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+          compute(lds + (it % NBUF) * TILEB, lds_sc[it % NBUF], valid_of(it));
+          if (it + 1 < ntiles) store(it + 1);
+          if (it + 2 < ntiles) load(it + 2);
+          __syncthreads();
+        }
+      }
+      // does any head of the workgroup need the second pass?
+      if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) redo_flag = 1;
+      __syncthreads();
+      const int redo = redo_flag;
+      __syncthreads();
+      if (!redo) break;
+      m_ref = m_seg;  // exact maximum of the segment for every head of every wave
+    }
+
+    // ---- normalised partial and its log-sum-exp (natural log)
+    const float inv_l = 1.f / l_run;
+    float* dst = o_part + (slot * NH + head) * DC;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v;
+        v[0] = O[cb][4 * r4 + 0] * inv_l; v[1] = O[cb][4 * r4 + 1] * inv_l;
+        v[2] = O[cb][4 * r4 + 2] * inv_l; v[3] = O[cb][4 * r4 + 3] * inv_l;
+        *(f32x4*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
+      }
+    }
+    if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
+
+    start = seg_end;
+    ++b;
+  }
+}
+
+// ================================================================================================
+// Generic kernel (any cache dtype, small dims): float32 arithmetic throughout. Used for the
+// running model and float32 caches. Limits: n_h*(d_c+d_r) <= 16384, d_c+d_r <= 512, n_h <= 64,
+// n_h*d_c <= 4096.
+namespace gen {
+constexpr int TT = 32;
+constexpr int OPT = 16;  // outputs per thread
+}
+
+template <int CDT>
+__device__ __forceinline__ float cache_elem(const CacheArgs& c, int64_t ridx, int rw, int e) {
+  if constexpr (CDT == MLA_F32) return ((const float*)c.rows)[ridx * rw + e];
+  else if constexpr (CDT == MLA_F16) return f16_bits_to_f32(((const uint16_t*)c.rows)[ridx * rw + e]);
+  else if constexpr (CDT == MLA_BF16) return bf16_bits_to_f32(((const uint16_t*)c.rows)[ridx * rw + e]);
+  else return e4m3_to_f32(((const uint8_t*)c.rows)[ridx * rw + e]) * c.scales[ridx];
+}
+
+template <int CDT>
+__global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_r,
+                                                        const float* __restrict__ q_lat,
+                                                        const float* __restrict__ q_pe, CacheArgs cache,
+                                                        const int64_t* __restrict__ cu, int B, int G,
+                                                        float qscale, float* __restrict__ lse_part,
+                                                        float* __restrict__ o_part) {
+  using namespace gen;
+  extern __shared__ float sm[];
+  const int rw = d_c + d_r;
+  float* qs = sm;                       // [n_h][rw]
+  float* ts = qs + n_h * rw;            // [TT][rw]
+  float* ss = ts + TT * rw;             // [n_h][TT]
+  float* mrun = ss + n_h * TT;          // [n_h]
+  float* lrun = mrun + n_h;             // [n_h]
+  float* alf = lrun + n_h;              // [n_h]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int p = range_for_block(blockIdx.x, G);
+  const int64_t total = cu[B];
+  int64_t start = range_start(p, total, G);
+  const int64_t end = range_start(p + 1, total, G);
+  if (start >= end) return;
+  int b = first_seq(cu, B, start);
+  const int nout = n_h * d_c;
+
+  while (start < end) {
+    const int64_t s0 = cu[b], s1 = cu[b + 1];
+    if (s1 <= start) { ++b; continue; }
+    const int64_t seg_end = end < s1 ? end : s1;
+    const int64_t t0 = start - s0, t1 = seg_end - s0;
+    const int64_t slot = (int64_t)p + b;
+    for (int i = tid; i < n_h * rw; i += 256) {
+      int h = i / rw, e = i % rw;
+      qs[i] = (e < d_c ? q_lat[((int64_t)b * n_h + h) * d_c + e] : q_pe[((int64_t)b * n_h + h) * d_r + e - d_c]) * qscale;
+    }
+    for (int h = tid; h < n_h; h += 256) { mrun[h] = -__builtin_inff(); lrun[h] = 0.f; }
+    float O[OPT];
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) O[k] = 0.f;
+    __syncthreads();
+    for (int64_t tb = t0; tb < t1; tb += TT) {
+      const int valid = (int)((t1 - tb) < TT ? (t1 - tb) : TT);
+      for (int i = tid; i < TT * rw; i += 256) {
+        int t = i / rw, e = i % rw;
+        int64_t tok = tb + (t < valid ? t : valid - 1);
+        ts[i] = cache_elem<CDT>(cache, row_index(cache, b, tok), rw, e);
+      }
+      __syncthreads();
+      for (int i = tid; i < n_h * TT; i += 256) {
+        int h = i / TT, t = i % TT;
+        float acc = 0.f;
+        for (int e = 0; e < rw; ++e) acc += qs[h * rw + e] * ts[t * rw + e];
+        ss[i] = t < valid ? acc : -__builtin_inff();
+      }
+      __syncthreads();
+      for (int h = w; h < n_h; h += 4) {
+        float v = lane < TT ? ss[h * TT + lane] : -__builtin_inff();
+        float mx = wave_max(v);
+        float m_new = fmaxf(mrun[h], mx);
+        float e = exp2f(v - m_new);
+        float sum = wave_sum(e);
+        if (lane < TT) ss[h * TT + lane] = e;
+        if (lane == 0) {
+          float a = exp2f(mrun[h] - m_new);
+          alf[h] = a;
+          lrun[h] = lrun[h] * a + sum;
+          mrun[h] = m_new;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < OPT; ++k) {
+        int idx = tid + 256 * k;
+        if (idx < nout) {
+          int h = idx / d_c, c = idx % d_c;
+          float acc = O[k] * alf[h];
+          for (int t = 0; t < valid; ++t) acc += ss[h * TT + t] * ts[t * rw + c];
+          O[k] = acc;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      int idx = tid + 256 * k;
+      if (idx < nout) {
+        int h = idx / d_c;
+        o_part[slot * nout + idx] = O[k] / lrun[h];
+      }
+    }
+    for (int h = tid; h < n_h; h += 256)
+      lse_part[slot * n_h + h] = (mrun[h] + __log2f(lrun[h])) * 0.69314718055994530942f;
+    __syncthreads();
+    start = seg_end;
+    ++b;
+  }
+}
+
+// ================================================================================================
+// Combine: per sequence, merge the pieces of the ranges that cover it. One block = one sequence
+// and CH heads; the piece list and the per-(piece, head) weights exp(lse_s - M) / sum are built
+// once in LDS, then every output element is a weighted sum over the pieces (fixed order).
+namespace cmb {
+constexpr int CH = 8;        // heads per block
+constexpr int MAXP = 1024;   // pieces per sequence handled in one pass of the piece list
+}
+
+__global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t* __restrict__ cu, int B, int G,
+                                                 const float* __restrict__ lse_part,
+                                                 const float* __restrict__ o_part, float* __restrict__ o_lat,
+                                                 float* __restrict__ lse_out) {
+  using namespace cmb;
+  __shared__ int64_t sh_plo, sh_phi;
+  __shared__ int slots[MAXP];
+  __shared__ float wts[MAXP][CH];
+  __shared__ int sh_np;
+  const int b = blockIdx.y;
+  const int h0 = blockIdx.x * CH;
+  const int nh = (n_h - h0) < CH ? (n_h - h0) : CH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t total = cu[B];
+  const int64_t s0 = cu[b], s1 = cu[b + 1];
+  float* dst = o_lat + ((int64_t)b * n_h + h0) * d_c;
+  if (s1 <= s0) {  // empty sequence (outside the contract): defined output
+    for (int e = tid; e < nh * d_c; e += 256) dst[e] = 0.f;
+    if (lse_out && tid < nh) lse_out[(int64_t)b * n_h + h0 + tid] = -__builtin_inff();
+    return;
+  }
+  if (tid == 0) {
+    sh_plo = range_of(s0, total, G);
+    sh_phi = range_of(s1 - 1, total, G);
+    int np = 0;
+    for (int64_t p = sh_plo; p <= sh_phi && np < MAXP; ++p)
+      if (range_start(p, total, G) != range_start(p + 1, total, G)) slots[np++] = (int)(p + b);
+    sh_np = np;
+  }
+  __syncthreads();
+  const int np = sh_np;
+  // weights: wave w handles heads w, w+4, ...
+  for (int hh = w; hh < nh; hh += 4) {
+    float M = -__builtin_inff();
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, lse_part[(int64_t)slots[i] * n_h + h0 + hh]);
+    M = wave_max(M);
+    float sum = 0.f;
+    for (int i = lane; i < np; i += 64) {
+      const float e = __expf(lse_part[(int64_t)slots[i] * n_h + h0 + hh] - M);
+      wts[i][hh] = e;
+      sum += e;
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.f / sum;
+    for (int i = lane; i < np; i += 64) wts[i][hh] *= inv;
+    if (lse_out && lane == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
+  }
+  __syncthreads();
+  for (int e = tid; e < nh * d_c; e += 256) {
+    const int hh = e / d_c;
+    float acc = 0.f;
+    for (int i = 0; i < np; ++i) acc += wts[i][hh] * o_part[((int64_t)slots[i] * n_h + h0) * d_c + e];
+    dst[e] = acc;
+  }
+}
+
+// ================================================================================================
+static bool is_v2(const mla_dims& d) { return d.n_h == v2::NH && d.d_c == v2::DC && d.d_r == v2::DR; }
+static bool v2_page_ok(int ps) { return ps == 0 || (ps >= 32 && (ps & (ps - 1)) == 0); }
+
+bool decode_supported(const mla_dims& d, int cdt, int page_size) {
+  if (is_v2(d) && (cdt == MLA_BF16 || cdt == MLA_FP8_E4M3)) return v2_page_ok(page_size);
+  const int rw = d.d_c + d.d_r;
+  return d.n_h * rw <= 16384 && rw <= 512 && d.n_h <= 64 && d.n_h * d.d_c <= 256 * gen::OPT;
+}
+
+hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const float* q_pe,
+                         const CacheArgs& c, const int32_t* seq_lens, int G, float sm_scale,
+                         void* ws, hipStream_t st) {
+  if (!decode_supported(d, c.dtype, c.page_size)) return hipErrorNotSupported;
+  DecodeLayout L = decode_layout(d, B, G);
+  char* base = (char*)ws;
+  int64_t* cu = (int64_t*)(base + L.off_cu);
+  float* lse_part = (float*)(base + L.off_lse);
+  float* o_part = (float*)(base + L.off_o);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, seq_lens, B, cu);
+  const float qscale = sm_scale * 1.44269504088896340736f;  // log2(e)
+  if (is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3)) {
+    const bool paged = c.page_size > 0;
+#define MLA_V2(CDT, PG) \
+    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part)
+    if (c.dtype == MLA_BF16) { if (paged) MLA_V2(MLA_BF16, true); else MLA_V2(MLA_BF16, false); }
+    else { if (paged) MLA_V2(MLA_FP8_E4M3, true); else MLA_V2(MLA_FP8_E4M3, false); }
+#undef MLA_V2
+  } else {
+    const int rw = d.d_c + d.d_r;
+    size_t smem = (size_t)(d.n_h * rw + gen::TT * rw + d.n_h * gen::TT + 3 * d.n_h) * 4;
+    switch (c.dtype) {
+      case MLA_F32:
+        hipLaunchKernelGGL(k_decode_generic<MLA_F32>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
+                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+        break;
+      case MLA_F16:
+        hipLaunchKernelGGL(k_decode_generic<MLA_F16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
+                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+        break;
+      case MLA_BF16:
+        hipLaunchKernelGGL(k_decode_generic<MLA_BF16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
+                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+        break;
+      default:
+        hipLaunchKernelGGL(k_decode_generic<MLA_FP8_E4M3>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c,
+                           d.d_r, q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+        break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const mla_dims& d, int B, int G, const void* ws, float* o_lat, float* lse,
+                          hipStream_t st) {
+  DecodeLayout L = decode_layout(d, B, G);
+  const char* base = (const char*)ws;
+  dim3 grid((unsigned)((d.n_h + cmb::CH - 1) / cmb::CH), B);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, d.n_h, d.d_c, (const int64_t*)(base + L.off_cu), B, G,
+                     (const float*)(base + L.off_lse), (const float*)(base + L.off_o), o_lat, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

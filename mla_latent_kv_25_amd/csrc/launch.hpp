@@ -1,0 +1,60 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+// Plain-value copy of mla_cache passed by value to kernels.
+struct CacheArgs {
+  void* rows;
+  float* scales;
+  const int32_t* block_table;
+  int64_t t_cap;
+  int32_t dtype;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t num_pages;
+};
+
+// Workspace layout of mla_decode_attn / mla_combine (byte offsets).
+struct DecodeLayout {
+  int64_t n_pieces;   // num_splits + B - 1
+  size_t off_cu;      // int64 [B + 1] prefix sums of seq_lens
+  size_t off_lse;     // float [n_pieces, n_h]
+  size_t off_o;       // float [n_pieces, n_h, d_c]
+  size_t bytes;
+};
+DecodeLayout decode_layout(const mla_dims& d, int B, int G);
+
+// GEMM workspace layouts.
+struct AbsorbQLayout { size_t off_cq, off_qc, off_part, part_floats, bytes; };
+AbsorbQLayout absorb_q_layout(const mla_dims& d, int B);
+struct AbsorbOutLayout { size_t off_o, off_part, part_floats, bytes; };
+AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B);
+
+hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float* q_pe, float* kv_new,
+                       const CacheArgs* cache, hipStream_t st);
+hipError_t launch_cache_store(const mla_dims& d, const CacheArgs& c, int B, const int32_t* n_rows,
+                              int max_rows, const float* src, int64_t src_stride, hipStream_t st);
+
+// Returns hipErrorNotSupported (nothing launched) when no kernel covers the dims/dtype.
+hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const float* q_pe,
+                         const CacheArgs& c, const int32_t* seq_lens, int G, float sm_scale,
+                         void* ws, hipStream_t st);
+bool decode_supported(const mla_dims& d, int cache_dtype, int page_size);
+hipError_t launch_combine(const mla_dims& d, int B, int G, const void* ws, float* o_lat, float* lse,
+                          hipStream_t st);
+
+hipError_t launch_absorb_q(const mla_dims& d, int B, int wdtype, const void* h, const void* W_dq,
+                           const void* W_uq, const void* W_qr, const void* W_uk, const void* W_dkv,
+                           const void* W_kr, void* ws, float* q_lat, float* q_pe, float* kv_new,
+                           hipStream_t st);
+hipError_t launch_absorb_out(const mla_dims& d, int B, int wdtype, const float* o_lat, const void* W_uv,
+                             const void* W_o, void* ws, float* u, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace mla

@@ -9,6 +9,6 @@ from .encodings import (  # noqa: F401
 )
 from .mla import (  # noqa: F401
     OracleDims, softmax, rope, decode_step_explicit, decode_step_absorbed, decode_batch,
-    head_slices,
+    head_slices, absorbed_query, output_projection,
 )
 from .counts import cache_counts  # noqa: F401

@@ -180,6 +180,23 @@ def decode_step_absorbed(W, h, prefix, dims: OracleDims, cdtype):
     return dict(u=u, o_lat=o_lat, lse=lse)
 
 
+def absorbed_query(W, h, pos, dims: OracleDims):
+    """Stage outputs of the query pathway with W^UK absorbed ([Scratch] sections 4.1 and 5.1):
+    q~_i = (W^UK_i)^T q^C_i [n_h, d_c], the rotated q^R [n_h, d_r], and the current token's row
+    [c^KV ; RoPE(W^KR h)] before storage rounding."""
+    qC, qR, row, _, _ = new_token(W, h, pos, dims, "f32")
+    _, _, Wuk, _, _ = head_slices(W, dims)
+    q_lat = np.stack([Wuk[i].T @ qC[i] for i in range(dims.n_h)])
+    return q_lat, qR, row
+
+
+def output_projection(W, o_lat, dims: OracleDims):
+    """u = W^O [W^UV_1 o_lat_1; ...; W^UV_nh o_lat_nh] ([Scratch] sections 5.2 and 6)."""
+    _, _, _, Wuv, _ = head_slices(W, dims)
+    o = np.stack([Wuv[i] @ o_lat[i] for i in range(dims.n_h)])
+    return W["W_o"] @ o.reshape(-1)
+
+
 def decode_batch(W, h, prefixes, dims: OracleDims, cdtype, heads=None, want_u=True):
     """decode_step_explicit over a batch; prefixes[b] are sequence b's stored rows."""
     return [decode_step_explicit(W, h[b], prefixes[b], dims, cdtype, heads=heads, want_u=want_u)

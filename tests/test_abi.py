@@ -1,0 +1,131 @@
+"""The C-ABI library: it loads, exports every symbol include/mla.h declares, and rejects invalid
+arguments on the host before enqueueing anything (no GPU needed: every call here fails
+validation, or is a no-op, before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mla_latent_kv_25_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from mla_latent_kv_25_amd.build import build
+        build()
+    return binding.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(L, n), n
+    from mla_latent_kv_25_amd.binding import EXPORTS
+    assert sorted(EXPORTS) == names
+    assert L.mla_version().decode().startswith("mla_latent_kv_25_amd")
+
+
+def _dims(**kw):
+    from mla_latent_kv_25_amd.binding import Dims
+    d = dict(d=512, n_h=8, d_h=64, d_c=128, d_cq=96, d_r=32, rope_base=10000.0, sm_scale=0.0)
+    d.update(kw)
+    return Dims(**d)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first in every use below
+
+
+def test_status_strings(L):
+    assert L.mla_status_str(0) == b"MLA_OK"
+    assert L.mla_status_str(3) == b"MLA_E_WORKSPACE"
+
+
+def test_dims_validation(L):
+    assert L.mla_rope(None, 1, None, None, None, None, None) == 1
+    assert b"dims is NULL" in L.mla_last_error()
+    for bad in (dict(n_h=0), dict(d_r=30), dict(d_c=100), dict(rope_base=1.0), dict(d=-5)):
+        d = _dims(**bad)
+        assert L.mla_rope(ctypes.byref(d), 1, FAKE, FAKE, FAKE, None, None) == 1, bad
+
+
+def test_absorb_q_validation(L):
+    d = _dims()
+    # bad weight dtype (fp8 is a cache-only format)
+    assert L.mla_absorb_q(ctypes.byref(d), 2, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                          FAKE, FAKE, FAKE, None) == 1
+    # null tensor
+    assert L.mla_absorb_q(ctypes.byref(d), 2, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                          FAKE, FAKE, FAKE, None) == 1
+    # workspace too small
+    need = L.mla_absorb_q_workspace_bytes(ctypes.byref(d), 2)
+    assert need > 0
+    assert L.mla_absorb_q(ctypes.byref(d), 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                          FAKE, FAKE, FAKE, None) == 3
+    assert b"workspace" in L.mla_last_error()
+    # empty batch: nothing to do
+    assert L.mla_absorb_q(ctypes.byref(d), 0, 0, None, None, None, None, None, None, None, None, 0,
+                          None, None, None, None) == 0
+    assert L.mla_absorb_q(ctypes.byref(d), -1, 0, None, None, None, None, None, None, None, None, 0,
+                          None, None, None, None) == 1
+
+
+def _cache(**kw):
+    from mla_latent_kv_25_amd.binding import CCache
+    c = dict(rows=0x1000, scales=None, dtype=2, page_size=0, t_cap=64, block_table=None, max_pages=0, num_pages=0)
+    c.update(kw)
+    return CCache(**c)
+
+
+def test_cache_validation(L):
+    d = _dims()
+    cases = [
+        (_cache(rows=None), b"rows is NULL"),
+        (_cache(dtype=9), b"bad cache dtype"),
+        (_cache(dtype=3), b"scales"),                       # fp8 without scales
+        (_cache(scales=0x2000), b"scales"),                 # scales on a bf16 cache
+        (_cache(t_cap=0), b"t_cap"),
+        (_cache(page_size=64, t_cap=128), b"block table"),
+        (_cache(page_size=64, t_cap=100, block_table=0x3000, max_pages=2, num_pages=4), b"max_pages * page_size"),
+    ]
+    for c, msg in cases:
+        assert L.mla_decode_attn(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, 1 << 30, None) == 1
+        assert msg in L.mla_last_error(), (msg, L.mla_last_error())
+
+
+def test_decode_validation(L):
+    d = _dims()
+    c = _cache()
+    assert L.mla_decode_attn(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(c), FAKE, -1, FAKE, 1 << 30, None) == 1
+    assert L.mla_decode_attn(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(c), FAKE, 1025, FAKE, 1 << 40, None) == 1
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 3, 8)
+    # (8 + 3 - 1) pieces of n_h * (d_c + 1) floats plus the prefix sums
+    assert need >= (8 + 3 - 1) * 8 * (128 + 1) * 4 + 4 * 8
+    assert L.mla_decode_attn(ctypes.byref(d), 3, FAKE, FAKE, ctypes.byref(c), FAKE, 8, FAKE, need - 1, None) == 3
+    assert L.mla_combine(ctypes.byref(d), 3, 8, FAKE, FAKE, need - 1, FAKE, None, None) == 3
+    # the MFMA path needs power-of-two pages of at least 32 rows at the V2 shape
+    v2 = _dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
+    pc = _cache(page_size=48, t_cap=96, block_table=0x3000, max_pages=2, num_pages=2)
+    assert L.mla_decode_attn(ctypes.byref(v2), 1, FAKE, FAKE, ctypes.byref(pc), FAKE, 4, FAKE, 1 << 40, None) == 2
+    # no kernel for a float32 cache at the V2 shape
+    fc = _cache(dtype=0)
+    assert L.mla_decode_attn(ctypes.byref(v2), 1, FAKE, FAKE, ctypes.byref(fc), FAKE, 4, FAKE, 1 << 40, None) == 2
+
+
+def test_absorb_out_and_store_validation(L):
+    d = _dims()
+    assert L.mla_absorb_out(ctypes.byref(d), 2, 0, None, FAKE, FAKE, FAKE, 1 << 30, FAKE, None) == 1
+    need = L.mla_absorb_out_workspace_bytes(ctypes.byref(d), 2)
+    assert L.mla_absorb_out(ctypes.byref(d), 2, 0, FAKE, FAKE, FAKE, FAKE, need - 1, FAKE, None) == 3
+    c = _cache()
+    assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 65, FAKE, 65, None) == 1  # > t_cap
+    assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 10, FAKE, 5, None) == 1   # stride
+    assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 0, None, 0, None, 0, None) == 0

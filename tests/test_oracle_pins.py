@@ -322,3 +322,23 @@ def test_appended_row_is_rounded_like_storage():
         e = decode_step_explicit(W, h, np.zeros((0, dims.d_c + dims.d_r)), dims, cdtype)
         ref = torch.from_numpy(e["row_new"].astype(np.float32)).to(tdt).to(torch.float64).numpy()
         np.testing.assert_array_equal(e["read_new"], ref)
+
+
+def test_stage_helpers_agree_with_explicit_step():
+    """absorbed_query / output_projection (used for stage-level GPU checks) reproduce the explicit
+    step: scores from the absorbed query equal the explicit scores, and projecting the explicit
+    step's attention-weighted latent gives its u."""
+    from oracle import absorbed_query, output_projection
+    rng = np.random.default_rng(11)
+    dims = SMALL
+    W = _rand_weights(dims, rng, sw=0.4, kappa=2.0)
+    h = rng.standard_normal(dims.d)
+    prefix = rng.standard_normal((6, dims.d_c + dims.d_r))
+    e = decode_step_explicit(W, h, prefix, dims, "f32")
+    q_lat, qR, row = absorbed_query(W, h, 6, dims)
+    np.testing.assert_allclose(row, e["row_new"], rtol=1e-14)
+    rows = np.vstack([prefix, e["read_new"]])
+    s = (rows[:, :dims.d_c] @ q_lat.T + rows[:, dims.d_c:] @ qR.T) / np.sqrt(dims.d_h + dims.d_r)
+    m = s.max(0)
+    np.testing.assert_allclose(m + np.log(np.exp(s - m).sum(0)), e["lse"], rtol=1e-12)
+    np.testing.assert_allclose(output_projection(W, e["o_lat"], dims), e["u"], rtol=1e-11)
