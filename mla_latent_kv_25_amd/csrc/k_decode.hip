@@ -109,6 +109,15 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
   return s | (__builtin_bit_cast(uint32_t, v) >> 16);
 }
 
+// 16-byte global -> LDS copy per lane (LDS destination: wave-uniform `lds_addr` + 16 * lane).
+// Written as asm so the compiler does not add its conservative "wait for every LDS DMA" before
+// each LDS read: the kernel tracks these loads itself (vm_wait_barrier). The instruction has no
+// VGPR result; only M0 (not used by any other instruction of these kernels) is changed.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding, then barrier.
 // The memory clobber keeps the compiler from moving LDS reads above it.
 template <int N>
@@ -129,7 +138,7 @@ struct Rows {
   int64_t tile_page0;
   __device__ __forceinline__ void init(const CacheArgs& c, int b) {
     if constexpr (PAGED) {
-      bt = c.block_table + (int64_t)b * c.max_pages;
+      bt = c.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * c.max_pages;
       ps_shift = __builtin_ctz((unsigned)c.page_size);
     } else {
       base_row = (int64_t)b * c.t_cap;
@@ -137,9 +146,24 @@ struct Rows {
   }
   __device__ __forceinline__ void tile(int64_t t0, int64_t t_last) {
     if constexpr (PAGED) {
+      // uniform page indices -> scalar loads (counted by lgkmcnt, so they never wait on the
+      // in-flight tile copies that vmcnt tracks)
       tile_page0 = t0 >> ps_shift;
-      pg0 = bt[tile_page0];
-      pg1 = bt[t_last >> ps_shift];
+      const int i0 = __builtin_amdgcn_readfirstlane((int)tile_page0);
+      const int i1 = __builtin_amdgcn_readfirstlane((int)(t_last >> ps_shift));
+      // the block table is read-only for the whole kernel: constant address space -> s_load
+      const __attribute__((address_space(4))) int32_t* btc = (const __attribute__((address_space(4))) int32_t*)bt;
+      pg0 = btc[i0];
+      pg1 = btc[i1];
+    }
+  }
+  // Byte address of row tt0 + tr (tr < 32) of the tile that starts at tt0 (row width rb bytes).
+  __device__ __forceinline__ const uint8_t* tile_row(const uint8_t* base, int64_t tt0, int tr, int rb) const {
+    if constexpr (PAGED) {
+      const int64_t tok = tt0 + tr;
+      return base + row(tok) * rb;
+    } else {
+      return base + (base_row + tt0) * rb + (uint32_t)(tr * rb);
     }
   }
   __device__ __forceinline__ int64_t row(int64_t tok) const {
@@ -155,25 +179,29 @@ struct Rows {
 // Scores of one tile: S^T[32 tok x 32 heads] = sum over 36 k-steps of K-tile rows x Q^T.
 // The chain is written with explicit MFMA instructions so that S lives in VGPRs: the 256
 // accumulators of O^T take all AGPRs, and letting the compiler place S in AGPRs too evicts the
-// query fragments. MFMA -> MFMA accumulation into the same registers needs no wait states; the
-// 24 wait states after the last step cover the MFMA-result -> VALU-read dependency and are in
-// the same asm statement so no reader can be scheduled between them.
+// query fragments. Volatile asm statements keep their program order relative to memory
+// operations, so the LDS reads are issued LA k-steps ahead of the MFMA that consumes them.
+// MFMA -> MFMA accumulation into the same registers needs no wait states; the 24 wait states
+// after the last step cover the MFMA-result -> VALU-read dependency and sit in the same asm
+// statement so no reader can be scheduled between them.
 __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_t (&kq)[4],
                                               const bf16x8 (&qf)[v2::KSTEPS]) {
-  f32x16 s;
-  bf16x8 a = *(const bf16x8*)(tile + kq[0]);
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qf[0]));
+  constexpr int KS = v2::KSTEPS, LA = 6;
+  bf16x8 a[KS];
 #pragma unroll
-  for (int ks = 1; ks < v2::KSTEPS - 1; ++ks) {
-    a = *(const bf16x8*)(tile + kq[ks & 3] + 128 * (ks >> 2));
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qf[ks]));
+  for (int j = 0; j < LA; ++j) a[j] = *(const bf16x8*)(tile + kq[j & 3] + 128 * (j >> 2));
+  f32x16 s;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a[0]), "v"(qf[0]));
+  a[LA] = *(const bf16x8*)(tile + kq[LA & 3] + 128 * (LA >> 2));
+#pragma unroll
+  for (int ks = 1; ks < KS - 1; ++ks) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a[ks]), "v"(qf[ks]));
+    if (ks + LA < KS) a[ks + LA] = *(const bf16x8*)(tile + kq[(ks + LA) & 3] + 128 * ((ks + LA) >> 2));
   }
-  constexpr int KL = v2::KSTEPS - 1;
-  a = *(const bf16x8*)(tile + kq[KL & 3] + 128 * (KL >> 2));
   asm volatile(
       "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : "+v"(s) : "v"(a), "v"(qf[KL]));
+      : "+v"(s) : "v"(a[KS - 1]), "v"(qf[KS - 1]));
   return s;
 }
 
@@ -331,18 +359,21 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         // bf16: 16-byte chunks go straight from HBM into LDS; two tiles stay in flight.
         const uint8_t* rows_b = (const uint8_t*)cache.rows;
         auto issue = [&](int it) {
+          // opaque copy of the thread id: keeps the per-chunk addresses from being hoisted out of
+          // the tile loop (spilled, then reloaded with vmcnt waits that would drain the prefetch)
+          int tid_o = tid;
+          asm volatile("" : "+v"(tid_o));
           const int64_t tt0 = t0 + (int64_t)it * TT;
-          const int64_t tlast = (tt0 + TT - 1 < t1 - 1) ? tt0 + TT - 1 : t1 - 1;
-          rows.tile(tt0, tlast);
-          uint8_t* dst = lds + (it % NBUF) * TILEB + w * 1024;
+          const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+          rows.tile(tt0, tt0 + last);
+          const uint32_t dst = __builtin_amdgcn_readfirstlane(
+              (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
 #pragma unroll
           for (int i = 0; i < LOADS; ++i) {
-            const int f = i * 256 + tid, t = f / CHUNKS;
-            int64_t tok = tt0 + t;
-            if (tok > t1 - 1) tok = t1 - 1;
-            const uint8_t* src = rows_b + rows.row(tok) * ROWB + (swz(t, f - t * CHUNKS) << 4);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (MLA_LDS void*)(dst + i * 4096), 16, 0, 0);
+            const int f = i * 256 + tid_o, t = f / CHUNKS;
+            const int ch = swz(t, f - t * CHUNKS);
+            const uint8_t* src = rows.tile_row(rows_b, tt0, t < last ? t : last, ROWB) + (ch << 4);
+            dma16(src, dst + i * 4096);
           }
         };
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
