@@ -97,9 +97,16 @@ constexpr int KSTEPS = RW / 16;            // 36
 constexpr int CB = DC / 32;                // 16 output column blocks
 }  // namespace v2
 
-// LDS position of chunk c of tile row t: XOR swizzle inside aligned groups of 8 chunks, so 16
-// consecutive rows read at one chunk index hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int t, int c) { return c ^ ((t >> 1) & 7); }
+// LDS position of chunk c of tile row t: XOR of the low 3 chunk-index bits with a per-row key
+// (stays inside the aligned group of 8 chunks, so rows of 72 chunks never overflow). The key is
+// (t>>1) with its bits permuted so that (a) 16 consecutive rows read at one chunk index hit 16
+// distinct 16-byte bank groups (score reads) and (b) the 8 rows x 4 chunks of one transposing
+// V read spread evenly over the 64 banks (2 bank cycles per 512-byte read, the minimum).
+__device__ __forceinline__ int swz_key(int t) {
+  const int g = t >> 1;
+  return ((g & 1) << 2) | (((g >> 2) & 1) << 1) | ((g >> 1) & 1);
+}
+__device__ __forceinline__ int swz(int t, int c) { return c ^ swz_key(t); }
 
 __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
   uint32_t s = (c & 0x80u) << 8;
@@ -116,6 +123,12 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+// Same copy with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding, then barrier.
@@ -186,7 +199,7 @@ struct Rows {
 // statement so no reader can be scheduled between them.
 __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_t (&kq)[4],
                                               const bf16x8 (&qf)[v2::KSTEPS]) {
-  constexpr int KS = v2::KSTEPS, LA = 6;
+  constexpr int KS = v2::KSTEPS, LA = 4;
   bf16x8 a[KS];
 #pragma unroll
   for (int j = 0; j < LA; ++j) a[j] = *(const bf16x8*)(tile + kq[j & 3] + 128 * (j >> 2));
@@ -237,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
   //  K rows (scores): chunk c = 2ks + g of row l32 -> base kq[ks & 3] + 128 * (ks >> 2)
   uint32_t kq[4];
   {
-    const int kx = (l32 >> 1) & 7;
+    const int kx = swz_key(l32);
 #pragma unroll
     for (int j = 0; j < 4; ++j) kq[j] = l32 * ROWB + (((2 * j + g) ^ kx) << 4);
   }
@@ -253,11 +266,26 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
 #pragma unroll
       for (int ab = 0; ab < 2; ++ab) {
         const int t = 16 * kk + 4 * g + (j16 >> 2) + 8 * ab;
-        const int key = (t >> 1) & 7;
+        const int key = swz_key(t);
 #pragma unroll
         for (int par = 0; par < 2; ++par) vq[kk][ab][par] = t * ROWB + sub + (((4 * par + cst) ^ key) << 4);
       }
   }
+
+  // Tile staging: thread tid copies chunks f = 256 i + tid (i < 9) of the tile; chunk f is LDS
+  // bytes [16 f, 16 f + 16) = row f / 72, swizzled position f % 72. doff[i] is the byte offset of
+  // its source inside the tile's rows (row * row_bytes + source chunk * chunk_bytes).
+  // Offsets are < 2^16, so they are kept packed two per register.
+  uint32_t doff2[(LOADS + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (LOADS + 1) / 2; ++i) doff2[i] = 0;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int f = i * 256 + tid, t = f / CHUNKS;
+    const uint32_t o = (uint32_t)(t * (FP8 ? RW : ROWB) + (swz(t, f - t * CHUNKS) << (FP8 ? 3 : 4)));
+    doff2[i >> 1] |= o << (16 * (i & 1));
+  }
+  auto doff = [&](int i) -> uint32_t { return (doff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
 
   while (start < end) {
     const int64_t s0 = cu[b], s1 = cu[b + 1];
@@ -310,15 +338,19 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         f32x16 s = tile_scores(tile, kq, qf);
         // register r holds token 8(r/4) + 4g + r%4 of the tile; lane holds head `head`
         float mx = -__builtin_inff();
+        if constexpr (FP8) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tk = 8 * (r >> 2) + 4 * g + (r & 3);
-          float v = s[r];
-          if constexpr (FP8) v *= sc[tk];
-          v = tk < valid ? v : -__builtin_inff();
-          s[r] = v;
-          mx = fmaxf(mx, v);
+          for (int r = 0; r < 16; ++r) s[r] *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
         }
+        if (valid < TT) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tk = 8 * (r >> 2) + 4 * g + (r & 3);
+            s[r] = tk < valid ? s[r] : -__builtin_inff();
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         if (!have_ref) { m_ref = mx; have_ref = true; }
         m_seg = fmaxf(m_seg, mx);
@@ -334,46 +366,80 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         }
         rs += __shfl_xor(rs, 32, 64);
         l_run += rs;
-        // O^T += V^T P^T
+        // O^T += V^T P^T: 32 MFMAs (kk, cb), each A operand from two transposing LDS reads issued
+        // LP MFMAs ahead (program order is the schedule around volatile asm). O stays in AGPRs
+        // ("a" constraint). Per-tile lane bases are opaque so the per-column-block offsets fold
+        // into the reads' immediate field.
+        uint32_t vb[2][2][2];
+        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 pk = kk == 0 ? pk0 : pk1;
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            // tile-dependent part in a scalar register so the per-lane part stays a few bases
-            const uint32_t sb = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 128u * (cb >> 1));
-            const uint32_t ia = vq[kk][0][cb & 1] + sb;
-            const uint32_t ib = vq[kk][1][cb & 1] + sb;
-            const u32x2 x0 = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
-            const u32x2 x1 = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
-            const u32x4 av = {x0.x, x0.y, x1.x, x1.y};
-            O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk, O[cb], 0, 0, 0);
-          }
+          for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+              vb[kk][ab][par] = tb + vq[kk][ab][par];
+              asm volatile("" : "+v"(vb[kk][ab][par]));
+            }
+        constexpr int NPV = 2 * CB, LP = 3;
+        u32x4 av[NPV];
+        auto ldv = [&](int j) __attribute__((always_inline)) {
+          const int kk = j / CB, cb = j % CB;
+          const uint32_t ia = vb[kk][0][cb & 1] + 128u * (cb >> 1);
+          const uint32_t ib = vb[kk][1][cb & 1] + 128u * (cb >> 1);
+          const u32x2 x0 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
+          const u32x2 x1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
+          av[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
+        };
+#pragma unroll
+        for (int j = 0; j < LP; ++j) ldv(j);
+        // 5 wait states: P was just written by VALU and is read by the first MFMA
+        asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(O[0]) : "v"(av[0]), "v"(pk0));
+        ldv(LP);
+#pragma unroll
+        for (int j = 1; j < NPV - 1; ++j) {
+          const int kk = j / CB, cb = j % CB;
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(O[cb]) : "v"(av[j]), "v"(kk ? pk1 : pk0));
+          if (j + LP < NPV) ldv(j + LP);
         }
+        // the last MFMA is followed by 24 wait states so any later read of O is safe
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(O[CB - 1]) : "v"(av[NPV - 1]), "v"(pk1));
       };
 
-      if constexpr (!FP8) {
+    if constexpr (!FP8) {
         // bf16: 16-byte chunks go straight from HBM into LDS; two tiles stay in flight.
         const uint8_t* rows_b = (const uint8_t*)cache.rows;
         auto issue = [&](int it) {
-          // opaque copy of the thread id: keeps the per-chunk addresses from being hoisted out of
-          // the tile loop (spilled, then reloaded with vmcnt waits that would drain the prefetch)
-          int tid_o = tid;
-          asm volatile("" : "+v"(tid_o));
           const int64_t tt0 = t0 + (int64_t)it * TT;
           const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
-          rows.tile(tt0, tt0 + last);
           const uint32_t dst = __builtin_amdgcn_readfirstlane(
               (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
+          uint32_t off[LOADS];
 #pragma unroll
           for (int i = 0; i < LOADS; ++i) {
-            const int f = i * 256 + tid_o, t = f / CHUNKS;
-            const int ch = swz(t, f - t * CHUNKS);
-            const uint8_t* src = rows.tile_row(rows_b, tt0, t < last ? t : last, ROWB) + (ch << 4);
-            dma16(src, dst + i * 4096);
+            off[i] = doff(i);
+            if (last < TT - 1) {  // partial tile: rows past the segment re-read its last row
+              const int t = (int)(off[i] / ROWB);
+              if (t > last) off[i] -= (uint32_t)(t - last) * ROWB;
+            }
+          }
+          if constexpr (!PAGED) {
+            const uint8_t* base = rows_b + (rows.base_row + tt0) * ROWB;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) dma16_s(base, off[i], dst + i * 4096);
+          } else {
+            // a 32-row tile spans at most two pages: rows before `split` live in the first one
+            rows.tile(tt0, tt0 + last);
+            const int ps = 1 << rows.ps_shift;
+            const int s_in = (int)(tt0 & (ps - 1));
+            const uint32_t split = (uint32_t)(ps - s_in) * ROWB;
+            const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * ROWB;
+            const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * ROWB - (int64_t)split;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) dma16((off[i] < split ? B0 : B1) + off[i], dst + i * 4096);
           }
         };
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
