@@ -226,14 +226,14 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
                                                       float* __restrict__ o_part) {
   using namespace v2;
   constexpr bool FP8 = CDT == MLA_FP8_E4M3;
-  constexpr int NBUF = FP8 ? 2 : 3;
+  constexpr int NBUF = FP8 ? 2 : 4;  // bf16: three tiles (108 KB) in flight behind the one in use
   // Softmax reference: per head, the maximum of the segment's first tile. Later probabilities are
   // exp2(s - m_ref) <= 2^HEAD (fine in float32/bf16), so the accumulators are never rescaled. A
   // score above m_ref + HEAD makes the workgroup run the segment once more with the segment's
   // true maximum as the reference (exact; at most one re-run).
   constexpr float HEAD = 64.f;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
-  __shared__ float lds_sc[NBUF][TT];
+  __shared__ float lds_sc[FP8 ? NBUF : 1][TT];
   __shared__ int redo_flag;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -296,6 +296,48 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
     Rows<PAGED> rows;
     rows.init(cache, b);
 
+    const int64_t n = t1 - t0;
+    const int ntiles = (int)((n + TT - 1) / TT);
+    // bf16: 16-byte chunks go straight from HBM into LDS (tile it -> buffer it % NBUF).
+    const uint8_t* rows_b = (const uint8_t*)cache.rows;
+    auto issue = [&](int it) {
+      const int64_t tt0 = t0 + (int64_t)it * TT;
+      const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
+      uint32_t off[LOADS];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        off[i] = doff(i);
+        if (last < TT - 1) {  // partial tile: rows past the segment re-read its last row
+          const int t = (int)(off[i] / ROWB);
+          if (t > last) off[i] -= (uint32_t)(t - last) * ROWB;
+        }
+      }
+      if constexpr (!PAGED) {
+        const uint8_t* base = rows_b + (rows.base_row + tt0) * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) dma16_s(base, off[i], dst + i * 4096);
+      } else {
+        // a 32-row tile spans at most two pages: rows before `split` live in the first one
+        rows.tile(tt0, tt0 + last);
+        const int ps = 1 << rows.ps_shift;
+        const int s_in = (int)(tt0 & (ps - 1));
+        const uint32_t split = (uint32_t)(ps - s_in) * ROWB;
+        const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * ROWB;
+        const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * ROWB - (int64_t)split;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) dma16((off[i] < split ? B0 : B1) + off[i], dst + i * 4096);
+      }
+    };
+    // the first three tiles are requested before the query is read, so both latencies overlap
+    auto prime = [&]() {
+      if constexpr (!FP8) {
+        for (int it = 0; it < 3 && it < ntiles; ++it) issue(it);
+      }
+    };
+    prime();
+
     // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
     bf16x8 qf[KSTEPS];
     {
@@ -315,8 +357,6 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
       }
     }
 
-    const int64_t n = t1 - t0;
-    const int ntiles = (int)((n + TT - 1) / TT);
     auto valid_of = [&](int it) -> int {
       const int64_t r = n - (int64_t)it * TT;
       return r < TT ? (int)r : TT;
@@ -410,44 +450,12 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
       };
 
     if constexpr (!FP8) {
-        // bf16: 16-byte chunks go straight from HBM into LDS; two tiles stay in flight.
-        const uint8_t* rows_b = (const uint8_t*)cache.rows;
-        auto issue = [&](int it) {
-          const int64_t tt0 = t0 + (int64_t)it * TT;
-          const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
-          const uint32_t dst = __builtin_amdgcn_readfirstlane(
-              (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
-          uint32_t off[LOADS];
-#pragma unroll
-          for (int i = 0; i < LOADS; ++i) {
-            off[i] = doff(i);
-            if (last < TT - 1) {  // partial tile: rows past the segment re-read its last row
-              const int t = (int)(off[i] / ROWB);
-              if (t > last) off[i] -= (uint32_t)(t - last) * ROWB;
-            }
-          }
-          if constexpr (!PAGED) {
-            const uint8_t* base = rows_b + (rows.base_row + tt0) * ROWB;
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) dma16_s(base, off[i], dst + i * 4096);
-          } else {
-            // a 32-row tile spans at most two pages: rows before `split` live in the first one
-            rows.tile(tt0, tt0 + last);
-            const int ps = 1 << rows.ps_shift;
-            const int s_in = (int)(tt0 & (ps - 1));
-            const uint32_t split = (uint32_t)(ps - s_in) * ROWB;
-            const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * ROWB;
-            const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * ROWB - (int64_t)split;
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) dma16((off[i] < split ? B0 : B1) + off[i], dst + i * 4096);
-          }
-        };
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        issue(0);
-        if (ntiles > 1) issue(1);
+        if (pass > 0) prime();
         for (int it = 0; it < ntiles; ++it) {
-          if (it + 1 < ntiles) vm_wait_barrier<LOADS>(); else vm_wait_barrier<0>();
-          if (it + 2 < ntiles) issue(it + 2);
+          if (it + 2 < ntiles) vm_wait_barrier<2 * LOADS>();
+          else if (it + 1 < ntiles) vm_wait_barrier<LOADS>();
+          else vm_wait_barrier<0>();
+          if (it + 3 < ntiles) issue(it + 3);
           compute(lds + (it % NBUF) * TILEB, nullptr, valid_of(it));
         }
       } else {
@@ -699,11 +707,49 @@ __global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t
     if (lse_out && lane == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
   }
   __syncthreads();
-  for (int e = tid; e < nh * d_c; e += 256) {
-    const int hh = e / d_c;
-    float acc = 0.f;
-    for (int i = 0; i < np; ++i) acc += wts[i][hh] * o_part[((int64_t)slots[i] * n_h + h0) * d_c + e];
-    dst[e] = acc;
+  // every thread owns up to 4 float4 outputs per round; the loads of 4 pieces are issued before
+  // their products are accumulated (piece order fixed, so the sum order is the same everywhere)
+  const int nv4 = nh * d_c / 4;
+  const float4* src = (const float4*)(o_part + (int64_t)h0 * d_c);
+  const int64_t pstride = (int64_t)n_h * d_c / 4;  // float4 per piece slot
+  float4* dst4 = (float4*)dst;
+  for (int e0 = 0; e0 < nv4; e0 += 1024) {
+    int idx[4];
+    float4 acc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      idx[v] = e0 + tid + 256 * v;
+      acc[v] = float4{0.f, 0.f, 0.f, 0.f};
+    }
+    int i = 0;
+    for (; i + 4 <= np; i += 4) {
+      float4 x[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          x[k][v] = idx[v] < nv4 ? src[(int64_t)slots[i + k] * pstride + idx[v]] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float wk = wts[i + k][(idx[v] < nv4 ? idx[v] : 0) * 4 / d_c];
+          acc[v].x += wk * x[k][v].x; acc[v].y += wk * x[k][v].y;
+          acc[v].z += wk * x[k][v].z; acc[v].w += wk * x[k][v].w;
+        }
+    }
+    for (; i < np; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (idx[v] >= nv4) continue;
+        const float4 x = src[(int64_t)slots[i] * pstride + idx[v]];
+        const float wk = wts[i][idx[v] * 4 / d_c];
+        acc[v].x += wk * x.x; acc[v].y += wk * x.y; acc[v].z += wk * x.z; acc[v].w += wk * x.w;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (idx[v] < nv4) dst4[idx[v]] = acc[v];
   }
 }
 

@@ -7,10 +7,11 @@
 //
 // All are "skinny" products Y[n][m] = sum_k W(m, k) X[n][k] with n over the batch (tens of rows)
 // and W read exactly once from HBM, so they are bound by weight bandwidth. bf16 weights run on
-// MFMA: W is the A operand, loaded from global memory directly in MFMA layout; float32
-// activations are split into hi + lo bf16 parts (x = hi + lo holds 16 significand bits), costing
-// a second MFMA that is free under the bandwidth bound and keeping the activation error near
-// float32 instead of bf16. float32 / float16 weights run on a tiled float32 VALU kernel.
+// MFMA: W (the A operand) streams through a ring of LDS stages fed by direct global->LDS copies,
+// several stages ahead of the math; float32 activations are split into hi + lo bf16 parts
+// (x = hi + lo holds 16 significand bits), costing a second MFMA that is free under the
+// bandwidth bound and keeping the activation error near float32 instead of bf16. float32 /
+// float16 weights run on a tiled float32 VALU kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,25 +21,47 @@ namespace mla {
 static size_t al256h(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace gm {
-constexpr int SPLIT_K1 = 8;   // split-K of the first projection (K = d, few outputs)
-constexpr int SPLIT_K5 = 4;   // split-K of the output projection (K = n_h d_h)
-constexpr int MAXB = 128;     // batch rows per MFMA launch
+constexpr int MAXB = 128;      // batch rows per MFMA launch
+constexpr int MT = 128;        // output rows per workgroup (4 waves x 32)
+constexpr int KC = 64;         // k per pipeline stage
+constexpr int TARGET_WG = 256; // workgroups aimed for when choosing the K split
+}
+
+// K split of a launch with `mtiles` row tiles, S stages of KC and Z batched problems: enough
+// workgroups to cover the chip once, never more slices than stages.
+static int split_for(int mtiles, int S, int Z) {
+  int sk = gm::TARGET_WG / (mtiles * Z);
+  if (sk < 1) sk = 1;
+  if (sk > S) sk = S;
+  return sk;
+}
+static int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+struct QSplits { int sk1; };
+static QSplits q_splits(const mla_dims& d) { return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT), d.d / gm::KC, 1)}; }
+struct OSplits { int sk4, sk5; };
+static OSplits o_splits(const mla_dims& d) {
+  return {split_for(cdiv(d.d_h, gm::MT), d.d_c / gm::KC, d.n_h), split_for(cdiv(d.d, gm::MT), d.n_h * d.d_h / gm::KC, 1)};
 }
 
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
   AbsorbQLayout L;
+  const int nb = B < gm::MAXB ? B : gm::MAXB;
   L.off_cq = 0;
   L.off_qc = al256h((size_t)B * d.d_cq * 4);
   L.off_part = L.off_qc + al256h((size_t)B * d.n_h * d.d_h * 4);
-  L.part_floats = (size_t)gm::SPLIT_K1 * B * (d.d_cq + d.d_c + d.d_r);
+  L.part_floats = (size_t)q_splits(d).sk1 * nb * (d.d_cq + d.d_c + d.d_r);
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
 }
 AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B) {
   AbsorbOutLayout L;
+  const int nb = B < gm::MAXB ? B : gm::MAXB;
+  const OSplits sp = o_splits(d);
   L.off_o = 0;
   L.off_part = al256h((size_t)B * d.n_h * d.d_h * 4);
-  L.part_floats = (size_t)gm::SPLIT_K5 * B * d.d;
+  const size_t p4 = (size_t)sp.sk4 * d.n_h * nb * d.d_h, p5 = (size_t)sp.sk5 * nb * d.d;
+  L.part_floats = p4 > p5 ? p4 : p5;
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
 }
@@ -60,128 +83,185 @@ __device__ __forceinline__ int seg_of(const Seg& s, int m) {
   return k;
 }
 
+// 16-byte global -> LDS copy per lane: uniform 64-bit base in SGPRs + 32-bit lane offset; the LDS
+// destination is the wave-uniform `lds_addr` + 16 * lane. Written as asm so the compiler does not
+// wait for every outstanding copy before each LDS read; the kernel counts them itself.
+__device__ __forceinline__ void g2l16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+// At most N copies of this wave still in flight, this wave's LDS reads done, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // ================================================================================================
-// MFMA bf16 skinny GEMM. Workgroup = 4 waves = one 64-row tile of the stacked output over one
-// K slice; the 4 waves split that slice and are summed through LDS. Each wave keeps
-// 2 (m-blocks of 32) x NB (n-blocks of 32) accumulators. The reduction over k is permuted per
-// 64-wide group so that each lane reads 64 contiguous bytes of its weight row and 128 contiguous
-// bytes (float32) of its activation row: lane half g of a group owns k in [32g, 32g + 32), split
-// into the four 8-wide MFMA k-slots of the group's four steps. Both operands use the same
-// permutation, so the products pair the same k.
-//   XF32 = true: X is float32, split hi/lo (2 MFMAs per step); false: X is bf16.
-//   split_k > 1: the workgroup writes its sum to part[ky][n][m] for a later ordered reduction;
-//   otherwise it writes Y directly.
+// Weight-streaming MFMA GEMM: Y[n][m] = sum_k W(m, k) X[n][k], W bf16 row-major (lda = K).
+// Workgroup = 128 output rows (wave w: rows 32w..32w+31) x all N <= 32*NB columns, over one K
+// slice. The slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the
+// matching X columns) filled by direct global->LDS copies, NS-1 stages ahead of the MFMAs.
+// LDS rows are XOR-swizzled in 16-byte chunks so the MFMA fragment reads are conflict-free.
+// The reduction index is permuted inside each 64-k stage: in step st, lane half g supplies
+// k = 32g + 8st + 0..7 for both operands (the same real k on both sides of every product).
+//   XF32: X is float32, split on the fly into bf16 hi + lo (2 MFMAs, ~16 significand bits);
+//         otherwise X is bf16.
+//   split_k > 1: partial sums go to part[(ky * Z + z) * N + n][m] for the ordered reduction.
 template <int NB, bool XF32>
-__global__ __launch_bounds__(256) void k_gemm_mfma(Seg seg, int N, int K, const void* __restrict__ Xv,
-                                                   int64_t ldx, int split_k, float* __restrict__ part,
-                                                   int Mtot, int64_t zW, int64_t zX, int64_t zY) {
-  __shared__ float red[4][64 * 32 * NB];  // per-wave partial tiles [m 64][n 32*NB]
+struct WCfg {
+  static constexpr int WB = gm::MT * gm::KC * 2;                 // W bytes per stage (16 KB)
+  static constexpr int XROW = gm::KC * (XF32 ? 4 : 2);            // X bytes per row per stage
+  static constexpr int XB = NB * 32 * XROW;                       // X bytes per stage
+  static constexpr int SB = WB + XB;
+  static constexpr int NS = (147456 / SB) < 6 ? (147456 / SB) : 6;
+  static constexpr int DW = WB / 4096;                            // copies per thread per stage
+  static constexpr int DX = XB / 4096;
+};
+
+template <int NB, bool XF32>
+__global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const void* __restrict__ Xv,
+                                                  int64_t ldx, int split_k, float* __restrict__ part,
+                                                  int Mtot, int64_t zW, int64_t zX, int64_t zY) {
+  using C = WCfg<NB, XF32>;
+  constexpr int MT = gm::MT, KC = gm::KC, NS = C::NS, DT = C::DW + C::DX;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * C::SB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int mt = blockIdx.x;                 // 64-row tile of the stacked output
-  const int ky = blockIdx.y;                 // K slice
-  const int z = blockIdx.z;                  // batched (per-head) problems
-  const int m_base = mt * 64;
+  const int mt = blockIdx.x, ky = blockIdx.y, z = blockIdx.z, Z = gridDim.z;
+  const int m_base = mt * MT;
   const int s = seg_of(seg, m_base);
-  const int lda = K;
-  const uint16_t* W = (const uint16_t*)seg.W[s] + (int64_t)z * zW + (int64_t)(m_base - seg.m0[s]) * lda;
+  const int r0 = m_base - seg.m0[s];                  // first tile row inside its segment
+  const int seg_rows = seg.m0[s + 1] - seg.m0[s];
+  const int S = K / KC;
+  const int st0 = (int)((int64_t)S * ky / split_k), st1 = (int)((int64_t)S * (ky + 1) / split_k);
+  const int ns = st1 - st0;
+  constexpr int ESX = XF32 ? 4 : 2;
+  const uint8_t* Wb = (const uint8_t*)seg.W[s] + ((int64_t)z * zW + (int64_t)r0 * K) * 2;
+  const uint8_t* Xb = (const uint8_t*)Xv + (int64_t)z * zX * ESX;
 
-  // k groups of 64 assigned to (slice, wave)
-  const int KG = K / 64;
-  const int part_id = ky * 4 + w, nparts = split_k * 4;
-  const int g0 = (int)((int64_t)KG * part_id / nparts), g1 = (int)((int64_t)KG * (part_id + 1) / nparts);
-
-  f32x16 acc[2][NB];
+  // Copy plan: thread tid fills 16-byte LDS slots p = 256 i + tid. W slot p: row p / 8, physical
+  // chunk p % 8, which holds logical chunk (p % 8) ^ ((row / 2) % 8). X slot (bf16): same with
+  // 8 chunks per row; X slot (float32): 16 chunks per row, logical chunk (p % 16) ^ (row % 16).
+  // Rows past the segment / past N re-read the last valid row (their results are dropped).
+  uint32_t wofs[C::DW], xofs[C::DX];
+  {
+    const int wc = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-
-  for (int kg = g0; kg < g1; ++kg) {
-    const int kb = kg * 64 + 32 * g;
-    // A fragments: rows l32 and 32 + l32, 32 contiguous k each (4 x 16 bytes)
-    u32x4 a[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4* src = (const u32x4*)(W + (int64_t)(32 * i + l32) * lda + kb);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) a[i][st] = src[st];
+    for (int i = 0; i < C::DW; ++i) {
+      int row = i * 32 + (tid >> 3);
+      if (row > seg_rows - r0 - 1) row = seg_rows - r0 - 1;
+      wofs[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(wc << 4);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int n = 32 * j + l32;
-      const bool nv = n < N;
-      bf16x8 bh[4], bl[4];
-      if constexpr (XF32) {
-        const float* xs = (const float*)Xv + (int64_t)z * zX + (int64_t)(nv ? n : 0) * ldx + kb;
+    for (int i = 0; i < C::DX; ++i) {
+      const int p = i * 256 + tid;
+      int row, c;
+      if constexpr (XF32) { row = p >> 4; c = (p & 15) ^ (row & 15); }
+      else { row = p >> 3; c = (p & 7) ^ ((row >> 1) & 7); }
+      if (row > N - 1) row = N - 1;
+      xofs[i] = (uint32_t)((int64_t)row * ldx * ESX) + (uint32_t)(c << 4);
+    }
+  }
+  auto issue = [&](int j) {
+    const int kst = (st0 + j) * KC;
+    uint8_t* buf = lds + (j % NS) * C::SB;
+    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
+    const uint8_t* wsrc = Wb + (int64_t)kst * 2;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          f32x4 x0 = nv ? *(const f32x4*)(xs + 8 * st) : f32x4{};
-          f32x4 x1 = nv ? *(const f32x4*)(xs + 8 * st + 4) : f32x4{};
+    for (int i = 0; i < C::DW; ++i) g2l16(wsrc, wofs[i], wl + i * 4096);
+    const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
+    const uint8_t* xsrc = Xb + (int64_t)kst * ESX;
+#pragma unroll
+    for (int i = 0; i < C::DX; ++i) g2l16(xsrc, xofs[i], xl + i * 4096);
+  };
+
+  // fragment read offsets inside a stage
+  const int key8 = (l32 >> 1) & 7;
+  uint32_t aoff[4], boff[4], bofx[4][2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    aoff[st] = (uint32_t)((32 * w + l32) * 128 + (((4 * g + st) ^ key8) << 4));
+    boff[st] = (uint32_t)(C::WB + l32 * 128 + (((4 * g + st) ^ key8) << 4));
+    bofx[st][0] = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * st) ^ (l32 & 15)) << 4));
+    bofx[st][1] = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * st + 1) ^ (l32 & 15)) << 4));
+  }
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
+
+  for (int j = 0; j < NS - 1 && j < ns; ++j) issue(j);
+  for (int j = 0; j < ns; ++j) {
+    const int ahead = (ns - 1 - j) < (NS - 2) ? (ns - 1 - j) : (NS - 2);
+    switch (ahead) {
+      case 0: wait_copies_barrier<0>(); break;
+      case 1: wait_copies_barrier<DT>(); break;
+      case 2: wait_copies_barrier<(NS > 3 ? 2 * DT : 0)>(); break;
+      case 3: wait_copies_barrier<(NS > 4 ? 3 * DT : 0)>(); break;
+      default: wait_copies_barrier<(NS > 5 ? 4 * DT : 0)>(); break;
+    }
+    if (j + NS - 1 < ns) issue(j + NS - 1);
+    const uint8_t* buf = lds + (j % NS) * C::SB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 a = *(const bf16x8*)(buf + aoff[st]);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        if constexpr (XF32) {
+          const f32x4 x0 = *(const f32x4*)(buf + bofx[st][0] + jb * 32 * 256);
+          const f32x4 x1 = *(const f32x4*)(buf + bofx[st][1] + jb * 32 * 256);
+          bf16x8 bh, bl;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
-            bh[st][e] = h0; bh[st][4 + e] = h1;
-            bl[st][e] = (__bf16)(x0[e] - (float)h0);
-            bl[st][4 + e] = (__bf16)(x1[e] - (float)h1);
+            const __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
+            bh[e] = h0; bh[4 + e] = h1;
+            bl[e] = (__bf16)(x0[e] - (float)h0);
+            bl[4 + e] = (__bf16)(x1[e] - (float)h1);
           }
-        }
-      } else {
-        const uint16_t* xs = (const uint16_t*)Xv + (int64_t)z * zX + (int64_t)(nv ? n : 0) * ldx + kb;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          u32x4 v = nv ? *(const u32x4*)(xs + 8 * st) : u32x4{};
-          bh[st] = __builtin_bit_cast(bf16x8, v);
-        }
-      }
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          bf16x8 av = __builtin_bit_cast(bf16x8, a[i][st]);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh[st], acc[i][j], 0, 0, 0);
-          if constexpr (XF32) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl[st], acc[i][j], 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[jb], 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[jb], 0, 0, 0);
+        } else {
+          const bf16x8 b = *(const bf16x8*)(buf + boff[st] + jb * 32 * 128);
+          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
         }
       }
     }
   }
-  // accumulator layout: lane holds column n = 32j + l32, rows m = 32i + 8(r/4) + 4g + r%4
-  float* my = red[w];
+  // accumulator: lane holds column n = 32 jb + l32, rows 32w + 8(r/4) + 4g + r%4 (4 consecutive)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int n = 32 * j + l32;
-        my[m * (32 * NB) + n] = acc[i][j][r];
-      }
-  __syncthreads();
-  for (int e = tid; e < 64 * 32 * NB; e += 256) {
-    const int m = e / (32 * NB), n = e % (32 * NB);
+  for (int jb = 0; jb < NB; ++jb) {
+    const int n = 32 * jb + l32;
     if (n >= N) continue;
-    const float v = red[0][e] + red[1][e] + red[2][e] + red[3][e];
-    const int mg = m_base + m;
-    if (split_k > 1) {
-      part[((int64_t)ky * N + n) * Mtot + mg] = v;
-    } else {
-      float* Y = seg.Y[s] + (int64_t)z * zY;
-      Y[(int64_t)n * seg.ldy[s] + (mg - seg.m0[s])] = v;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int mloc = 32 * w + 8 * r4 + 4 * g;
+      if (r0 + mloc >= seg_rows) continue;
+      const f32x4 v = {acc[jb][4 * r4], acc[jb][4 * r4 + 1], acc[jb][4 * r4 + 2], acc[jb][4 * r4 + 3]};
+      if (split_k > 1) {
+        *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m_base + mloc) = v;
+      } else {
+        *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)n * seg.ldy[s] + r0 + mloc) = v;
+      }
     }
   }
 }
 
-// Ordered split-K reduction: Y[n][m] = sum_{ky} part[ky][n][m], scattered to the segments.
+// Ordered split-K reduction: Y[n][m] = sum_{ky} part[ky][n][m] (4 consecutive m per thread),
+// scattered to the segments; blockIdx.y = batched problem z.
 __global__ __launch_bounds__(256) void k_splitk_reduce(Seg seg, int N, int Mtot, int split_k,
-                                                       const float* __restrict__ part) {
+                                                       const float* __restrict__ part, int64_t zY) {
+  const int z = blockIdx.y, Z = gridDim.y;
+  const int M4 = Mtot / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)N * Mtot) return;
-  const int n = (int)(e / Mtot), m = (int)(e % Mtot);
-  float v = 0.f;
-  for (int k = 0; k < split_k; ++k) v += part[(int64_t)k * N * Mtot + e];
+  if (e >= (int64_t)N * M4) return;
+  const int n = (int)(e / M4), m = (int)(e % M4) * 4;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < split_k; ++k) {
+    const f32x4 x = *(const f32x4*)(part + ((int64_t)(k * Z + z) * N + n) * Mtot + m);
+    v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
+  }
   const int s = seg_of(seg, m);
-  seg.Y[s][(int64_t)n * seg.ldy[s] + (m - seg.m0[s])] = v;
+  *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)n * seg.ldy[s] + (m - seg.m0[s])) = v;
 }
 
 // ================================================================================================
@@ -190,21 +270,46 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(Seg seg, int N, int Mtot,
 // transposing LDS load (4 consecutive e of one column per lane). Workgroup = (head, 128 columns);
 // wave w owns 32 columns; MFMA D[c][b] = sum_e A[c][e] X^T[e][b].
 namespace absq {
-constexpr int DH = 128, TC = 128, PITCH = 136;  // bf16 elements per LDS row (padded)
+constexpr int DH = 128, TC = 128, PITCH = 136;  // bf16 elements per W^UK row in LDS (padded)
+constexpr int XP = DH + 4;                      // floats per q^C row in LDS (padded)
 }
+// One round trip per workgroup: the W^UK tile and this head's q^C rows (all N of them) are
+// requested together, stored to LDS, then the 8 k-steps run from LDS.
 template <int NB>
 __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, const uint16_t* __restrict__ W_uk,
                                                    const float* __restrict__ qC, float* __restrict__ q_lat) {
   using namespace absq;
   __shared__ __attribute__((aligned(16))) uint16_t tile[DH * PITCH];
+  __shared__ __attribute__((aligned(16))) float xs[NB * 32 * XP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int i = blockIdx.y;              // head
   const int c0 = blockIdx.x * TC;        // column tile
-  // stage W^UK[i*128 .. +128][c0 .. c0+128] (row-major, 16-byte pieces)
-  for (int f = tid; f < DH * TC / 8; f += 256) {
-    const int e = f / (TC / 8), cc = (f % (TC / 8)) * 8;
-    *(u32x4*)(tile + e * PITCH + cc) = *(const u32x4*)(W_uk + ((int64_t)i * DH + e) * d_c + c0 + cc);
+  {
+    // W^UK[i*128 .. +128][c0 .. c0+128]: 2048 16-byte pieces, 8 per thread;
+    // q^C[n][i*128 .. +128] for n < 32 NB: 32 NB * 32 pieces, 4 NB per thread
+    u32x4 wv[8];
+    f32x4 xv[4 * NB];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = k * 256 + tid, e = f >> 4, cc = (f & 15) * 8;
+      wv[k] = *(const u32x4*)(W_uk + ((int64_t)i * DH + e) * d_c + c0 + cc);
+    }
+#pragma unroll
+    for (int k = 0; k < 4 * NB; ++k) {
+      const int f = k * 256 + tid, n = f >> 5, ee = (f & 31) * 4;
+      xv[k] = n < N ? *(const f32x4*)(qC + (int64_t)n * n_h * DH + (int64_t)i * DH + ee) : f32x4{};
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = k * 256 + tid, e = f >> 4, cc = (f & 15) * 8;
+      *(u32x4*)(tile + e * PITCH + cc) = wv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4 * NB; ++k) {
+      const int f = k * 256 + tid, n = f >> 5, ee = (f & 31) * 4;
+      *(f32x4*)(xs + n * XP + ee) = xv[k];
+    }
   }
   __syncthreads();
   const int j16 = lane & 15, h2 = (lane >> 4) & 1;
@@ -224,13 +329,10 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
     const bf16x8 a = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int n = 32 * j + l32;
-      const bool nv = n < N;
-      // B[e][n] = q^C[n][i*128 + e], e = 16ks + 8g + 0..7: first 4 from rows e0.., i.e. the slot
-      // order of the transposed read: slots 0-3 -> e = 16ks + 8g + 0..3, slots 4-7 -> +4..7.
-      const float* xs = qC + (int64_t)(nv ? n : 0) * n_h * DH + (int64_t)i * DH + 16 * ks + 8 * g;
-      f32x4 v0 = nv ? *(const f32x4*)xs : f32x4{};
-      f32x4 v1 = nv ? *(const f32x4*)(xs + 4) : f32x4{};
+      // B[e][n] = q^C[n][i*128 + e], e = 16ks + 8g + 0..7: slots 0-3 come from the first
+      // transposed read (rows e0..), slots 4-7 from the second (rows e0 + 4..).
+      const float* xr = xs + (32 * j + l32) * XP + 16 * ks + 8 * g;
+      const f32x4 v0 = *(const f32x4*)xr, v1 = *(const f32x4*)(xr + 4);
       bf16x8 bh, bl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -342,22 +444,25 @@ static bool mfma_dims_ok(const mla_dims& d) {
          d.d_h == absq::DH && (d.n_h * d.d_h) % 256 == 0;
 }
 
+template <int NB, bool XF32>
+static void wgemm_nb(hipStream_t st, dim3 grid, const Seg& sg, int N, int K, const void* X, int64_t ldx,
+                     int split_k, float* part, int Mtot, int64_t zW, int64_t zX, int64_t zY) {
+  hipLaunchKernelGGL((k_wgemm<NB, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+}
+
+// Y = W X over stacked segments (segment boundaries on multiples of gm::MT), N <= gm::MAXB.
 template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
                       float* part, int Z, int64_t zW, int64_t zX, int64_t zY) {
   const int Mtot = sg.m0[sg.nseg];
-  dim3 grid(Mtot / 64, split_k, Z);
-  if (N <= 32)
-    hipLaunchKernelGGL((k_gemm_mfma<1, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
-  else if (N <= 64)
-    hipLaunchKernelGGL((k_gemm_mfma<2, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
-  else if (N <= 96)
-    hipLaunchKernelGGL((k_gemm_mfma<3, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
-  else
-    hipLaunchKernelGGL((k_gemm_mfma<4, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  dim3 grid(cdiv(Mtot, gm::MT), split_k, Z);
+  if (N <= 32) wgemm_nb<1, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  else if (N <= 64) wgemm_nb<2, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  else wgemm_nb<4, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
   if (split_k > 1) {
-    const int64_t tot = (int64_t)N * Mtot;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, sg, N, Mtot, split_k, part);
+    const int64_t tot = (int64_t)N * (Mtot / 4);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((tot + 255) / 256), Z), dim3(256), 0, st, sg, N, Mtot,
+                       split_k, part, zY);
   }
 }
 
@@ -380,7 +485,7 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
       s1.Y[1] = kv_new + (int64_t)b0 * rw; s1.ldy[1] = rw;
       s1.Y[2] = kv_new + (int64_t)b0 * rw + d.d_c; s1.ldy[2] = rw;
       s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
-      mfma_gemm<false>(st, s1, nb, d.d, (const uint16_t*)h + (int64_t)b0 * d.d, d.d, gm::SPLIT_K1, part, 1, 0, 0, 0);
+      mfma_gemm<false>(st, s1, nb, d.d, (const uint16_t*)h + (int64_t)b0 * d.d, d.d, q_splits(d).sk1, part, 1, 0, 0, 0);
       // stage 2: [q^C | q^R raw] = [W^UQ; W^QR] c^Q
       Seg s2{};
       s2.W[0] = W_uq; s2.W[1] = W_qr;
@@ -425,13 +530,14 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
       Seg s4{};
       s4.W[0] = W_uv; s4.Y[0] = o + (int64_t)b0 * nhdh; s4.ldy[0] = nhdh;
       s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
-      mfma_gemm<true>(st, s4, nb, d.d_c, o_lat + (int64_t)b0 * d.n_h * d.d_c, (int64_t)d.n_h * d.d_c, 1, nullptr,
+      const OSplits sp = o_splits(d);
+      mfma_gemm<true>(st, s4, nb, d.d_c, o_lat + (int64_t)b0 * d.n_h * d.d_c, (int64_t)d.n_h * d.d_c, sp.sk4, part,
                       d.n_h, (int64_t)d.d_h * d.d_c, d.d_c, d.d_h);
       // u = W^O [o_1; ...; o_nh]
       Seg s5{};
       s5.W[0] = W_o; s5.Y[0] = u + (int64_t)b0 * d.d; s5.ldy[0] = d.d;
       s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, gm::SPLIT_K5, part, 1, 0, 0, 0);
+      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0);
     }
     return hipGetLastError();
   }

@@ -44,6 +44,9 @@ __device__ void store_row_block(const CacheArgs& c, int64_t ridx, const float* v
   }
 }
 
+// Grid (B, 1 + head blocks): blockIdx.y == 0 rotates k^R and appends the row; block y > 0
+// rotates the queries of heads [(y-1) * RH, y * RH). Each block forms the cos/sin table itself.
+constexpr int RH = 32;
 __global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, double base,
                                                       const int32_t* __restrict__ seq_lens,
                                                       float* __restrict__ q_pe, float* __restrict__ kv_new,
@@ -67,13 +70,17 @@ __global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, 
     sn[m] = (float)s;
   }
   __syncthreads();
-  // rotary queries of every head
-  float* q = q_pe + (int64_t)b * n_h * d_r;
-  for (int i = tid; i < n_h * half; i += blockDim.x) {
-    int h = i / half, m = i % half;
-    float x0 = q[h * d_r + 2 * m], x1 = q[h * d_r + 2 * m + 1];
-    q[h * d_r + 2 * m] = x0 * cs[m] - x1 * sn[m];
-    q[h * d_r + 2 * m + 1] = x0 * sn[m] + x1 * cs[m];
+  if (blockIdx.y > 0) {
+    // rotary queries of this block's heads; one thread per (head, pair), pairs read as float2
+    const int h0 = (blockIdx.y - 1) * RH;
+    const int nh = (n_h - h0) < RH ? (n_h - h0) : RH;
+    float2* q = (float2*)(q_pe + ((int64_t)b * n_h + h0) * d_r);
+    for (int i = tid; i < nh * half; i += blockDim.x) {
+      const int m = i % half;
+      const float2 x = q[i];
+      q[i] = float2{x.x * cs[m] - x.y * sn[m], x.x * sn[m] + x.y * cs[m]};
+    }
+    return;
   }
   // shared rotary key (after the latent in the row)
   float* kv = kv_new + (int64_t)b * rw;
@@ -123,7 +130,7 @@ hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float*
                        const CacheArgs* cache, hipStream_t st) {
   CacheArgs c = cache ? *cache : CacheArgs{};
   size_t smem = (size_t)(d.d_r + d.d_c + d.d_r + 4) * sizeof(float);
-  hipLaunchKernelGGL(k_rope_append, dim3(B), dim3(256), smem, st, d.n_h, d.d_c, d.d_r, d.rope_base,
+  hipLaunchKernelGGL(k_rope_append, dim3(B, 1 + (d.n_h + RH - 1) / RH), dim3(256), smem, st, d.n_h, d.d_c, d.d_r, d.rope_base,
                      seq_lens, q_pe, kv_new, c, cache ? 1 : 0);
   return hipGetLastError();
 }

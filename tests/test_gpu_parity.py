@@ -102,6 +102,32 @@ def test_stage_outputs():
             assert e < (1e-5 if key == "0" else 2e-4)
 
 
+@pytest.mark.parametrize("B", [33, 100, 130])
+def test_stage_outputs_wide_batch(B):
+    """Projection stages at batch widths that use every column-block count of the MFMA GEMMs
+    (33: two blocks with a ragged one, 100: four, 130: two launches of 128 + 2 rows)."""
+    case = _case("2", B, [5] * B)
+    d = mla.Dims.of(case.dims)
+    step = mla.DecodeStep(case.dims, B, 0)
+    mla.absorb_q(d, case.h, case.weights, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    o_lat = (torch.randn((B, case.dims.n_h, case.dims.d_c), generator=g) * 0.3).cuda()
+    mla.absorb_out(d, o_lat, case.weights["W_uv"], case.weights["W_o"], step.ws_o, step.u)
+    torch.cuda.synchronize()
+    W = weights64(case)
+    od = OracleDims.of(case.dims)
+    worst = 0.0
+    for b in range(B):
+        q_lat, _, row = absorbed_query(W, case.h[b].double().cpu().numpy(), 4, od)
+        u_ref = output_projection(W, o_lat[b].double().cpu().numpy(), od)
+        e = max(rel_l2(step.q_lat[b].double().cpu().numpy(), q_lat),
+                rel_l2(step.kv_new[b, :case.dims.d_c].double().cpu().numpy(), row[:case.dims.d_c]),
+                rel_l2(step.u[b].double().cpu().numpy(), u_ref))
+        worst = max(worst, e)
+    print(f"B={B} worst stage rel-L2 {worst:.2e}", flush=True)
+    assert worst < 2e-4
+
+
 def test_split_count_invariance():
     case = _case("2", 3, [700, 33, 250], stress=True)
     outs = []
