@@ -98,8 +98,7 @@ __device__ __forceinline__ void wait_copies_barrier() {
 
 // ================================================================================================
 // Weight-streaming MFMA GEMM: Y[n][m] = sum_k W(m, k) X[n][k], W bf16 row-major (lda = K).
-// Workgroup = 128 output rows (wave w: rows 32w..32w+31) x all N <= 32*NB columns, over one K
-// slice. The slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the
+// Workgroup = 128 output rows x all N <= 32*NB columns, over one K slice. The slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the
 // matching X columns) filled by direct global->LDS copies, NS-1 stages ahead of the MFMAs.
 // LDS rows are XOR-swizzled in 16-byte chunks so the MFMA fragment reads are conflict-free.
 // The reduction index is permuted inside each 64-k stage: in step st, lane half g supplies
@@ -175,20 +174,21 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
     for (int i = 0; i < C::DX; ++i) g2l16(xsrc, xofs[i], xl + i * 4096);
   };
 
-  // fragment read offsets inside a stage
+  // Wave w runs k-step w of every stage for all 128 rows (4 m-blocks) and all N columns; the
+  // four partial tiles are summed through LDS at the end. Fragment offsets inside a stage:
+  //   A (m-block mb): row 32 mb + l32, logical chunk 4g + w;  B (bf16): row 32 jb + l32, same
+  //   chunk;  B (float32): row 32 jb + l32, logical chunks 8g + 2w and 8g + 2w + 1.
   const int key8 = (l32 >> 1) & 7;
-  uint32_t aoff[4], boff[4], bofx[4][2];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    aoff[st] = (uint32_t)((32 * w + l32) * 128 + (((4 * g + st) ^ key8) << 4));
-    boff[st] = (uint32_t)(C::WB + l32 * 128 + (((4 * g + st) ^ key8) << 4));
-    bofx[st][0] = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * st) ^ (l32 & 15)) << 4));
-    bofx[st][1] = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * st + 1) ^ (l32 & 15)) << 4));
-  }
+  const uint32_t aoff = (uint32_t)(l32 * 128 + (((4 * g + w) ^ key8) << 4));
+  const uint32_t boff = (uint32_t)(C::WB + l32 * 128 + (((4 * g + w) ^ key8) << 4));
+  const uint32_t bofx0 = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * w) ^ (l32 & 15)) << 4));
+  const uint32_t bofx1 = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * w + 1) ^ (l32 & 15)) << 4));
 
-  f32x16 acc[NB];
+  f32x16 acc[4][NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[mb][j] = f32x16{};
 
   for (int j = 0; j < NS - 1 && j < ns; ++j) issue(j);
   for (int j = 0; j < ns; ++j) {
@@ -202,41 +202,65 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
     }
     if (j + NS - 1 < ns) issue(j + NS - 1);
     const uint8_t* buf = lds + (j % NS) * C::SB;
+    bf16x8 a[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 a = *(const bf16x8*)(buf + aoff[st]);
+    for (int mb = 0; mb < 4; ++mb) a[mb] = *(const bf16x8*)(buf + aoff + mb * 32 * 128);
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
-        if constexpr (XF32) {
-          const f32x4 x0 = *(const f32x4*)(buf + bofx[st][0] + jb * 32 * 256);
-          const f32x4 x1 = *(const f32x4*)(buf + bofx[st][1] + jb * 32 * 256);
-          bf16x8 bh, bl;
+    for (int jb = 0; jb < NB; ++jb) {
+      if constexpr (XF32) {
+        const f32x4 x0 = *(const f32x4*)(buf + bofx0 + jb * 32 * 256);
+        const f32x4 x1 = *(const f32x4*)(buf + bofx1 + jb * 32 * 256);
+        bf16x8 bh, bl;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
-            bh[e] = h0; bh[4 + e] = h1;
-            bl[e] = (__bf16)(x0[e] - (float)h0);
-            bl[4 + e] = (__bf16)(x1[e] - (float)h1);
-          }
-          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[jb], 0, 0, 0);
-          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[jb], 0, 0, 0);
-        } else {
-          const bf16x8 b = *(const bf16x8*)(buf + boff[st] + jb * 32 * 128);
-          acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
+          bh[e] = h0; bh[4 + e] = h1;
+          bl[e] = (__bf16)(x0[e] - (float)h0);
+          bl[4 + e] = (__bf16)(x1[e] - (float)h1);
         }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bh, acc[mb][jb], 0, 0, 0);
+          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bl, acc[mb][jb], 0, 0, 0);
+        }
+      } else {
+        const bf16x8 b = *(const bf16x8*)(buf + boff + jb * 32 * 128);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b, acc[mb][jb], 0, 0, 0);
       }
     }
   }
-  // accumulator: lane holds column n = 32 jb + l32, rows 32w + 8(r/4) + 4g + r%4 (4 consecutive)
+
+  // Sum of the four waves' tiles, one m-block at a time through two alternating LDS regions
+  // (wave-major, fixed order w = 0..3). Accumulator element r of lane (g, l32) is column
+  // n = 32 jb + l32, row 32 mb + 8(r/4) + 4g + r%4: four consecutive rows per r/4.
+  __syncthreads();  // every wave is done with the last stage
+  constexpr int RB = 4 * NB * 4 * 64;  // float4 slots per region (waves x blocks x r4 x lanes)
+  f32x4* red = (f32x4*)lds;
 #pragma unroll
-  for (int jb = 0; jb < NB; ++jb) {
-    const int n = 32 * jb + l32;
-    if (n >= N) continue;
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x4* reg = red + (mb & 1) * RB;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int mloc = 32 * w + 8 * r4 + 4 * g;
-      if (r0 + mloc >= seg_rows) continue;
-      const f32x4 v = {acc[jb][4 * r4], acc[jb][4 * r4 + 1], acc[jb][4 * r4 + 2], acc[jb][4 * r4 + 3]};
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        reg[((w * NB + jb) * 4 + r4) * 64 + lane] =
+            f32x4{acc[mb][jb][4 * r4], acc[mb][jb][4 * r4 + 1], acc[mb][jb][4 * r4 + 2], acc[mb][jb][4 * r4 + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int idx = q * 256 + tid;           // (jb, r4, lane) of one output float4
+      const int ln = idx & 63, r4 = (idx >> 6) & 3, jb = idx >> 8;
+      const int n = 32 * jb + (ln & 31);
+      const int mloc = 32 * mb + 8 * r4 + 4 * (ln >> 5);
+      f32x4 v = reg[(jb * 4 + r4) * 64 + ln];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        const f32x4 x = reg[((ww * NB + jb) * 4 + r4) * 64 + ln];
+        v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
+      }
+      if (n >= N || r0 + mloc >= seg_rows) continue;
       if (split_k > 1) {
         *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m_base + mloc) = v;
       } else {
