@@ -16,13 +16,18 @@
 
 namespace mla {
 
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 DecodeLayout decode_layout(const mla_dims& d, int B, int G) {
   DecodeLayout L;
   L.n_pieces = (int64_t)G + B - 1;
   L.off_cu = 0;
-  L.off_lse = ((size_t)(B + 1) * 8 + 255) & ~(size_t)255;
-  L.off_o = (L.off_lse + (size_t)L.n_pieces * d.n_h * 4 + 255) & ~(size_t)255;
-  L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;
+  L.off_fmt = al256((size_t)(B + 1) * 8);
+  L.off_plan = L.off_fmt + 256;
+  L.off_lse = al256(L.off_plan + (size_t)G * sizeof(RangePlan));
+  L.off_sc = al256(L.off_lse + (size_t)L.n_pieces * d.n_h * 4);
+  L.off_o = al256(L.off_sc + (size_t)L.n_pieces * d.n_h * 4);
+  L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;  // sized for float32 partials
   return L;
 }
 
@@ -33,9 +38,12 @@ __device__ __forceinline__ int64_t row_index(const CacheArgs& c, int b, int64_t 
 }
 
 // ------------------------------------------------------------------------------------------------
-// cu[b] = sum_{b' < b} seq_lens[b'] (int64), one block.
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seq_lens, int B,
-                                               int64_t* __restrict__ cu) {
+// Plan, one block: cu[b] = sum_{b' < b} seq_lens[b'] (int64), the partial-output format word, and
+// for every range p its interval, first sequence and that sequence's interval (so a decode
+// workgroup starts from a single record instead of a chain of dependent searches).
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seq_lens, int B, int G, int fmt,
+                                               int64_t* __restrict__ cu, int32_t* __restrict__ fmt_out,
+                                               RangePlan* __restrict__ plan) {
   __shared__ int64_t part[1024];
   __shared__ int64_t carry;
   const int tid = threadIdx.x;
@@ -57,7 +65,25 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seq_l
     if (tid == 1023) carry += part[1023];
     __syncthreads();
   }
-  if (tid == 0) cu[0] = 0;
+  if (tid == 0) { cu[0] = 0; *fmt_out = fmt; }
+  __syncthreads();  // cu is complete and visible to the whole block
+  const int64_t total = carry;
+  for (int p = tid; p < G; p += 1024) {
+    RangePlan r;
+    r.start = range_start(p, total, G);
+    r.end = range_start(p + 1, total, G);
+    int lo = 0, hi = B - 1;  // largest b with cu[b] <= start
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= r.start) lo = mid; else hi = mid - 1;
+    }
+    r.b = lo;
+    r.s0 = cu[lo];
+    r.s1 = cu[lo + 1];
+    r.pad0 = 0;
+    r.pad1 = 0;
+    plan[p] = r;
+  }
 }
 
 // Range assignment: workgroups are dispatched round-robin over the 8 XCDs; consecutive ranges
@@ -221,9 +247,11 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
 template <int CDT, bool PAGED>
 __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ q_lat,
                                                       const float* __restrict__ q_pe, CacheArgs cache,
-                                                      const int64_t* __restrict__ cu, int B, int G,
+                                                      const int64_t* __restrict__ cu,
+                                                      const RangePlan* __restrict__ plan, int G,
                                                       float qscale, float* __restrict__ lse_part,
-                                                      float* __restrict__ o_part) {
+                                                      float* __restrict__ sc_part,
+                                                      uint16_t* __restrict__ o_part) {
   using namespace v2;
   constexpr bool FP8 = CDT == MLA_FP8_E4M3;
   constexpr int NBUF = FP8 ? 2 : 4;  // bf16: three tiles (108 KB) in flight behind the one in use
@@ -234,15 +262,19 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
   constexpr float HEAD = 64.f;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
   __shared__ float lds_sc[FP8 ? NBUF : 1][TT];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[NH * TT * 2];  // P of the current tile, [head][token]
+  __shared__ float lds_l[NH];                                           // softmax denominators
+  __shared__ float lds_m[4][NH];                                        // per-wave max |O| per head
   __shared__ int redo_flag;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int p = range_for_block(blockIdx.x, G);
-  const int64_t total = cu[B];
-  int64_t start = range_start(p, total, G);
-  const int64_t end = range_start(p + 1, total, G);
+  const RangePlan rp = plan[p];
+  int64_t start = rp.start;
+  const int64_t end = rp.end;
   if (start >= end) return;
-  int b = first_seq(cu, B, start);
+  int b = rp.b;
+  int64_t s0 = rp.s0, s1 = rp.s1;
   const int head = 32 * w + l32;
 
   // Per-lane LDS byte offsets inside a tile. The swizzle only permutes the low 3 bits of a chunk
@@ -288,8 +320,12 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
   auto doff = [&](int i) -> uint32_t { return (doff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
 
   while (start < end) {
-    const int64_t s0 = cu[b], s1 = cu[b + 1];
-    if (s1 <= start) { ++b; continue; }
+    if (s1 <= start) {  // an empty sequence: move on
+      ++b;
+      s0 = cu[b];
+      s1 = cu[b + 1];
+      continue;
+    }
     const int64_t seg_end = end < s1 ? end : s1;
     const int64_t t0 = start - s0, t1 = seg_end - s0;
     const int64_t slot = (int64_t)p + b;
@@ -305,10 +341,18 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
       const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
+      // the packed offsets are re-read through an opaque copy at every call, so the compiler
+      // neither precomputes per-call offset sets (which it would have to spill) nor hoists them
+      uint32_t d2[(LOADS + 1) / 2];
+#pragma unroll
+      for (int i = 0; i < (LOADS + 1) / 2; ++i) {
+        d2[i] = doff2[i];
+        asm volatile("" : "+v"(d2[i]));
+      }
       uint32_t off[LOADS];
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        off[i] = doff(i);
+        off[i] = (d2[i >> 1] >> (16 * (i & 1))) & 0xffffu;
         if (last < TT - 1) {  // partial tile: rows past the segment re-read its last row
           const int t = (int)(off[i] / ROWB);
           if (t > last) off[i] -= (uint32_t)(t - last) * ROWB;
@@ -333,6 +377,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
     // the first three tiles are requested before the query is read, so both latencies overlap
     auto prime = [&]() {
       if constexpr (!FP8) {
+#pragma unroll 1
         for (int it = 0; it < 3 && it < ntiles; ++it) issue(it);
       }
     };
@@ -406,12 +451,22 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         }
         rs += __shfl_xor(rs, 32, 64);
         l_run += rs;
-        // O^T += V^T P^T: 32 MFMAs (kk, cb), each A operand from two transposing LDS reads issued
-        // LP MFMAs ahead (program order is the schedule around volatile asm). O stays in AGPRs
-        // ("a" constraint). Per-tile lane bases are opaque so the per-column-block offsets fold
-        // into the reads' immediate field.
+        // Publish P: head row `head` of lds_p holds the tile's 32 probabilities as four 16-byte
+        // chunks; chunk 2kk + g is this lane's pk<kk> (tokens 16kk + 8(j/4) + 4g + j%4 for slot
+        // j), stored at chunk position (2kk + g) ^ ((head / 4) % 4) (conflict-free reads below).
+        {
+          const int key = (head >> 2) & 3;
+          uint8_t* prow = lds_p + head * 64;
+          *(bf16x8*)(prow + ((g ^ key) << 4)) = pk0;
+          *(bf16x8*)(prow + (((2 + g) ^ key) << 4)) = pk1;
+        }
+        __syncthreads();
+        // O^T[128 columns of this wave x 128 heads] += V^T P^T: 32 MFMAs ordered (kk, hb, cb).
+        // A = V^T fragment of columns 128w + 32cb (two transposing LDS reads; the four of one kk
+        // are live together), B = P fragment of heads 32hb.. (one LDS read, one MFMA group
+        // ahead). O stays in AGPRs. Loads are placed in program order around the volatile MFMAs.
         uint32_t vb[2][2][2];
-        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile;
+        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 256u * w;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -421,32 +476,46 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
               vb[kk][ab][par] = tb + vq[kk][ab][par];
               asm volatile("" : "+v"(vb[kk][ab][par]));
             }
-        constexpr int NPV = 2 * CB, LP = 3;
-        u32x4 av[NPV];
-        auto ldv = [&](int j) __attribute__((always_inline)) {
-          const int kk = j / CB, cb = j % CB;
+        auto ldv = [&](int kk, int cb) __attribute__((always_inline)) -> u32x4 {
           const uint32_t ia = vb[kk][0][cb & 1] + 128u * (cb >> 1);
           const uint32_t ib = vb[kk][1][cb & 1] + 128u * (cb >> 1);
           const u32x2 x0 = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
           const u32x2 x1 = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
-          av[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
+          return u32x4{x0.x, x0.y, x1.x, x1.y};
         };
+        auto ldp = [&](int kk, int hb) __attribute__((always_inline)) -> bf16x8 {
+          const int hr = 32 * hb + l32;
+          return *(const bf16x8*)(lds_p + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
+        };
+        u32x4 av[4];
+        bf16x8 pbc, pbn;
 #pragma unroll
-        for (int j = 0; j < LP; ++j) ldv(j);
-        // 5 wait states: P was just written by VALU and is read by the first MFMA
-        asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(O[0]) : "v"(av[0]), "v"(pk0));
-        ldv(LP);
+        for (int cb = 0; cb < 4; ++cb) av[cb] = ldv(0, cb);
+        pbc = ldp(0, 0);
 #pragma unroll
-        for (int j = 1; j < NPV - 1; ++j) {
-          const int kk = j / CB, cb = j % CB;
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(O[cb]) : "v"(av[j]), "v"(kk ? pk1 : pk0));
-          if (j + LP < NPV) ldv(j + LP);
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            const bool last_group = kk == 1 && hb == 3;
+            if (!last_group) pbn = ldp(hb == 3 ? kk + 1 : kk, hb == 3 ? 0 : hb + 1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              if (last_group && cb == 3) {
+                // the last MFMA is followed by 24 wait states so any later read of O is safe
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              } else {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              }
+              // the next kk's A fragment replaces this one after its last use
+              if (kk == 0 && hb == 3) av[cb] = ldv(1, cb);
+            }
+            pbc = pbn;
+          }
         }
-        // the last MFMA is followed by 24 wait states so any later read of O is safe
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+a"(O[CB - 1]) : "v"(av[NPV - 1]), "v"(pk1));
       };
 
     if constexpr (!FP8) {
@@ -515,23 +584,424 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
       m_ref = m_seg;  // exact maximum of the segment for every head of every wave
     }
 
-    // ---- normalised partial and its log-sum-exp (natural log)
-    const float inv_l = 1.f / l_run;
-    float* dst = o_part + (slot * NH + head) * DC;
+    // ---- normalised partial and its log-sum-exp (natural log). The partial row of a head is a
+    // convex combination of cached rows; it is stored as float16 after scaling by a power of
+    // two 2^-e that brings its largest magnitude into [0.5, 1); 2^e goes to the scale array.
+    if (g == 0) lds_l[head] = l_run;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int hb = 0; hb < 4; ++hb) {
+      float m = 0.f;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v;
-        v[0] = O[cb][4 * r4 + 0] * inv_l; v[1] = O[cb][4 * r4 + 1] * inv_l;
-        v[2] = O[cb][4 * r4 + 2] * inv_l; v[3] = O[cb][4 * r4 + 3] * inv_l;
-        *(f32x4*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
-      }
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(O[4 * cb + hb][r]));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0) lds_m[w][32 * hb + l32] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int hr = 32 * hb + l32;
+      const float inv_l = 1.f / lds_l[hr];
+      const float mx = fmaxf(fmaxf(lds_m[0][hr], lds_m[1][hr]), fmaxf(lds_m[2][hr], lds_m[3][hr])) * inv_l;
+      int e = 0;
+      if (mx > 0.f) (void)frexpf(mx, &e);
+      const float f = ldexpf(inv_l, -e);
+      uint16_t* dst = o_part + (slot * NH + hr) * DC + 128 * w;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& o = O[4 * cb + hb];
+          const u32x2 v = {pack_f16x2(o[4 * r4 + 0] * f, o[4 * r4 + 1] * f),
+                           pack_f16x2(o[4 * r4 + 2] * f, o[4 * r4 + 3] * f)};
+          *(u32x2*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
+        }
+      if (w == 0 && g == 0) sc_part[slot * NH + hr] = ldexpf(1.f, e);
     }
     if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
+    __syncthreads();  // lds_l / lds_m are reused by the next segment
 
     start = seg_end;
-    ++b;
+    if (start < end) {
+      ++b;
+      s0 = cu[b];
+      s1 = cu[b + 1];
+    }
+  }
+}
+
+// ================================================================================================
+// MFMA kernel for bf16 caches at the DeepSeek-V2 shape. Same work split, tile staging, LDS
+// layout and fragment layouts as the kernel above, with the memory traffic spread over the math:
+// per iteration `it` (tiles it+1.. it+3 in flight),
+//   scores of tile it (36 MFMAs) with the nine copies of tile it+3 slotted between them, so the
+//   four waves do not all queue 36 KB of copies at the same instant,
+//   softmax of tile it; P published to LDS; barrier,
+//   O^T[128 columns of wave w x 128 heads] += V^T P^T (32 MFMAs, P of all heads from LDS).
+// The softmax keeps per-lane (half-head) maxima and sums: no cross-lane traffic per tile; the
+// two halves of a head are joined once per segment. Reference maximum as in the kernel above.
+namespace v3 {
+constexpr int NBUF = 4;
+}
+
+// Scores of one tile (as tile_scores) with between(ks) run after MFMA ks; the calls sit between
+// the volatile MFMA statements in program order (used to issue tile copies under the math).
+template <typename F>
+__device__ __forceinline__ f32x16 tile_scores_copy(const uint8_t* tile, const uint32_t (&kq)[4],
+                                                   const bf16x8 (&qf)[v2::KSTEPS], F&& between) {
+  constexpr int KS = v2::KSTEPS, LA = 4;
+  bf16x8 a[KS];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) a[j] = *(const bf16x8*)(tile + kq[j & 3] + 128 * (j >> 2));
+  f32x16 s;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a[0]), "v"(qf[0]));
+  between(0);
+  a[LA] = *(const bf16x8*)(tile + kq[LA & 3] + 128 * (LA >> 2));
+#pragma unroll
+  for (int ks = 1; ks < KS - 1; ++ks) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a[ks]), "v"(qf[ks]));
+    between(ks);
+    if (ks + LA < KS) a[ks + LA] = *(const bf16x8*)(tile + kq[(ks + LA) & 3] + 128 * ((ks + LA) >> 2));
+  }
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(s) : "v"(a[KS - 1]), "v"(qf[KS - 1]));
+  return s;
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ q_lat,
+                                                      const float* __restrict__ q_pe, CacheArgs cache,
+                                                      const int64_t* __restrict__ cu,
+                                                      const RangePlan* __restrict__ plan, int G,
+                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ sc_part,
+                                                      uint16_t* __restrict__ o_part) {
+  using namespace v2;
+  constexpr int NBUF = v3::NBUF;
+  constexpr float HEAD = 64.f;
+  constexpr int FILL_STEPS = 20;  // softmax steps
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[NH * TT * 2];  // P of one tile, [head][token]
+  __shared__ float lds_l[NH];
+  __shared__ float lds_m[4][NH];
+  __shared__ int redo_flag[1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int p = range_for_block(blockIdx.x, G);
+  const RangePlan rp = plan[p];
+  int64_t start = rp.start;
+  const int64_t end = rp.end;
+  if (start >= end) return;
+  int b = rp.b;
+  int64_t s0 = rp.s0, s1 = rp.s1;
+  const int head = 32 * w + l32;
+
+  uint32_t kq[4];
+  {
+    const int kx = swz_key(l32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kq[j] = l32 * ROWB + (((2 * j + g) ^ kx) << 4);
+  }
+  uint32_t vq[2][2][2];
+  {
+    const int j16 = lane & 15, h2 = (lane >> 4) & 1;
+    const int cst = 2 * h2 + ((j16 & 3) >> 1);
+    const int sub = (j16 & 1) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int ab = 0; ab < 2; ++ab) {
+        const int t = 16 * kk + 4 * g + (j16 >> 2) + 8 * ab;
+        const int key = swz_key(t);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) vq[kk][ab][par] = t * ROWB + sub + (((4 * par + cst) ^ key) << 4);
+      }
+  }
+  uint32_t doff2[(LOADS + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (LOADS + 1) / 2; ++i) doff2[i] = 0;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int f = i * 256 + tid, t = f / CHUNKS;
+    const uint32_t o = (uint32_t)(t * ROWB + (swz(t, f - t * CHUNKS) << 4));
+    doff2[i >> 1] |= o << (16 * (i & 1));
+  }
+
+  while (start < end) {
+    if (s1 <= start) {  // an empty sequence: move on
+      ++b;
+      s0 = cu[b];
+      s1 = cu[b + 1];
+      continue;
+    }
+    const int64_t seg_end = end < s1 ? end : s1;
+    const int64_t t0 = start - s0, t1 = seg_end - s0;
+    const int64_t slot = (int64_t)p + b;
+    Rows<PAGED> rows;
+    rows.init(cache, b);
+    const int64_t n = t1 - t0;
+    const int ntiles = (int)((n + TT - 1) / TT);
+    const uint8_t* rows_b = (const uint8_t*)cache.rows;
+
+    // ---- tile copies: plan(it) fixes the uniform sources of tile it, copy(cp, i) issues the
+    // lane's i-th 16-byte chunk (rows past the segment re-read its last row)
+    struct CopyPlan {
+      const uint8_t* b0;
+      const uint8_t* b1;
+      uint32_t split, dst;
+      int last;
+    };
+    auto plan_tile = [&](int it) -> CopyPlan {
+      CopyPlan cp;
+      const int64_t tt0 = t0 + (int64_t)it * TT;
+      cp.last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+      cp.dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
+      if constexpr (!PAGED) {
+        cp.b0 = rows_b + (rows.base_row + tt0) * ROWB;
+        cp.b1 = cp.b0;
+        cp.split = 0xffffffffu;
+      } else {
+        rows.tile(tt0, tt0 + cp.last);
+        const int ps = 1 << rows.ps_shift;
+        const int s_in = (int)(tt0 & (ps - 1));
+        cp.split = (uint32_t)(ps - s_in) * ROWB;
+        cp.b0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * ROWB;
+        cp.b1 = rows_b + (int64_t)rows.pg1 * ps * ROWB - (int64_t)cp.split;
+      }
+      return cp;
+    };
+    auto copy = [&](const CopyPlan& cp, int i) __attribute__((always_inline)) {
+      uint32_t d2 = doff2[i >> 1];
+      asm volatile("" : "+v"(d2));
+      uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
+      if (cp.last < TT - 1) {  // only the last tile of a segment is partial
+        const int t = (int)(off / ROWB);
+        if (t > cp.last) off -= (uint32_t)(t - cp.last) * ROWB;
+      }
+      if constexpr (!PAGED) dma16_s(cp.b0, off, cp.dst + i * 4096);
+      else dma16((off < cp.split ? cp.b0 : cp.b1) + off, cp.dst + i * 4096);
+    };
+    auto issue_all = [&](int it) {
+      const CopyPlan cp = plan_tile(it);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) copy(cp, i);
+    };
+    auto prime = [&]() {
+#pragma unroll 1
+      for (int it = 0; it < 3 && it < ntiles; ++it) issue_all(it);
+    };
+    prime();
+
+    // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
+    bf16x8 qf[KSTEPS];
+    {
+      const float* ql = q_lat + ((int64_t)b * NH + head) * DC;
+      const float* qp = q_pe + ((int64_t)b * NH + head) * DR;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int f0 = 16 * ks + 8 * g;
+        const float* src = f0 < DC ? ql + f0 : qp + (f0 - DC);
+        const f32x4 a = *(const f32x4*)src, c = *(const f32x4*)(src + 4);
+        bf16x8 v;
+        v[0] = (__bf16)(a[0] * qscale); v[1] = (__bf16)(a[1] * qscale);
+        v[2] = (__bf16)(a[2] * qscale); v[3] = (__bf16)(a[3] * qscale);
+        v[4] = (__bf16)(c[0] * qscale); v[5] = (__bf16)(c[1] * qscale);
+        v[6] = (__bf16)(c[2] * qscale); v[7] = (__bf16)(c[3] * qscale);
+        qf[ks] = v;
+      }
+    }
+    auto valid_of = [&](int it) -> int {
+      const int64_t r = n - (int64_t)it * TT;
+      return r < TT ? (int)r : TT;
+    };
+
+    f32x16 O[CB];
+    float m_ref = -__builtin_inff(), m_seg = -__builtin_inff(), l_lane = 0.f;
+    bool have_ref = false;
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) O[cb] = f32x16{};
+      l_lane = 0.f;
+      bool over = false;
+      if (pass > 0) prime();
+
+      // softmax of one tile in FILL_STEPS steps; register r of s holds token 8(r/4) + 4g + r%4
+      f32x16 S;
+      bf16x8 pk0, pk1;
+      float mx = 0.f, rs = 0.f;
+      int valid = TT;
+      auto fill = [&](int ks) __attribute__((always_inline)) {
+        if (ks == 0) {
+          if (valid < TT) {
+            // token 8(r/4) + 4g + r%4 is valid iff 8(r/4) + r%4 < valid - 4g (constants per r,
+            // so no per-register index is kept live)
+            const int vg = valid - 4 * g;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = (8 * (r >> 2) + (r & 3)) < vg ? S[r] : -__builtin_inff();
+          }
+          mx = fmaxf(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])), fmaxf(fmaxf(S[4], S[5]), fmaxf(S[6], S[7])));
+          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(S[8], S[9]), fmaxf(S[10], S[11])),
+                               fmaxf(fmaxf(S[12], S[13]), fmaxf(S[14], S[15]))));
+        } else if (ks == 1) {
+          if (!have_ref) {  // first tile of the segment: the head's maximum over both halves
+            m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            have_ref = true;
+          }
+          m_seg = fmaxf(m_seg, mx);
+          over |= mx > m_ref + HEAD;
+          rs = 0.f;
+        } else if (ks < 18) {
+          const int r = ks - 2;
+          const float e = __builtin_amdgcn_exp2f(fminf(S[r] - m_ref, HEAD));
+          rs += e;
+          S[r] = e;
+        } else if (ks == 18) {
+          l_lane += rs;
+          pk0 = bf16x8{(__bf16)S[0], (__bf16)S[1], (__bf16)S[2], (__bf16)S[3],
+                       (__bf16)S[4], (__bf16)S[5], (__bf16)S[6], (__bf16)S[7]};
+        } else if (ks == 19) {
+          pk1 = bf16x8{(__bf16)S[8], (__bf16)S[9], (__bf16)S[10], (__bf16)S[11],
+                       (__bf16)S[12], (__bf16)S[13], (__bf16)S[14], (__bf16)S[15]};
+        }
+      };
+
+      // PV of tile `tile` (P from lds_p) with between(j) after MFMA j (0..31)
+      auto pv = [&](const uint8_t* tile) __attribute__((always_inline)) {
+        uint32_t vb[2][2][2];
+        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 256u * w;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+              vb[kk][ab][par] = tb + vq[kk][ab][par];
+              asm volatile("" : "+v"(vb[kk][ab][par]));
+            }
+        auto ldv = [&](int kk, int cb) __attribute__((always_inline)) -> u32x4 {
+          const uint32_t ia = vb[kk][0][cb & 1] + 128u * (cb >> 1);
+          const uint32_t ib = vb[kk][1][cb & 1] + 128u * (cb >> 1);
+          const u32x2 x0 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
+          const u32x2 x1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
+          return u32x4{x0.x, x0.y, x1.x, x1.y};
+        };
+        auto ldp = [&](int kk, int hb) __attribute__((always_inline)) -> bf16x8 {
+          const int hr = 32 * hb + l32;
+          return *(const bf16x8*)(lds_p + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
+        };
+        u32x4 av[4];
+        bf16x8 pbc, pbn;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) av[cb] = ldv(0, cb);
+        pbc = ldp(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            const bool last_group = kk == 1 && hb == 3;
+            if (!last_group) pbn = ldp(hb == 3 ? kk + 1 : kk, hb == 3 ? 0 : hb + 1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              if (last_group && cb == 3) {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              } else {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              }
+              if (kk == 0 && hb == 3) av[cb] = ldv(1, cb);
+            }
+            pbc = pbn;
+          }
+        }
+      };
+
+      for (int it = 0; it < ntiles; ++it) {
+        if (it + 2 < ntiles) vm_wait_barrier<2 * LOADS>();
+        else if (it + 1 < ntiles) vm_wait_barrier<LOADS>();
+        else vm_wait_barrier<0>();
+        valid = valid_of(it);
+        if (it + 3 < ntiles) {
+          const CopyPlan cp = plan_tile(it + 3);
+          S = tile_scores_copy(lds + (it % NBUF) * TILEB, kq, qf, [&](int ks) __attribute__((always_inline)) {
+            if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4);
+          });
+        } else {
+          S = tile_scores(lds + (it % NBUF) * TILEB, kq, qf);
+        }
+#pragma unroll
+        for (int ks = 0; ks < FILL_STEPS; ++ks) fill(ks);
+        {
+          const int key = (head >> 2) & 3;
+          uint8_t* prow = lds_p + head * 64;
+          *(bf16x8*)(prow + ((g ^ key) << 4)) = pk0;
+          *(bf16x8*)(prow + (((2 + g) ^ key) << 4)) = pk1;
+        }
+        __syncthreads();
+        pv(lds + (it % NBUF) * TILEB);
+      }
+      // does any head of the workgroup need the second pass?
+      __syncthreads();
+      if (tid == 0) *redo_flag = 0;
+      __syncthreads();
+      if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) *redo_flag = 1;
+      __syncthreads();
+      const int redo = *redo_flag;
+      __syncthreads();
+      if (!redo) break;
+      m_ref = fmaxf(m_seg, __shfl_xor(m_seg, 32, 64));  // exact maximum of the segment per head
+    }
+
+    // ---- normalised partial (float16 rows scaled by 2^-e, 2^e to the scale array) and lse
+    const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
+    if (g == 0) lds_l[head] = l_run;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      float m = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(O[4 * cb + hb][r]));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0) lds_m[w][32 * hb + l32] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int hr = 32 * hb + l32;
+      const float inv_l = 1.f / lds_l[hr];
+      const float mx2 = fmaxf(fmaxf(lds_m[0][hr], lds_m[1][hr]), fmaxf(lds_m[2][hr], lds_m[3][hr])) * inv_l;
+      int e = 0;
+      if (mx2 > 0.f) (void)frexpf(mx2, &e);
+      const float f = ldexpf(inv_l, -e);
+      uint16_t* dst = o_part + (slot * NH + hr) * DC + 128 * w;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& o = O[4 * cb + hb];
+          const u32x2 v = {pack_f16x2(o[4 * r4 + 0] * f, o[4 * r4 + 1] * f),
+                           pack_f16x2(o[4 * r4 + 2] * f, o[4 * r4 + 3] * f)};
+          *(u32x2*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
+        }
+      if (w == 0 && g == 0) sc_part[slot * NH + hr] = ldexpf(1.f, e);
+    }
+    if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
+    __syncthreads();  // lds_l / lds_m are reused by the next segment
+
+    start = seg_end;
+    if (start < end) {
+      ++b;
+      s0 = cu[b];
+      s1 = cu[b + 1];
+    }
   }
 }
 
@@ -654,17 +1124,77 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
 // Combine: per sequence, merge the pieces of the ranges that cover it. One block = one sequence
 // and CH heads; the piece list and the per-(piece, head) weights exp(lse_s - M) / sum are built
 // once in LDS, then every output element is a weighted sum over the pieces (fixed order).
+// Partial outputs are float32 (generic kernel, format 0) or float16 rows with a power-of-two
+// scale per (piece, head) (MFMA kernel, format 2), as the format word says; the scale is folded
+// into the piece weights.
 namespace cmb {
 constexpr int CH = 8;        // heads per block
 constexpr int MAXP = 1024;   // pieces per sequence handled in one pass of the piece list
 }
 
+__device__ __forceinline__ f32x4 load4(const float* p, int64_t i) { return ((const f32x4*)p)[i]; }
+__device__ __forceinline__ f32x4 load4(const _Float16* p, int64_t i) {
+  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_convertvector(((const f16x4_t*)p)[i], f32x4);
+}
+
+// every thread owns up to 4 float4 outputs per round; the loads of 4 pieces are issued before
+// their products are accumulated (piece order fixed, so the sum order is the same everywhere)
+template <typename PT>
+__device__ __forceinline__ void combine_sum(const PT* __restrict__ o_part, int n_h, int d_c, int h0, int nh,
+                                            int np, const int* slots, const float (*wts)[cmb::CH], float* dst) {
+  const int tid = threadIdx.x;
+  const int nv4 = nh * d_c / 4;
+  const PT* src = o_part + (int64_t)h0 * d_c;
+  const int64_t pstride = (int64_t)n_h * d_c / 4;  // 4-element groups per piece slot
+  f32x4* dst4 = (f32x4*)dst;
+  for (int e0 = 0; e0 < nv4; e0 += 1024) {
+    int idx[4];
+    f32x4 acc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      idx[v] = e0 + tid + 256 * v;
+      acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int i = 0;
+    for (; i + 4 <= np; i += 4) {
+      f32x4 x[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          x[k][v] = idx[v] < nv4 ? load4(src, (int64_t)slots[i + k] * pstride + idx[v]) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float wk = wts[i + k][(idx[v] < nv4 ? idx[v] : 0) * 4 / d_c];
+          acc[v][0] += wk * x[k][v][0]; acc[v][1] += wk * x[k][v][1];
+          acc[v][2] += wk * x[k][v][2]; acc[v][3] += wk * x[k][v][3];
+        }
+    }
+    for (; i < np; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (idx[v] >= nv4) continue;
+        const f32x4 x = load4(src, (int64_t)slots[i] * pstride + idx[v]);
+        const float wk = wts[i][idx[v] * 4 / d_c];
+        acc[v][0] += wk * x[0]; acc[v][1] += wk * x[1]; acc[v][2] += wk * x[2]; acc[v][3] += wk * x[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (idx[v] < nv4) dst4[idx[v]] = acc[v];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t* __restrict__ cu, int B, int G,
+                                                 const int32_t* __restrict__ fmt,
                                                  const float* __restrict__ lse_part,
-                                                 const float* __restrict__ o_part, float* __restrict__ o_lat,
+                                                 const float* __restrict__ sc_part,
+                                                 const void* __restrict__ o_part, float* __restrict__ o_lat,
                                                  float* __restrict__ lse_out) {
   using namespace cmb;
-  __shared__ int64_t sh_plo, sh_phi;
   __shared__ int slots[MAXP];
   __shared__ float wts[MAXP][CH];
   __shared__ int sh_np;
@@ -681,15 +1211,15 @@ __global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t
     return;
   }
   if (tid == 0) {
-    sh_plo = range_of(s0, total, G);
-    sh_phi = range_of(s1 - 1, total, G);
+    const int64_t plo = range_of(s0, total, G), phi = range_of(s1 - 1, total, G);
     int np = 0;
-    for (int64_t p = sh_plo; p <= sh_phi && np < MAXP; ++p)
+    for (int64_t p = plo; p <= phi && np < MAXP; ++p)
       if (range_start(p, total, G) != range_start(p + 1, total, G)) slots[np++] = (int)(p + b);
     sh_np = np;
   }
   __syncthreads();
   const int np = sh_np;
+  const bool f16 = *fmt == 2;
   // weights: wave w handles heads w, w+4, ...
   for (int hh = w; hh < nh; hh += 4) {
     float M = -__builtin_inff();
@@ -703,54 +1233,13 @@ __global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t
     }
     sum = wave_sum(sum);
     const float inv = 1.f / sum;
-    for (int i = lane; i < np; i += 64) wts[i][hh] *= inv;
+    for (int i = lane; i < np; i += 64)
+      wts[i][hh] *= f16 ? inv * sc_part[(int64_t)slots[i] * n_h + h0 + hh] : inv;
     if (lse_out && lane == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
   }
   __syncthreads();
-  // every thread owns up to 4 float4 outputs per round; the loads of 4 pieces are issued before
-  // their products are accumulated (piece order fixed, so the sum order is the same everywhere)
-  const int nv4 = nh * d_c / 4;
-  const float4* src = (const float4*)(o_part + (int64_t)h0 * d_c);
-  const int64_t pstride = (int64_t)n_h * d_c / 4;  // float4 per piece slot
-  float4* dst4 = (float4*)dst;
-  for (int e0 = 0; e0 < nv4; e0 += 1024) {
-    int idx[4];
-    float4 acc[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      idx[v] = e0 + tid + 256 * v;
-      acc[v] = float4{0.f, 0.f, 0.f, 0.f};
-    }
-    int i = 0;
-    for (; i + 4 <= np; i += 4) {
-      float4 x[4][4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          x[k][v] = idx[v] < nv4 ? src[(int64_t)slots[i + k] * pstride + idx[v]] : float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float wk = wts[i + k][(idx[v] < nv4 ? idx[v] : 0) * 4 / d_c];
-          acc[v].x += wk * x[k][v].x; acc[v].y += wk * x[k][v].y;
-          acc[v].z += wk * x[k][v].z; acc[v].w += wk * x[k][v].w;
-        }
-    }
-    for (; i < np; ++i) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (idx[v] >= nv4) continue;
-        const float4 x = src[(int64_t)slots[i] * pstride + idx[v]];
-        const float wk = wts[i][idx[v] * 4 / d_c];
-        acc[v].x += wk * x.x; acc[v].y += wk * x.y; acc[v].z += wk * x.z; acc[v].w += wk * x.w;
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (idx[v] < nv4) dst4[idx[v]] = acc[v];
-  }
+  if (f16) combine_sum((const _Float16*)o_part, n_h, d_c, h0, nh, np, slots, wts, dst);
+  else combine_sum((const float*)o_part, n_h, d_c, h0, nh, np, slots, wts, dst);
 }
 
 // ================================================================================================
@@ -770,17 +1259,25 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   DecodeLayout L = decode_layout(d, B, G);
   char* base = (char*)ws;
   int64_t* cu = (int64_t*)(base + L.off_cu);
+  int32_t* fmt = (int32_t*)(base + L.off_fmt);
+  RangePlan* plan = (RangePlan*)(base + L.off_plan);
   float* lse_part = (float*)(base + L.off_lse);
   float* o_part = (float*)(base + L.off_o);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, seq_lens, B, cu);
+  const bool mfma = is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, seq_lens, B, G, mfma ? 2 : 0, cu, fmt, plan);
   const float qscale = sm_scale * 1.44269504088896340736f;  // log2(e)
-  if (is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3)) {
+  if (mfma) {
     const bool paged = c.page_size > 0;
 #define MLA_V2(CDT, PG) \
-    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part)
-    if (c.dtype == MLA_BF16) { if (paged) MLA_V2(MLA_BF16, true); else MLA_V2(MLA_BF16, false); }
+    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, plan, G, qscale, \
+                       lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
+#define MLA_V3(PG) \
+    hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, plan, G, qscale, \
+                       lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
+    if (c.dtype == MLA_BF16) { if (paged) MLA_V3(true); else MLA_V3(false); }
     else { if (paged) MLA_V2(MLA_FP8_E4M3, true); else MLA_V2(MLA_FP8_E4M3, false); }
 #undef MLA_V2
+#undef MLA_V3
   } else {
     const int rw = d.d_c + d.d_r;
     size_t smem = (size_t)(d.n_h * rw + gen::TT * rw + d.n_h * gen::TT + 3 * d.n_h) * 4;
@@ -812,7 +1309,8 @@ hipError_t launch_combine(const mla_dims& d, int B, int G, const void* ws, float
   const char* base = (const char*)ws;
   dim3 grid((unsigned)((d.n_h + cmb::CH - 1) / cmb::CH), B);
   hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, d.n_h, d.d_c, (const int64_t*)(base + L.off_cu), B, G,
-                     (const float*)(base + L.off_lse), (const float*)(base + L.off_o), o_lat, lse);
+                     (const int32_t*)(base + L.off_fmt), (const float*)(base + L.off_lse),
+                     (const float*)(base + L.off_sc), (const void*)(base + L.off_o), o_lat, lse);
   return hipGetLastError();
 }
 
