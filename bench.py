@@ -36,7 +36,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size: each launch reads and writes 256 MiB."""
+    import torch
+    n = 64 << 20  # float32 elements
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                                           "launches": 5}}), flush=True)
 
 
 def build_cache(mla, case):
@@ -84,6 +99,9 @@ def cpu_baseline(case, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "
                                    "for how the path shards across GPUs"}))

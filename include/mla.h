@@ -11,8 +11,10 @@
  * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
  *
  * Conventions shared by every entry point
- *  - Pointers are DEVICE pointers unless the comment says host. The caller owns every buffer
- *    (inputs, outputs, workspaces); the library never allocates, frees or keeps per-call state.
+ *  - Pointers are DEVICE pointers unless the comment says host. Tensors and workspaces must be
+ *    16-byte aligned (kernels use vector accesses); int32 arrays (lengths, block tables), the fp8
+ *    scales and lse need 4 bytes. The caller owns every buffer (inputs, outputs, workspaces);
+ *    the library never allocates, frees or keeps per-call state.
  *  - Every call only enqueues work on `stream` (may be NULL = the default stream) and returns.
  *    Nothing synchronises. Work is ordered with the caller's other work on that stream.
  *  - Arguments are validated on the host before anything is enqueued. On an error nothing is
@@ -136,8 +138,12 @@ MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_
  * and the result is the softmax-weighted latent sum plus its log-sum-exp.
  * The batch's tokens (sum of seq_lens) are cut into `num_splits` contiguous ranges of equal
  * length (0 = one per compute unit; at most 1024); each range is one workgroup, and a sequence
- * is split where ranges cut it. Each (range, sequence) piece writes a partial result into the workspace;
- * mla_combine merges them. At most num_splits + B - 1 pieces exist.
+ * is split where ranges cut it. Each (range, sequence) piece writes a partial result into the
+ * workspace: its normalised latent sum and log-sum-exp per head; mla_combine merges them. At most
+ * num_splits + B - 1 pieces exist. The partial latent sums are float32, except on the MFMA path
+ * (n_h = 128, d_c = 512, d_r = 64 with a bf16 or fp8 cache) where each (piece, head) row is kept
+ * as float16 after scaling by a power of two that brings its largest magnitude into [0.5, 1):
+ * a relative rounding of at most 2^-11 per element, below the bf16 rounding of the operands.
  *   q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] (rotated): float32.
  *   seq_lens: device int32 [B] (including the current token, already appended).
  *   workspace: at least mla_decode_workspace_bytes(dims, B, num_splits) bytes. */

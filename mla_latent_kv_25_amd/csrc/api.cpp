@@ -36,6 +36,17 @@ mla_status hip_status(hipError_t e, const char* what) {
 bool valid_wdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16; }
 bool valid_cdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
 
+// Kernels use 16-byte vector accesses on tensors and workspaces (16-byte alignment required);
+// int32 / float arrays read element by element (lengths, block tables, scales) need 4 bytes.
+template <typename... P>
+bool misaligned(const P*... ptrs) {
+  return ((((uintptr_t)(const void*)ptrs) & 15u) || ...);
+}
+template <typename... P>
+bool misaligned4(const P*... ptrs) {
+  return ((((uintptr_t)(const void*)ptrs) & 3u) || ...);
+}
+
 mla_status check_dims(const mla_dims* d, const char* fn) {
   if (!d) return fail(MLA_E_ARG, "%s: dims is NULL", fn);
   if (d->d <= 0 || d->n_h <= 0 || d->d_h <= 0 || d->d_c <= 0 || d->d_cq <= 0 || d->d_r <= 0)
@@ -50,6 +61,8 @@ mla_status check_cache(const mla_cache* c, const char* fn, mla::CacheArgs* out) 
   if (!c) return fail(MLA_E_ARG, "%s: cache is NULL", fn);
   if (!c->rows) return fail(MLA_E_ARG, "%s: cache rows is NULL", fn);
   if (!valid_cdtype(c->dtype)) return fail(MLA_E_ARG, "%s: bad cache dtype %d", fn, c->dtype);
+  if (misaligned(c->rows) || misaligned4(c->scales, c->block_table))
+    return fail(MLA_E_ARG, "%s: cache pointers must be 16-byte aligned", fn);
   if ((c->dtype == MLA_FP8_E4M3) != (c->scales != nullptr))
     return fail(MLA_E_ARG, "%s: scales must be given exactly for the fp8 cache", fn);
   if (c->page_size < 0) return fail(MLA_E_ARG, "%s: page_size < 0", fn);
@@ -126,6 +139,8 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype, const v
   if (B == 0) return ok();
   if (!h || !W_dq || !W_uq || !W_qr || !W_uk || !W_dkv || !W_kr || !q_lat || !q_pe || !kv_new)
     return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(h, W_dq, W_uq, W_qr, W_uk, W_dkv, W_kr, q_lat, q_pe, kv_new, workspace))
+    return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   if (!workspace || ws_bytes < mla_absorb_q_workspace_bytes(dims, B))
     return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_q_workspace_bytes(dims, B));
   return hip_status(mla::launch_absorb_q(*dims, B, wdtype, h, W_dq, W_uq, W_qr, W_uk, W_dkv, W_kr, workspace, q_lat,
@@ -141,6 +156,7 @@ mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, fl
   if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
   if (B == 0) return ok();
   if (!seq_lens || !q_pe || !kv_new) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(q_pe, kv_new) || misaligned4(seq_lens)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   mla::CacheArgs c{};
   if (cache) {
     s = check_cache(cache, fn, &c);
@@ -167,6 +183,7 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, 
   if (s) return s;
   if (B == 0) return ok();
   if (!q_lat || !q_pe || !seq_lens) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(q_lat, q_pe, workspace) || misaligned4(seq_lens)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   if (!mla::decode_supported(*dims, c.dtype, c.page_size))
     return fail(MLA_E_UNSUPPORTED, "%s: no decode kernel for n_h=%d d_c=%d d_r=%d with cache dtype %d", fn,
                 dims->n_h, dims->d_c, dims->d_r, c.dtype);
@@ -186,6 +203,7 @@ mla_status mla_combine(const mla_dims* dims, int32_t B, int32_t num_splits, cons
   if (num_splits < 0 || num_splits > 1024) return fail(MLA_E_ARG, "%s: num_splits must be in [0, 1024]", fn);
   if (B == 0) return ok();
   if (!seq_lens || !o_lat) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(o_lat, workspace) || misaligned4(seq_lens, lse)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   const int G = resolve_splits(num_splits);
   const size_t need = mla::decode_layout(*dims, B, G).bytes;
   if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
@@ -206,6 +224,7 @@ mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const
   if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
   if (B == 0) return ok();
   if (!o_lat || !W_uv || !W_o || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(o_lat, W_uv, W_o, u, workspace)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   if (!workspace || ws_bytes < mla_absorb_out_workspace_bytes(dims, B))
     return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_out_workspace_bytes(dims, B));
   return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
@@ -222,6 +241,7 @@ mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t
   if (B < 0 || max_rows < 0) return fail(MLA_E_ARG, "%s: B and max_rows must be >= 0", fn);
   if (B == 0 || max_rows == 0) return ok();
   if (!n_rows || !src) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(src) || misaligned4(n_rows)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
   if (src_stride < max_rows) return fail(MLA_E_ARG, "%s: src_stride < max_rows", fn);
   if (max_rows > c.t_cap) return fail(MLA_E_ARG, "%s: max_rows exceeds the cache capacity", fn);
   return hip_status(mla::launch_cache_store(*dims, c, B, n_rows, max_rows, src, src_stride, stream), fn);

@@ -23,8 +23,7 @@ DecodeLayout decode_layout(const mla_dims& d, int B, int G) {
   L.n_pieces = (int64_t)G + B - 1;
   L.off_cu = 0;
   L.off_fmt = al256((size_t)(B + 1) * 8);
-  L.off_plan = L.off_fmt + 256;
-  L.off_lse = al256(L.off_plan + (size_t)G * sizeof(RangePlan));
+  L.off_lse = L.off_fmt + 256;
   L.off_sc = al256(L.off_lse + (size_t)L.n_pieces * d.n_h * 4);
   L.off_o = al256(L.off_sc + (size_t)L.n_pieces * d.n_h * 4);
   L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;  // sized for float32 partials
@@ -38,51 +37,83 @@ __device__ __forceinline__ int64_t row_index(const CacheArgs& c, int b, int64_t 
 }
 
 // ------------------------------------------------------------------------------------------------
-// Plan, one block: cu[b] = sum_{b' < b} seq_lens[b'] (int64), the partial-output format word, and
-// for every range p its interval, first sequence and that sequence's interval (so a decode
-// workgroup starts from a single record instead of a chain of dependent searches).
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ seq_lens, int B, int G, int fmt,
-                                               int64_t* __restrict__ cu, int32_t* __restrict__ fmt_out,
-                                               RangePlan* __restrict__ plan) {
-  __shared__ int64_t part[1024];
-  __shared__ int64_t carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    int i = base + tid;
-    int64_t v = i < B ? (int64_t)seq_lens[i] : 0;
-    part[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-      int64_t x = tid >= o ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] += x;
-      __syncthreads();
-    }
-    if (i < B) cu[i + 1] = carry + part[tid];
-    __syncthreads();
-    if (tid == 1023) carry += part[1023];
-    __syncthreads();
+// Range planning on the device, inside the decode kernels (no separate launch): every wave of a
+// workgroup locates its range from seq_lens with wave-wide scans; workgroup 0 also writes the
+// prefix sums cu[b] = sum_{b' < b} seq_lens[b'] and the partial-output format word that
+// mla_combine reads.
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
   }
-  if (tid == 0) { cu[0] = 0; *fmt_out = fmt; }
-  __syncthreads();  // cu is complete and visible to the whole block
-  const int64_t total = carry;
-  for (int p = tid; p < G; p += 1024) {
-    RangePlan r;
-    r.start = range_start(p, total, G);
-    r.end = range_start(p + 1, total, G);
-    int lo = 0, hi = B - 1;  // largest b with cu[b] <= start
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cu[mid] <= r.start) lo = mid; else hi = mid - 1;
+  return v;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Range p: token interval [start, end) of the concatenated batch, the first sequence b whose
+// interval [s0, s1) reaches past `start`. Uniform across the wave (kept in scalar registers).
+struct RangeStart {
+  int64_t start, end, s0, s1;
+  int b;
+};
+__device__ __forceinline__ RangeStart locate_range(const int32_t* __restrict__ seq_lens, int B, int G, int p,
+                                                   int lane) {
+  int64_t acc = 0;
+  for (int i = lane; i < B; i += 64) acc += seq_lens[i];
+  const int64_t total = wave_sum_i64(acc);
+  RangeStart r;
+  r.start = range_start(p, total, G);
+  r.end = range_start(p + 1, total, G);
+  r.b = 0;
+  r.s0 = r.s1 = 0;
+  int64_t base = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int i = c0 + lane;
+    const int64_t v = i < B ? (int64_t)seq_lens[i] : 0;
+    const int64_t inc = wave_incl_scan_i64(v, lane);
+    const uint64_t hit = __ballot(base + inc > r.start);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      r.b = c0 + f;
+      r.s1 = base + __shfl(inc, f, 64);
+      r.s0 = r.s1 - __shfl(v, f, 64);
+      break;
     }
-    r.b = lo;
-    r.s0 = cu[lo];
-    r.s1 = cu[lo + 1];
-    r.pad0 = 0;
-    r.pad1 = 0;
-    plan[p] = r;
+    base += __shfl(inc, 63, 64);
+  }
+  r.start = uniform_i64(r.start);
+  r.end = uniform_i64(r.end);
+  r.s0 = uniform_i64(r.s0);
+  r.s1 = uniform_i64(r.s1);
+  r.b = __builtin_amdgcn_readfirstlane(r.b);
+  return r;
+}
+
+// cu[0..B] and the format word, by one wave of workgroup 0.
+__device__ __forceinline__ void write_prefix(const int32_t* __restrict__ seq_lens, int B, int fmt,
+                                             int64_t* __restrict__ cu, int32_t* __restrict__ fmt_out, int lane) {
+  int64_t base = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int i = c0 + lane;
+    const int64_t v = i < B ? (int64_t)seq_lens[i] : 0;
+    const int64_t inc = wave_incl_scan_i64(v, lane);
+    if (i < B) cu[i + 1] = base + inc;
+    base += __shfl(inc, 63, 64);
+  }
+  if (lane == 0) {
+    cu[0] = 0;
+    *fmt_out = fmt;
   }
 }
 
@@ -93,14 +124,6 @@ __device__ __forceinline__ int range_for_block(int bid, int G) {
   return bid;
 }
 
-__device__ __forceinline__ int first_seq(const int64_t* cu, int B, int64_t t) {
-  int lo = 0, hi = B - 1;  // largest b with cu[b] <= t
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 // ================================================================================================
 // MFMA kernel for the DeepSeek-V2 shape: n_h = 128, d_c = 512, d_r = 64 (row = 576).
@@ -247,8 +270,8 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
 template <int CDT, bool PAGED>
 __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ q_lat,
                                                       const float* __restrict__ q_pe, CacheArgs cache,
-                                                      const int64_t* __restrict__ cu,
-                                                      const RangePlan* __restrict__ plan, int G,
+                                                      const int32_t* __restrict__ seq_lens, int B, int G,
+                                                      int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
                                                       float qscale, float* __restrict__ lse_part,
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
@@ -269,7 +292,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int p = range_for_block(blockIdx.x, G);
-  const RangePlan rp = plan[p];
+  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 2, cu_out, fmt_out, lane);
+  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
   int64_t start = rp.start;
   const int64_t end = rp.end;
   if (start >= end) return;
@@ -322,8 +346,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
   while (start < end) {
     if (s1 <= start) {  // an empty sequence: move on
       ++b;
-      s0 = cu[b];
-      s1 = cu[b + 1];
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
       continue;
     }
     const int64_t seg_end = end < s1 ? end : s1;
@@ -625,8 +649,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
     start = seg_end;
     if (start < end) {
       ++b;
-      s0 = cu[b];
-      s1 = cu[b + 1];
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
     }
   }
 }
@@ -674,8 +698,8 @@ __device__ __forceinline__ f32x16 tile_scores_copy(const uint8_t* tile, const ui
 template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ q_lat,
                                                       const float* __restrict__ q_pe, CacheArgs cache,
-                                                      const int64_t* __restrict__ cu,
-                                                      const RangePlan* __restrict__ plan, int G,
+                                                      const int32_t* __restrict__ seq_lens, int B, int G,
+                                                      int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
                                                       float qscale, float* __restrict__ lse_part,
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
@@ -691,7 +715,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int p = range_for_block(blockIdx.x, G);
-  const RangePlan rp = plan[p];
+  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 2, cu_out, fmt_out, lane);
+  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
   int64_t start = rp.start;
   const int64_t end = rp.end;
   if (start >= end) return;
@@ -733,8 +758,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
   while (start < end) {
     if (s1 <= start) {  // an empty sequence: move on
       ++b;
-      s0 = cu[b];
-      s1 = cu[b + 1];
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
       continue;
     }
     const int64_t seg_end = end < s1 ? end : s1;
@@ -999,8 +1024,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
     start = seg_end;
     if (start < end) {
       ++b;
-      s0 = cu[b];
-      s1 = cu[b + 1];
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
     }
   }
 }
@@ -1026,7 +1051,8 @@ template <int CDT>
 __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_r,
                                                         const float* __restrict__ q_lat,
                                                         const float* __restrict__ q_pe, CacheArgs cache,
-                                                        const int64_t* __restrict__ cu, int B, int G,
+                                                        const int32_t* __restrict__ seq_lens, int B, int G,
+                                                        int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
                                                         float qscale, float* __restrict__ lse_part,
                                                         float* __restrict__ o_part) {
   using namespace gen;
@@ -1040,16 +1066,22 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
   float* alf = lrun + n_h;              // [n_h]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int p = range_for_block(blockIdx.x, G);
-  const int64_t total = cu[B];
-  int64_t start = range_start(p, total, G);
-  const int64_t end = range_start(p + 1, total, G);
+  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 0, cu_out, fmt_out, lane);
+  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
+  int64_t start = rp.start;
+  const int64_t end = rp.end;
   if (start >= end) return;
-  int b = first_seq(cu, B, start);
+  int b = rp.b;
+  int64_t s0 = rp.s0, s1 = rp.s1;
   const int nout = n_h * d_c;
 
   while (start < end) {
-    const int64_t s0 = cu[b], s1 = cu[b + 1];
-    if (s1 <= start) { ++b; continue; }
+    if (s1 <= start) {
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+      continue;
+    }
     const int64_t seg_end = end < s1 ? end : s1;
     const int64_t t0 = start - s0, t1 = seg_end - s0;
     const int64_t slot = (int64_t)p + b;
@@ -1116,7 +1148,11 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
       lse_part[slot * n_h + h] = (mrun[h] + __log2f(lrun[h])) * 0.69314718055994530942f;
     __syncthreads();
     start = seg_end;
-    ++b;
+    if (start < end) {
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+    }
   }
 }
 
@@ -1260,19 +1296,17 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   char* base = (char*)ws;
   int64_t* cu = (int64_t*)(base + L.off_cu);
   int32_t* fmt = (int32_t*)(base + L.off_fmt);
-  RangePlan* plan = (RangePlan*)(base + L.off_plan);
   float* lse_part = (float*)(base + L.off_lse);
   float* o_part = (float*)(base + L.off_o);
   const bool mfma = is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, seq_lens, B, G, mfma ? 2 : 0, cu, fmt, plan);
   const float qscale = sm_scale * 1.44269504088896340736f;  // log2(e)
   if (mfma) {
     const bool paged = c.page_size > 0;
 #define MLA_V2(CDT, PG) \
-    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, plan, G, qscale, \
+    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
 #define MLA_V3(PG) \
-    hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, cu, plan, G, qscale, \
+    hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
     if (c.dtype == MLA_BF16) { if (paged) MLA_V3(true); else MLA_V3(false); }
     else { if (paged) MLA_V2(MLA_FP8_E4M3, true); else MLA_V2(MLA_FP8_E4M3, false); }
@@ -1284,19 +1318,19 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
     switch (c.dtype) {
       case MLA_F32:
         hipLaunchKernelGGL(k_decode_generic<MLA_F32>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
         break;
       case MLA_F16:
         hipLaunchKernelGGL(k_decode_generic<MLA_F16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
         break;
       case MLA_BF16:
         hipLaunchKernelGGL(k_decode_generic<MLA_BF16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
         break;
       default:
         hipLaunchKernelGGL(k_decode_generic<MLA_FP8_E4M3>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c,
-                           d.d_r, q_lat, q_pe, c, cu, B, G, qscale, lse_part, o_part);
+                           d.d_r, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
         break;
     }
   }

@@ -24,18 +24,10 @@ struct DecodeLayout {
   int64_t n_pieces;   // num_splits + B - 1
   size_t off_cu;      // int64 [B + 1] prefix sums of seq_lens
   size_t off_fmt;     // int32: partial-output format (0 float32, 2 scaled float16)
-  size_t off_plan;    // RangePlan [num_splits]
   size_t off_lse;     // float [n_pieces, n_h]
   size_t off_sc;      // float [n_pieces, n_h]: row scales of float16 partials
   size_t off_o;       // float or float16 [n_pieces, n_h, d_c]
   size_t bytes;
-};
-// Where range p starts: its token interval [start, end) of the concatenated batch, the first
-// sequence b it touches and that sequence's interval [s0, s1).
-struct RangePlan {
-  int64_t start, end, s0, s1;
-  int32_t b, pad0;
-  int64_t pad1;
 };
 DecodeLayout decode_layout(const mla_dims& d, int B, int G);
 

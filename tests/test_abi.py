@@ -129,3 +129,17 @@ def test_absorb_out_and_store_validation(L):
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 65, FAKE, 65, None) == 1  # > t_cap
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 10, FAKE, 5, None) == 1   # stride
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 0, None, 0, None, 0, None) == 0
+
+
+def test_alignment_validation(L):
+    """Kernels use 16-byte vector accesses: misaligned tensor pointers are rejected up front."""
+    d = _dims()
+    odd = ctypes.c_void_p(0x1004)
+    assert L.mla_rope(ctypes.byref(d), 1, FAKE, odd, FAKE, None, None) == 1
+    assert b"aligned" in L.mla_last_error()
+    c = _cache(rows=0x1008)
+    assert L.mla_decode_attn(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, 1 << 30, None) == 1
+    assert b"aligned" in L.mla_last_error()
+    need = L.mla_absorb_out_workspace_bytes(ctypes.byref(d), 2)
+    assert L.mla_absorb_out(ctypes.byref(d), 2, 0, FAKE, FAKE, FAKE, odd, need, FAKE, None) == 1
+    assert b"aligned" in L.mla_last_error()
