@@ -41,7 +41,9 @@ struct QSplits { int sk1; };
 static QSplits q_splits(const mla_dims& d) { return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT), d.d / gm::KC, 1)}; }
 struct OSplits { int sk4, sk5; };
 static OSplits o_splits(const mla_dims& d) {
-  return {split_for(cdiv(d.d_h, gm::MT), d.d_c / gm::KC, d.n_h), split_for(cdiv(d.d, gm::MT), d.n_h * d.d_h / gm::KC, 1)};
+  // W^UV: one workgroup per (head, 128 rows); a K split would add a reduction pass costing more
+  // than the idle compute units at n_h = 128
+  return {1, split_for(cdiv(d.d, gm::MT), d.n_h * d.d_h / gm::KC, 1)};
 }
 
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
