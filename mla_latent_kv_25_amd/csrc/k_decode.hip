@@ -882,7 +882,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
           rs = 0.f;
         } else if (ks < 18) {
           const int r = ks - 2;
-          const float e = __builtin_amdgcn_exp2f(fminf(S[r] - m_ref, HEAD));
+          // no clamp: a score past m_ref + HEAD sets `over`, and the whole pass is redone
+          const float e = __builtin_amdgcn_exp2f(S[r] - m_ref);
           rs += e;
           S[r] = e;
         } else if (ks == 18) {

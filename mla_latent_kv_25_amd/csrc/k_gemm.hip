@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
 }
 
 // Ordered split-K reduction: Y[n][m] = sum_{ky} part[ky][n][m] (4 consecutive m per thread),
-// scattered to the segments; blockIdx.y = batched problem z.
+// scattered to the segments; blockIdx.y = batched problem z. The partials of up to 16 slices are
+// requested together and then added in slice order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(Seg seg, int N, int Mtot, int split_k,
                                                        const float* __restrict__ part, int64_t zY) {
   const int z = blockIdx.y, Z = gridDim.y;
@@ -281,10 +282,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(Seg seg, int N, int Mtot,
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (int64_t)N * M4) return;
   const int n = (int)(e / M4), m = (int)(e % M4) * 4;
+  const int64_t slice = (int64_t)Z * N * Mtot;
+  const float* src = part + ((int64_t)z * N + n) * Mtot + m;
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < split_k; ++k) {
-    const f32x4 x = *(const f32x4*)(part + ((int64_t)(k * Z + z) * N + n) * Mtot + m);
-    v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
+  for (int k0 = 0; k0 < split_k; k0 += 16) {
+    f32x4 x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      x[k] = k0 + k < split_k ? *(const f32x4*)(src + (int64_t)(k0 + k) * slice) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[0] += x[k][0]; v[1] += x[k][1]; v[2] += x[k][2]; v[3] += x[k][3];
+    }
   }
   const int s = seg_of(seg, m);
   *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)n * seg.ldy[s] + (m - seg.m0[s])) = v;
