@@ -157,14 +157,6 @@ __device__ __forceinline__ int swz_key(int t) {
 }
 __device__ __forceinline__ int swz(int t, int c) { return c ^ swz_key(t); }
 
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 8;
-  uint32_t em = c & 0x7fu;
-  if (em >= 8u) return s | ((em + (120u << 3)) << 4);
-  float v = (float)em * 0.001953125f;  // subnormal: em * 2^-9, exact in bf16
-  return s | (__builtin_bit_cast(uint32_t, v) >> 16);
-}
-
 // 16-byte global -> LDS copy per lane (LDS destination: wave-uniform `lds_addr` + 16 * lane).
 // Written as asm so the compiler does not add its conservative "wait for every LDS DMA" before
 // each LDS read: the kernel tracks these loads itself (vm_wait_barrier). The instruction has no
@@ -577,12 +569,15 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
           uint8_t* dst = lds + (it % NBUF) * TILEB;
 #pragma unroll
           for (int i = 0; i < LOADS; ++i) {
+            // OCP e4m3 -> bf16 is exact; the hardware pair conversion (scale 1: the per-token
+            // scale is applied to the scores and probabilities instead) takes the codes of
+            // one 16-bit half, low byte first
             u32x4 o;
             const uint32_t lo = r8[i].x, hi = r8[i].y;
-            o.x = e4m3_to_bf16_bits(lo & 0xff) | (e4m3_to_bf16_bits((lo >> 8) & 0xff) << 16);
-            o.y = e4m3_to_bf16_bits((lo >> 16) & 0xff) | (e4m3_to_bf16_bits(lo >> 24) << 16);
-            o.z = e4m3_to_bf16_bits(hi & 0xff) | (e4m3_to_bf16_bits((hi >> 8) & 0xff) << 16);
-            o.w = e4m3_to_bf16_bits((hi >> 16) & 0xff) | (e4m3_to_bf16_bits(hi >> 24) << 16);
+            o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+            o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+            o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+            o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
             *(u32x4*)(dst + (size_t)(i * 256 + tid) * 16) = o;
           }
           if (tid < TT) lds_sc[it % NBUF][tid] = scv;
@@ -1165,8 +1160,7 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
 // scale per (piece, head) (MFMA kernel, format 2), as the format word says; the scale is folded
 // into the piece weights.
 namespace cmb {
-constexpr int CH = 8;        // heads per block
-constexpr int MAXP = 1024;   // pieces per sequence handled in one pass of the piece list
+constexpr int CH = 8;        // most heads per block
 }
 
 __device__ __forceinline__ f32x4 load4(const float* p, int64_t i) { return ((const f32x4*)p)[i]; }
@@ -1175,16 +1169,57 @@ __device__ __forceinline__ f32x4 load4(const _Float16* p, int64_t i) {
   return __builtin_convertvector(((const f16x4_t*)p)[i], f32x4);
 }
 
-// every thread owns up to 4 float4 outputs per round; the loads of 4 pieces are issued before
-// their products are accumulated (piece order fixed, so the sum order is the same everywhere)
+// Weighted sum over the pieces. With ng = nh * d_c / 4 output groups of 4 elements:
+//  - ng >= 256: every thread owns up to 4 groups per round and issues the loads of 4 pieces
+//    before accumulating them;
+//  - ng < 256 (few heads per block, many pieces): psplit = 256 / ng threads share a group, thread
+//    part q takes pieces q, q + psplit, ..., and the parts are added through LDS in order q.
+// Either way the order of the sum is fixed for a given launch shape (deterministic).
+// The block covers columns [c0, c0 + dcc) of heads h0 .. h0 + nh - 1 (dcc < d_c only with nh = 1).
 template <typename PT>
 __device__ __forceinline__ void combine_sum(const PT* __restrict__ o_part, int n_h, int d_c, int h0, int nh,
-                                            int np, const int* slots, const float (*wts)[cmb::CH], float* dst) {
+                                            int c0, int dcc, int np, const int* slots,
+                                            const float* wts, int ws, float* dst, f32x4* red) {
   const int tid = threadIdx.x;
-  const int nv4 = nh * d_c / 4;
-  const PT* src = o_part + (int64_t)h0 * d_c;
+  const int nv4 = nh * dcc / 4;
+  const int d_c_ = dcc;  // row width seen by the group -> head mapping below
+  const PT* src = o_part + (int64_t)h0 * d_c + c0;
   const int64_t pstride = (int64_t)n_h * d_c / 4;  // 4-element groups per piece slot
   f32x4* dst4 = (f32x4*)dst;
+  if (nv4 < 256) {
+    const int psplit = 256 / nv4;
+    const int grp = tid % nv4, part = tid / nv4;
+    const float* wcol = wts + grp * 4 / d_c_;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (part < psplit) {
+      int i = part;
+      for (; i + 3 * psplit < np; i += 4 * psplit) {
+        f32x4 x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = load4(src, (int64_t)slots[i + k * psplit] * pstride + grp);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wk = wcol[(i + k * psplit) * ws];
+          acc[0] += wk * x[k][0]; acc[1] += wk * x[k][1]; acc[2] += wk * x[k][2]; acc[3] += wk * x[k][3];
+        }
+      }
+      for (; i < np; i += psplit) {
+        const f32x4 x = load4(src, (int64_t)slots[i] * pstride + grp);
+        const float wk = wcol[i * ws];
+        acc[0] += wk * x[0]; acc[1] += wk * x[1]; acc[2] += wk * x[2]; acc[3] += wk * x[3];
+      }
+      red[tid] = acc;
+    }
+    __syncthreads();
+    if (part == 0) {
+      for (int q = 1; q < psplit; ++q) {
+        const f32x4 y = red[q * nv4 + grp];
+        acc[0] += y[0]; acc[1] += y[1]; acc[2] += y[2]; acc[3] += y[3];
+      }
+      dst4[grp] = acc;
+    }
+    return;
+  }
   for (int e0 = 0; e0 < nv4; e0 += 1024) {
     int idx[4];
     f32x4 acc[4];
@@ -1205,7 +1240,7 @@ __device__ __forceinline__ void combine_sum(const PT* __restrict__ o_part, int n
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float wk = wts[i + k][(idx[v] < nv4 ? idx[v] : 0) * 4 / d_c];
+          const float wk = wts[(i + k) * ws + (idx[v] < nv4 ? idx[v] : 0) * 4 / d_c_];
           acc[v][0] += wk * x[k][v][0]; acc[v][1] += wk * x[k][v][1];
           acc[v][2] += wk * x[k][v][2]; acc[v][3] += wk * x[k][v][3];
         }
@@ -1215,7 +1250,7 @@ __device__ __forceinline__ void combine_sum(const PT* __restrict__ o_part, int n
       for (int v = 0; v < 4; ++v) {
         if (idx[v] >= nv4) continue;
         const f32x4 x = load4(src, (int64_t)slots[i] * pstride + idx[v]);
-        const float wk = wts[i][idx[v] * 4 / d_c];
+        const float wk = wts[i * ws + idx[v] * 4 / d_c_];
         acc[v][0] += wk * x[0]; acc[v][1] += wk * x[1]; acc[v][2] += wk * x[2]; acc[v][3] += wk * x[3];
       }
     }
@@ -1225,58 +1260,74 @@ __device__ __forceinline__ void combine_sum(const PT* __restrict__ o_part, int n
   }
 }
 
-__global__ __launch_bounds__(256) void k_combine(int n_h, int d_c, const int64_t* __restrict__ cu, int B, int G,
+// Dynamic LDS: slots[G] (piece slot of each range of the sequence, in range order), then lse and
+// scale of every (piece, head) and finally the weights, ch floats per piece each. A sequence is
+// covered by at most G ranges, so G entries always suffice.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_combine(int n_h, int d_c, int ch, int dcc, const int64_t* __restrict__ cu, int B, int G,
                                                  const int32_t* __restrict__ fmt,
                                                  const float* __restrict__ lse_part,
                                                  const float* __restrict__ sc_part,
                                                  const void* __restrict__ o_part, float* __restrict__ o_lat,
                                                  float* __restrict__ lse_out) {
-  using namespace cmb;
-  __shared__ int slots[MAXP];
-  __shared__ float wts[MAXP][CH];
+  extern __shared__ float dyn[];
+  __shared__ f32x4 red[256];
   __shared__ int sh_np;
+  int* slots = (int*)dyn;
+  float* lse_s = dyn + G;
+  float* sc_s = lse_s + (int64_t)G * ch;
+  float* wts = lse_s;  // the weights overwrite the lse values in place
   const int b = blockIdx.y;
-  const int h0 = blockIdx.x * CH;
-  const int nh = (n_h - h0) < CH ? (n_h - h0) : CH;
+  const int h0 = blockIdx.x * ch;
+  const int nh = (n_h - h0) < ch ? (n_h - h0) : ch;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t total = cu[B];
   const int64_t s0 = cu[b], s1 = cu[b + 1];
-  float* dst = o_lat + ((int64_t)b * n_h + h0) * d_c;
+  const int c0 = blockIdx.z * dcc;
+  float* dst = o_lat + ((int64_t)b * n_h + h0) * d_c + c0;
   if (s1 <= s0) {  // empty sequence (outside the contract): defined output
-    for (int e = tid; e < nh * d_c; e += 256) dst[e] = 0.f;
-    if (lse_out && tid < nh) lse_out[(int64_t)b * n_h + h0 + tid] = -__builtin_inff();
+    for (int e = tid; e < nh * dcc; e += 256) dst[(e / dcc) * d_c + e % dcc] = 0.f;
+    if (lse_out && tid < nh && blockIdx.z == 0) lse_out[(int64_t)b * n_h + h0 + tid] = -__builtin_inff();
     return;
   }
-  if (tid == 0) {
+  if (w == 0) {  // piece list, in range order: one candidate range per lane, compacted by ballot
     const int64_t plo = range_of(s0, total, G), phi = range_of(s1 - 1, total, G);
     int np = 0;
-    for (int64_t p = plo; p <= phi && np < MAXP; ++p)
-      if (range_start(p, total, G) != range_start(p + 1, total, G)) slots[np++] = (int)(p + b);
-    sh_np = np;
+    for (int64_t p0 = plo; p0 <= phi && np < G; p0 += 64) {
+      const int64_t p = p0 + lane;
+      const bool keep = p <= phi && range_start(p, total, G) != range_start(p + 1, total, G);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+      const int pos = np + (int)__builtin_popcountll(m & ((1ull << lane) - 1));
+      if (keep && pos < G) slots[pos] = (int)(p + b);
+      np += (int)__builtin_popcountll(m);
+    }
+    if (lane == 0) sh_np = np < G ? np : G;
   }
   __syncthreads();
   const int np = sh_np;
   const bool f16 = *fmt == 2;
+  // every (piece, head) lse and scale, loaded by the whole block in one pass
+  for (int e = tid; e < np * nh; e += 256) {
+    const int i = e / nh, hh = e - i * nh;
+    const int64_t r = (int64_t)slots[i] * n_h + h0 + hh;
+    lse_s[i * ch + hh] = lse_part[r];
+    sc_s[i * ch + hh] = f16 ? sc_part[r] : 1.f;
+  }
+  __syncthreads();
   // weights: wave w handles heads w, w+4, ...
   for (int hh = w; hh < nh; hh += 4) {
     float M = -__builtin_inff();
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, lse_part[(int64_t)slots[i] * n_h + h0 + hh]);
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, lse_s[i * ch + hh]);
     M = wave_max(M);
     float sum = 0.f;
-    for (int i = lane; i < np; i += 64) {
-      const float e = __expf(lse_part[(int64_t)slots[i] * n_h + h0 + hh] - M);
-      wts[i][hh] = e;
-      sum += e;
-    }
+    for (int i = lane; i < np; i += 64) sum += __expf(lse_s[i * ch + hh] - M);
     sum = wave_sum(sum);
     const float inv = 1.f / sum;
-    for (int i = lane; i < np; i += 64)
-      wts[i][hh] *= f16 ? inv * sc_part[(int64_t)slots[i] * n_h + h0 + hh] : inv;
-    if (lse_out && lane == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
+    for (int i = lane; i < np; i += 64) wts[i * ch + hh] = __expf(lse_s[i * ch + hh] - M) * inv * sc_s[i * ch + hh];
+    if (lse_out && lane == 0 && blockIdx.z == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
   }
   __syncthreads();
-  if (f16) combine_sum((const _Float16*)o_part, n_h, d_c, h0, nh, np, slots, wts, dst);
-  else combine_sum((const float*)o_part, n_h, d_c, h0, nh, np, slots, wts, dst);
+  if (f16) combine_sum((const _Float16*)o_part, n_h, d_c, h0, nh, c0, dcc, np, slots, wts, ch, dst, red);
+  else combine_sum((const float*)o_part, n_h, d_c, h0, nh, c0, dcc, np, slots, wts, ch, dst, red);
 }
 
 // ================================================================================================
@@ -1342,8 +1393,19 @@ hipError_t launch_combine(const mla_dims& d, int B, int G, const void* ws, float
                           hipStream_t st) {
   DecodeLayout L = decode_layout(d, B, G);
   const char* base = (const char*)ws;
-  dim3 grid((unsigned)((d.n_h + cmb::CH - 1) / cmb::CH), B);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, d.n_h, d.d_c, (const int64_t*)(base + L.off_cu), B, G,
+  // heads per block: up to CH, fewer when the batch is small, so that about 1024 blocks run
+  int ch = (int)(((int64_t)B * d.n_h) / 1024);
+  ch = ch < 1 ? 1 : (ch > cmb::CH ? cmb::CH : ch);
+  while (ch > 1 && (size_t)G * (4 + 8 * (size_t)ch) > 60 * 1024) --ch;  // dynamic LDS below 60 KB
+  // with one head per block and still few blocks, the columns are split too (chunks of >= 64)
+  int nchunk = 1;
+  if (ch == 1) {
+    const int64_t nb = (int64_t)B * d.n_h;
+    while (nb * nchunk * 2 <= 1024 && d.d_c % (nchunk * 2 * 4) == 0 && d.d_c / (nchunk * 2) >= 64) nchunk *= 2;
+  }
+  dim3 grid((unsigned)((d.n_h + ch - 1) / ch), B, nchunk);
+  const size_t smem = (size_t)G * (4 + 8 * (size_t)ch);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), smem, st, d.n_h, d.d_c, ch, d.d_c / nchunk, (const int64_t*)(base + L.off_cu), B, G,
                      (const int32_t*)(base + L.off_fmt), (const float*)(base + L.off_lse),
                      (const float*)(base + L.off_sc), (const void*)(base + L.off_o), o_lat, lse);
   return hipGetLastError();
