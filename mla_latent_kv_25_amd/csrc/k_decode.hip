@@ -702,11 +702,14 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
   constexpr int NBUF = v3::NBUF;
   constexpr float HEAD = 64.f;
   constexpr int FILL_STEPS = 20;  // softmax steps
+  constexpr int PB = NH * TT * 2;  // bytes of P of one tile, [head][token]
   __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_p[NH * TT * 2];  // P of one tile, [head][token]
-  __shared__ float lds_l[NH];
-  __shared__ float lds_m[4][NH];
-  __shared__ int redo_flag[1];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[2 * PB];  // P of two consecutive tiles
+  // scratch of the pass / segment end, on the tile ring (idle there: every copy has landed and
+  // every wave is past its last tile read at the barriers that precede each use)
+  int* const redo_flag = (int*)lds;
+  float* const lds_l = (float*)(lds + 16);
+  float (*const lds_m)[NH] = (float (*)[NH])(lds + 16 + NH * 4);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int p = range_for_block(blockIdx.x, G);
@@ -852,23 +855,28 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
 
       // softmax of one tile in FILL_STEPS steps; register r of s holds token 8(r/4) + 4g + r%4
       f32x16 S;
-      bf16x8 pk0, pk1;
       float mx = 0.f, rs = 0.f;
       int valid = TT;
-      auto fill = [&](int ks) __attribute__((always_inline)) {
-        if (ks == 0) {
-          if (valid < TT) {
-            // token 8(r/4) + 4g + r%4 is valid iff 8(r/4) + r%4 < valid - 4g (constants per r,
-            // so no per-register index is kept live)
-            const int vg = valid - 4 * g;
+      uint8_t* pw = lds_p;  // where fill() puts P
+      auto mask_tail = [&]() __attribute__((always_inline)) {
+        if (valid < TT) {
+          // token 8(r/4) + 4g + r%4 is valid iff 8(r/4) + r%4 < valid - 4g (constants per r,
+          // so no per-register index is kept live)
+          const int vg = valid - 4 * g;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = (8 * (r >> 2) + (r & 3)) < vg ? S[r] : -__builtin_inff();
-          }
+          for (int r = 0; r < 16; ++r) S[r] = (8 * (r >> 2) + (r & 3)) < vg ? S[r] : -__builtin_inff();
+        }
+      };
+      // Softmax step ks of the tile in S (tail already masked). `first`: the segment's first
+      // tile, which fixes m_ref (pass 0); inside the tile loop m_ref is set and the steps are
+      // branch-free, so they interleave with the PV MFMAs.
+      auto fill = [&](int ks, bool first) __attribute__((always_inline)) {
+        if (ks == 0) {
           mx = fmaxf(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])), fmaxf(fmaxf(S[4], S[5]), fmaxf(S[6], S[7])));
           mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(S[8], S[9]), fmaxf(S[10], S[11])),
                                fmaxf(fmaxf(S[12], S[13]), fmaxf(S[14], S[15]))));
         } else if (ks == 1) {
-          if (!have_ref) {  // first tile of the segment: the head's maximum over both halves
+          if (first && !have_ref) {  // first tile of the segment: the head's maximum over both halves
             m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
             have_ref = true;
           }
@@ -877,22 +885,26 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
           rs = 0.f;
         } else if (ks < 18) {
           const int r = ks - 2;
+          // keeps the step behind the MFMA issued before it (the MFMAs are volatile asm)
+          if (!first) asm volatile("" : "+v"(S[r]));
           // no clamp: a score past m_ref + HEAD sets `over`, and the whole pass is redone
           const float e = __builtin_amdgcn_exp2f(S[r] - m_ref);
           rs += e;
           S[r] = e;
-        } else if (ks == 18) {
+        } else if (ks == 18) {  // P of this tile straight to lds_p, [head][token], swizzled
           l_lane += rs;
-          pk0 = bf16x8{(__bf16)S[0], (__bf16)S[1], (__bf16)S[2], (__bf16)S[3],
-                       (__bf16)S[4], (__bf16)S[5], (__bf16)S[6], (__bf16)S[7]};
+          *(bf16x8*)(pw + head * 64 + ((g ^ ((head >> 2) & 3)) << 4)) =
+              bf16x8{(__bf16)S[0], (__bf16)S[1], (__bf16)S[2], (__bf16)S[3],
+                     (__bf16)S[4], (__bf16)S[5], (__bf16)S[6], (__bf16)S[7]};
         } else if (ks == 19) {
-          pk1 = bf16x8{(__bf16)S[8], (__bf16)S[9], (__bf16)S[10], (__bf16)S[11],
-                       (__bf16)S[12], (__bf16)S[13], (__bf16)S[14], (__bf16)S[15]};
+          *(bf16x8*)(pw + head * 64 + (((2 + g) ^ ((head >> 2) & 3)) << 4)) =
+              bf16x8{(__bf16)S[8], (__bf16)S[9], (__bf16)S[10], (__bf16)S[11],
+                     (__bf16)S[12], (__bf16)S[13], (__bf16)S[14], (__bf16)S[15]};
         }
       };
 
-      // PV of tile `tile` (P from lds_p) with between(j) after MFMA j (0..31)
-      auto pv = [&](const uint8_t* tile) __attribute__((always_inline)) {
+      // PV of tile `tile` (P from `pr`) with between(j) after MFMA j (0..31)
+      auto pv = [&](const uint8_t* tile, const uint8_t* pr, auto&& between) __attribute__((always_inline)) {
         uint32_t vb[2][2][2];
         const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 256u * w;
 #pragma unroll
@@ -915,7 +927,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
         };
         auto ldp = [&](int kk, int hb) __attribute__((always_inline)) -> bf16x8 {
           const int hr = 32 * hb + l32;
-          return *(const bf16x8*)(lds_p + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
+          return *(const bf16x8*)(pr + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
         };
         u32x4 av[4];
         bf16x8 pbc, pbn;
@@ -937,6 +949,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
                 asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                              : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
               }
+              between(16 * kk + 4 * hb + cb);
               if (kk == 0 && hb == 3) av[cb] = ldv(1, cb);
             }
             pbc = pbn;
@@ -944,29 +957,44 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
         }
       };
 
-      for (int it = 0; it < ntiles; ++it) {
-        if (it + 2 < ntiles) vm_wait_barrier<2 * LOADS>();
-        else if (it + 1 < ntiles) vm_wait_barrier<LOADS>();
-        else vm_wait_barrier<0>();
-        valid = valid_of(it);
-        if (it + 3 < ntiles) {
-          const CopyPlan cp = plan_tile(it + 3);
-          S = tile_scores_copy(lds + (it % NBUF) * TILEB, kq, qf, [&](int ks) __attribute__((always_inline)) {
-            if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4);
-          });
-        } else {
-          S = tile_scores(lds + (it % NBUF) * TILEB, kq, qf);
-        }
+      // Software pipeline over the tiles of the segment. Iteration it computes the scores of tile
+      // it + 1, issuing the copies of tile it + 3 (into the buffer of tile it - 1) between its
+      // MFMAs, then PV of tile it with the softmax of tile it + 1 between the PV MFMAs. P
+      // alternates between the two halves of lds_p; one barrier per tile orders it all.
+      auto tile_buf = [&](int it) -> const uint8_t* { return lds + (it % NBUF) * TILEB; };
+      if (ntiles > 2) vm_wait_barrier<2 * LOADS>();
+      else if (ntiles > 1) vm_wait_barrier<LOADS>();
+      else vm_wait_barrier<0>();
+      S = tile_scores(lds, kq, qf);
+      valid = valid_of(0);
+      mask_tail();
+      pw = lds_p;
 #pragma unroll
-        for (int ks = 0; ks < FILL_STEPS; ++ks) fill(ks);
-        {
-          const int key = (head >> 2) & 3;
-          uint8_t* prow = lds_p + head * 64;
-          *(bf16x8*)(prow + ((g ^ key) << 4)) = pk0;
-          *(bf16x8*)(prow + (((2 + g) ^ key) << 4)) = pk1;
+      for (int ks = 0; ks < FILL_STEPS; ++ks) fill(ks, true);
+      for (int it = 0; it < ntiles; ++it) {
+        // P(it) visible, tile it + 1 resident (tile it + 2 may be in flight), every wave past PV(it - 1)
+        if (it + 2 < ntiles) vm_wait_barrier<LOADS>();
+        else vm_wait_barrier<0>();
+        const uint8_t* pr = lds_p + (it & 1) * PB;
+        if (it + 1 < ntiles) {
+          const uint8_t* tn = tile_buf(it + 1);
+          if (it + 3 < ntiles) {
+            const CopyPlan cp = plan_tile(it + 3);
+            S = tile_scores_copy(tn, kq, qf, [&](int ks) __attribute__((always_inline)) {
+              if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4);
+            });
+          } else {
+            S = tile_scores(tn, kq, qf);
+          }
         }
-        __syncthreads();
-        pv(lds + (it % NBUF) * TILEB);
+        // after the last tile the softmax runs on no valid token: every score is masked, so it
+        // adds nothing and only writes zeros into the P buffer nobody reads any more
+        valid = it + 1 < ntiles ? valid_of(it + 1) : 0;
+        mask_tail();
+        pw = lds_p + ((it + 1) & 1) * PB;
+        pv(tile_buf(it), pr, [&](int j) __attribute__((always_inline)) {
+          if (j < FILL_STEPS) fill(j, false);
+        });
       }
       // does any head of the workgroup need the second pass?
       __syncthreads();
