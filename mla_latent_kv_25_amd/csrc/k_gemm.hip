@@ -40,10 +40,12 @@ static int cdiv(int a, int b) { return (a + b - 1) / b; }
 struct QSplits { int sk1; };
 static QSplits q_splits(const mla_dims& d) { return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT), d.d / gm::KC, 1)}; }
 struct OSplits { int sk4, sk5; };
-static OSplits o_splits(const mla_dims& d) {
+// W^O runs on 256-row tiles when the batch chunk is at most 64 rows
+static bool o_wide(int nb) { return nb <= 64; }
+static OSplits o_splits(const mla_dims& d, int nb) {
   // W^UV: one workgroup per (head, 128 rows); a K split would add a reduction pass costing more
   // than the idle compute units at n_h = 128
-  return {1, split_for(cdiv(d.d, gm::MT), d.n_h * d.d_h / gm::KC, 1)};
+  return {1, split_for(cdiv(d.d, o_wide(nb) ? 2 * gm::MT : gm::MT), d.n_h * d.d_h / gm::KC, 1)};
 }
 
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
@@ -59,7 +61,7 @@ AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
 AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B) {
   AbsorbOutLayout L;
   const int nb = B < gm::MAXB ? B : gm::MAXB;
-  const OSplits sp = o_splits(d);
+  const OSplits sp = o_splits(d, nb);
   L.off_o = 0;
   L.off_part = al256h((size_t)B * d.n_h * d.d_h * 4);
   const size_t p4 = (size_t)sp.sk4 * d.n_h * nb * d.d_h, p5 = (size_t)sp.sk5 * nb * d.d;
@@ -100,31 +102,57 @@ __device__ __forceinline__ void wait_copies_barrier() {
 
 // ================================================================================================
 // Weight-streaming MFMA GEMM: Y[n][m] = sum_k W(m, k) X[n][k], W bf16 row-major (lda = K).
-// Workgroup = 128 output rows x all N <= 32*NB columns, over one K slice. The slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the
-// matching X columns) filled by direct global->LDS copies, NS-1 stages ahead of the MFMAs.
-// LDS rows are XOR-swizzled in 16-byte chunks so the MFMA fragment reads are conflict-free.
-// The reduction index is permuted inside each 64-k stage: in step st, lane half g supplies
-// k = 32g + 8st + 0..7 for both operands (the same real k on both sides of every product).
+// Workgroup = 32*MB output rows x all N <= 32*NB columns, over one K slice, one wave per SIMD. The
+// slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the matching X
+// columns) filled by direct global->LDS copies, up to NS-1 stages ahead of the MFMAs. LDS rows
+// are XOR-swizzled in 16-byte chunks so the MFMA fragment reads are conflict-free.
+// Wave w runs k-step w of every stage for all rows (MB m-blocks) and all N columns; the four
+// partial tiles are summed through LDS at the end. The reduction index is permuted inside each
+// 64-k stage: in k-step st, lane half g supplies k = 32g + 8st + 0..7 for both operands (the same
+// real k on both sides of every product).
+// Software pipeline per stage j: the copies of stage j + NS - 1 are issued one after each of the
+// first MFMAs; four MFMAs before the end, the wave waits for stage j + 1, joins the barrier and
+// requests the next fragments, so the LDS latency and the barrier hide under the last MFMAs.
+// The MFMAs are volatile asm (the copies must stay between them): each starts with 2 wait states
+// for a VALU-written operand, and the accumulators are read only after the loop's closing nops.
 //   XF32: X is float32, split on the fly into bf16 hi + lo (2 MFMAs, ~16 significand bits);
 //         otherwise X is bf16.
 //   split_k > 1: partial sums go to part[(ky * Z + z) * N + n][m] for the ordered reduction.
-template <int NB, bool XF32>
+template <int NB, bool XF32, int MB>
 struct WCfg {
-  static constexpr int WB = gm::MT * gm::KC * 2;                 // W bytes per stage (16 KB)
+  static constexpr int WB = 32 * MB * gm::KC * 2;                // W bytes per stage
   static constexpr int XROW = gm::KC * (XF32 ? 4 : 2);            // X bytes per row per stage
   static constexpr int XB = NB * 32 * XROW;                       // X bytes per stage
   static constexpr int SB = WB + XB;
-  static constexpr int NS = (147456 / SB) < 6 ? (147456 / SB) : 6;
+  static constexpr int NS = (163840 / SB) < 6 ? (163840 / SB) : 6;
   static constexpr int DW = WB / 4096;                            // copies per thread per stage
   static constexpr int DX = XB / 4096;
+  static constexpr int DT = DW + DX;
+  static constexpr int NM = MB * NB * (XF32 ? 2 : 1);             // MFMAs per wave per stage
 };
 
-template <int NB, bool XF32>
+template <int N>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  switch (ahead) {
+    case 0: wait_copies_barrier<0>(); break;
+    case 1: wait_copies_barrier<N>(); break;
+    case 2: wait_copies_barrier<2 * N>(); break;
+    case 3: wait_copies_barrier<3 * N>(); break;
+    default: wait_copies_barrier<4 * N>(); break;
+  }
+}
+
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+template <int NB, bool XF32, int MB>
 __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part,
                                                   int Mtot, int64_t zW, int64_t zX, int64_t zY) {
-  using C = WCfg<NB, XF32>;
-  constexpr int MT = gm::MT, KC = gm::KC, NS = C::NS, DT = C::DW + C::DX;
+  using C = WCfg<NB, XF32, MB>;
+  constexpr int MT = 32 * MB, KC = gm::KC, NS = C::NS, DT = C::DT, NM = C::NM;
+  static_assert(NS >= 3 && (NS - 1) * DT <= 63, "ring depth / vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * C::SB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -144,14 +172,14 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
   // chunk p % 8, which holds logical chunk (p % 8) ^ ((row / 2) % 8). X slot (bf16): same with
   // 8 chunks per row; X slot (float32): 16 chunks per row, logical chunk (p % 16) ^ (row % 16).
   // Rows past the segment / past N re-read the last valid row (their results are dropped).
-  uint32_t wofs[C::DW], xofs[C::DX];
+  uint32_t ofs[DT];
   {
     const int wc = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
     for (int i = 0; i < C::DW; ++i) {
       int row = i * 32 + (tid >> 3);
       if (row > seg_rows - r0 - 1) row = seg_rows - r0 - 1;
-      wofs[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(wc << 4);
+      ofs[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(wc << 4);
     }
 #pragma unroll
     for (int i = 0; i < C::DX; ++i) {
@@ -160,24 +188,23 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
       if constexpr (XF32) { row = p >> 4; c = (p & 15) ^ (row & 15); }
       else { row = p >> 3; c = (p & 7) ^ ((row >> 1) & 7); }
       if (row > N - 1) row = N - 1;
-      xofs[i] = (uint32_t)((int64_t)row * ldx * ESX) + (uint32_t)(c << 4);
+      ofs[C::DW + i] = (uint32_t)((int64_t)row * ldx * ESX) + (uint32_t)(c << 4);
     }
   }
-  auto issue = [&](int j) {
+  // copy i (0 .. DT-1) of stage j: W pieces first, then X pieces
+  auto copy = [&](int j, int i) __attribute__((always_inline)) {
     const int kst = (st0 + j) * KC;
     uint8_t* buf = lds + (j % NS) * C::SB;
-    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
-    const uint8_t* wsrc = Wb + (int64_t)kst * 2;
-#pragma unroll
-    for (int i = 0; i < C::DW; ++i) g2l16(wsrc, wofs[i], wl + i * 4096);
-    const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
-    const uint8_t* xsrc = Xb + (int64_t)kst * ESX;
-#pragma unroll
-    for (int i = 0; i < C::DX; ++i) g2l16(xsrc, xofs[i], xl + i * 4096);
+    if (i < C::DW) {
+      const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
+      g2l16(Wb + (int64_t)kst * 2, ofs[i], wl + i * 4096);
+    } else {
+      const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
+      g2l16(Xb + (int64_t)kst * ESX, ofs[i], xl + (i - C::DW) * 4096);
+    }
   };
 
-  // Wave w runs k-step w of every stage for all 128 rows (4 m-blocks) and all N columns; the
-  // four partial tiles are summed through LDS at the end. Fragment offsets inside a stage:
+  // Fragment offsets inside a stage (k-step w):
   //   A (m-block mb): row 32 mb + l32, logical chunk 4g + w;  B (bf16): row 32 jb + l32, same
   //   chunk;  B (float32): row 32 jb + l32, logical chunks 8g + 2w and 8g + 2w + 1.
   const int key8 = (l32 >> 1) & 7;
@@ -186,53 +213,81 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
   const uint32_t bofx0 = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * w) ^ (l32 & 15)) << 4));
   const uint32_t bofx1 = (uint32_t)(C::WB + l32 * 256 + (((8 * g + 2 * w + 1) ^ (l32 & 15)) << 4));
 
-  f32x16 acc[4][NB];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[mb][j] = f32x16{};
-
-  for (int j = 0; j < NS - 1 && j < ns; ++j) issue(j);
-  for (int j = 0; j < ns; ++j) {
-    const int ahead = (ns - 1 - j) < (NS - 2) ? (ns - 1 - j) : (NS - 2);
-    switch (ahead) {
-      case 0: wait_copies_barrier<0>(); break;
-      case 1: wait_copies_barrier<DT>(); break;
-      case 2: wait_copies_barrier<(NS > 3 ? 2 * DT : 0)>(); break;
-      case 3: wait_copies_barrier<(NS > 4 ? 3 * DT : 0)>(); break;
-      default: wait_copies_barrier<(NS > 5 ? 4 * DT : 0)>(); break;
-    }
-    if (j + NS - 1 < ns) issue(j + NS - 1);
+  // raw fragments of one stage, straight from LDS
+  struct Frag {
+    bf16x8 a[MB];
+    f32x4 x0[XF32 ? NB : 1], x1[XF32 ? NB : 1];
+    bf16x8 b[XF32 ? 1 : NB];
+  };
+  auto load_frag = [&](int j, Frag& f) __attribute__((always_inline)) {
     const uint8_t* buf = lds + (j % NS) * C::SB;
-    bf16x8 a[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) a[mb] = *(const bf16x8*)(buf + aoff + mb * 32 * 128);
+    for (int mb = 0; mb < MB; ++mb) f.a[mb] = *(const bf16x8*)(buf + aoff + mb * 32 * 128);
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
       if constexpr (XF32) {
-        const f32x4 x0 = *(const f32x4*)(buf + bofx0 + jb * 32 * 256);
-        const f32x4 x1 = *(const f32x4*)(buf + bofx1 + jb * 32 * 256);
-        bf16x8 bh, bl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
-          bh[e] = h0; bh[4 + e] = h1;
-          bl[e] = (__bf16)(x0[e] - (float)h0);
-          bl[4 + e] = (__bf16)(x1[e] - (float)h1);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bh, acc[mb][jb], 0, 0, 0);
-          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bl, acc[mb][jb], 0, 0, 0);
-        }
+        f.x0[jb] = *(const f32x4*)(buf + bofx0 + jb * 32 * 256);
+        f.x1[jb] = *(const f32x4*)(buf + bofx1 + jb * 32 * 256);
       } else {
-        const bf16x8 b = *(const bf16x8*)(buf + boff + jb * 32 * 128);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[mb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b, acc[mb][jb], 0, 0, 0);
+        f.b[jb] = *(const bf16x8*)(buf + boff + jb * 32 * 128);
       }
     }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[mb][j] = f32x16{};
+
+  for (int j = 0; j < NS - 1 && j < ns; ++j)
+#pragma unroll
+    for (int i = 0; i < DT; ++i) copy(j, i);
+  {
+    const int ahead = (ns - 1) < (NS - 2) ? (ns - 1) : (NS - 2);
+    wait_ahead<DT>(ahead);
   }
+  Frag cur;
+  load_frag(0, cur);
+  constexpr int QB = NM > 4 ? NM - 4 : 0;  // MFMA slot before which the next stage is requested
+  for (int j = 0; j < ns; ++j) {
+    const bool more = j + 1 < ns;
+    const bool refill = j + NS - 1 < ns;
+    Frag nxt;
+    bf16x8 bh, bl;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      // MFMA order: (jb, half, mb); one accumulator is never used by two consecutive MFMAs
+      const int jb = q / (XF32 ? 2 * MB : MB), half = XF32 ? (q / MB) & 1 : 0, mb = q % MB;
+      if (q == QB) {
+        if (refill)
+#pragma unroll
+          for (int i = (QB < DT ? QB : DT); i < DT; ++i) copy(j + NS - 1, i);
+        if (more) {
+          const int ahead = (ns - 2 - j) < (NS - 2) ? (ns - 2 - j) : (NS - 2);
+          wait_ahead<DT>(ahead);
+          load_frag(j + 1, nxt);
+        }
+      }
+      if constexpr (XF32) {
+        if (q % (2 * MB) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const __bf16 h0 = (__bf16)cur.x0[jb][e], h1 = (__bf16)cur.x1[jb][e];
+            bh[e] = h0; bh[4 + e] = h1;
+            bl[e] = (__bf16)(cur.x0[jb][e] - (float)h0);
+            bl[4 + e] = (__bf16)(cur.x1[jb][e] - (float)h1);
+          }
+        }
+        mfma_acc(acc[mb][jb], cur.a[mb], half ? bl : bh);
+      } else {
+        mfma_acc(acc[mb][jb], cur.a[mb], cur.b[jb]);
+      }
+      if (refill && q < QB && q < DT) copy(j + NS - 1, q);
+    }
+    cur = nxt;
+  }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // last MFMA results readable
 
   // Sum of the four waves' tiles, one m-block at a time through two alternating LDS regions
   // (wave-major, fixed order w = 0..3). Accumulator element r of lane (g, l32) is column
@@ -241,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
   constexpr int RB = 4 * NB * 4 * 64;  // float4 slots per region (waves x blocks x r4 x lanes)
   f32x4* red = (f32x4*)lds;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     f32x4* reg = red + (mb & 1) * RB;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
@@ -479,21 +534,28 @@ static bool mfma_dims_ok(const mla_dims& d) {
          d.d_h == absq::DH && (d.n_h * d.d_h) % 256 == 0;
 }
 
-template <int NB, bool XF32>
+template <int NB, bool XF32, int MB>
 static void wgemm_nb(hipStream_t st, dim3 grid, const Seg& sg, int N, int K, const void* X, int64_t ldx,
                      int split_k, float* part, int Mtot, int64_t zW, int64_t zX, int64_t zY) {
-  hipLaunchKernelGGL((k_wgemm<NB, XF32>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  hipLaunchKernelGGL((k_wgemm<NB, XF32, MB>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
 }
 
-// Y = W X over stacked segments (segment boundaries on multiples of gm::MT), N <= gm::MAXB.
+// Y = W X over stacked segments (segment boundaries on multiples of the row tile), N <= gm::MAXB.
+// wide: 256-row tiles (half the X traffic per W byte) where N <= 64; else 128-row tiles.
 template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
-                      float* part, int Z, int64_t zW, int64_t zX, int64_t zY) {
+                      float* part, int Z, int64_t zW, int64_t zX, int64_t zY, bool wide = false) {
   const int Mtot = sg.m0[sg.nseg];
-  dim3 grid(cdiv(Mtot, gm::MT), split_k, Z);
-  if (N <= 32) wgemm_nb<1, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
-  else if (N <= 64) wgemm_nb<2, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
-  else wgemm_nb<4, XF32>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  wide = wide && N <= 64;
+  dim3 grid(cdiv(Mtot, wide ? 2 * gm::MT : gm::MT), split_k, Z);
+  if (wide) {
+    if (N <= 32) wgemm_nb<1, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else wgemm_nb<2, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  } else {
+    if (N <= 32) wgemm_nb<1, XF32, 4>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else if (N <= 64) wgemm_nb<2, XF32, 4>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else wgemm_nb<4, XF32, 4>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  }
   if (split_k > 1) {
     const int64_t tot = (int64_t)N * (Mtot / 4);
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((tot + 255) / 256), Z), dim3(256), 0, st, sg, N, Mtot,
@@ -565,14 +627,14 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
       Seg s4{};
       s4.W[0] = W_uv; s4.Y[0] = o + (int64_t)b0 * nhdh; s4.ldy[0] = nhdh;
       s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
-      const OSplits sp = o_splits(d);
+      const OSplits sp = o_splits(d, nb);
       mfma_gemm<true>(st, s4, nb, d.d_c, o_lat + (int64_t)b0 * d.n_h * d.d_c, (int64_t)d.n_h * d.d_c, sp.sk4, part,
                       d.n_h, (int64_t)d.d_h * d.d_c, d.d_c, d.d_h);
       // u = W^O [o_1; ...; o_nh]
       Seg s5{};
       s5.W[0] = W_o; s5.Y[0] = u + (int64_t)b0 * d.d; s5.ldy[0] = d.d;
       s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0);
+      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0, o_wide(nb));
     }
     return hipGetLastError();
   }
