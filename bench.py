@@ -23,6 +23,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+# HBM bytes per decode_attn launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), both scaled by
+# a plain copy of known size; recorded in profiles/decode_attn_config2_hbm_counters.md for the
+# decode kernel as it stands. Workloads without a recorded measurement report null.
+DECODE_TRAFFIC_BYTES = {"2": 158748 * 1024 * 2 + 37380 * 1024}
 
 
 def parse():
@@ -222,7 +226,7 @@ def main():
         "weights_gbps": {"absorb_q": wq_bytes / stage[0] / 1e9, "absorb_out": wo_bytes / stage[4] / 1e9},
         "attn_mfma_tflops": flops_attn / t_dec / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": DECODE_TRAFFIC_BYTES.get(cfg.key),
                      "kernel": "decode_attn", "bytes_per_launch": cache_bytes,
                      "per_unit": f"{row_bytes} B per cached token x {sigma_T} tokens"},
         "wall_s": wall,
