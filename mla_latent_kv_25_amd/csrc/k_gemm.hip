@@ -43,8 +43,7 @@ struct OSplits { int sk4, sk5; };
 // W^O runs on 256-row tiles when the batch chunk is at most 64 rows
 static bool o_wide(int nb) { return nb <= 64; }
 static OSplits o_splits(const mla_dims& d, int nb) {
-  // W^UV: one workgroup per (head, 128 rows); a K split would add a reduction pass costing more
-  // than the idle compute units at n_h = 128
+  // W^UV: one workgroup per (head, 64 rows); a K split would add a reduction pass
   return {1, split_for(cdiv(d.d, o_wide(nb) ? 2 * gm::MT : gm::MT), d.n_h * d.d_h / gm::KC, 1)};
 }
 
@@ -541,16 +540,22 @@ static void wgemm_nb(hipStream_t st, dim3 grid, const Seg& sg, int N, int K, con
 }
 
 // Y = W X over stacked segments (segment boundaries on multiples of the row tile), N <= gm::MAXB.
-// wide: 256-row tiles (half the X traffic per W byte) where N <= 64; else 128-row tiles.
+// Row tiles of 32*mb rows: mb = 8 halves the X traffic per W byte (N <= 64 only), mb = 2 doubles
+// the workgroup count of short problems; otherwise 128 rows.
+static int tile_mb(int mb, int N) { return (mb == 8 && N > 64) ? 4 : mb; }
 template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
-                      float* part, int Z, int64_t zW, int64_t zX, int64_t zY, bool wide = false) {
+                      float* part, int Z, int64_t zW, int64_t zX, int64_t zY, int mb = 4) {
   const int Mtot = sg.m0[sg.nseg];
-  wide = wide && N <= 64;
-  dim3 grid(cdiv(Mtot, wide ? 2 * gm::MT : gm::MT), split_k, Z);
-  if (wide) {
+  mb = tile_mb(mb, N);
+  dim3 grid(cdiv(Mtot, 32 * mb), split_k, Z);
+  if (mb == 8) {
     if (N <= 32) wgemm_nb<1, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
     else wgemm_nb<2, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  } else if (mb == 2) {
+    if (N <= 32) wgemm_nb<1, XF32, 2>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else if (N <= 64) wgemm_nb<2, XF32, 2>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else wgemm_nb<4, XF32, 2>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
   } else {
     if (N <= 32) wgemm_nb<1, XF32, 4>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
     else if (N <= 64) wgemm_nb<2, XF32, 4>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
@@ -629,12 +634,12 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
       s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
       const OSplits sp = o_splits(d, nb);
       mfma_gemm<true>(st, s4, nb, d.d_c, o_lat + (int64_t)b0 * d.n_h * d.d_c, (int64_t)d.n_h * d.d_c, sp.sk4, part,
-                      d.n_h, (int64_t)d.d_h * d.d_c, d.d_c, d.d_h);
+                      d.n_h, (int64_t)d.d_h * d.d_c, d.d_c, d.d_h, 2);
       // u = W^O [o_1; ...; o_nh]
       Seg s5{};
       s5.W[0] = W_o; s5.Y[0] = u + (int64_t)b0 * d.d; s5.ldy[0] = d.d;
       s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0, o_wide(nb));
+      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0, o_wide(nb) ? 8 : 4);
     }
     return hipGetLastError();
   }
