@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
+    ap.add_argument("--prefill", type=int, default=0, metavar="C",
+                    help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
+                         "(a separate JSON line; the default run is the decode step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -101,10 +104,87 @@ def cpu_baseline(case, budget_s):
                       f"{dt:.1f} s, numpy float64 explicit K/V reconstruction"}
 
 
+def prefill_bench(args):
+    """Chunked prefill of C tokens per sequence (B=16, 2048 stored rows each, bf16 V2 shape, paged):
+    mla_prefill_tables + the five decode calls over B*C causal pseudo-sequences. Throughput in chunk
+    tokens/s; the dominant kernel (decode_attn over the pseudo-sequences) is priced against the
+    dense bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_25_amd as mla
+    from synth import get_config, make_prefill_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mla.lib()
+    C, B, P0 = args.prefill, 16, 2048
+    cfg = get_config("3")
+    case = make_prefill_case(cfg, [P0] * B, C, device="cuda")
+    dims = case.dims
+    cache = build_cache(mla, case)
+    pf = mla.PrefillStep(dims, B, C, int(case.block_table.shape[1]), args.splits)
+    W = case.weights
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mla.prefill_tables(cache, B, C, case.p0, pf.seq_lens, pf.block_table)
+        view = mla.LatentCache(cache.rows, cache.dtype, cache.t_cap, cache.scales, pf.block_table, cache.page_size)
+        st, d = pf.step, pf.dims
+        mla.absorb_q(d, case.h_chunk.view(B * C, -1), W, st.ws_q, st.q_lat, st.q_pe, st.kv_new)
+        mla.rope(d, pf.seq_lens, st.q_pe, st.kv_new, view)
+        if ev is not None:
+            ev[1].record()
+        mla.decode_attn(d, st.q_lat, st.q_pe, view, pf.seq_lens, args.splits, st.ws_d)
+        if ev is not None:
+            ev[2].record()
+        mla.combine(d, args.splits, pf.seq_lens, st.ws_d, st.o_lat, st.lse)
+        mla.absorb_out(d, st.o_lat, W["W_uv"], W["W_o"], st.ws_o, st.u)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    st = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) * 1e-3 for k in range(3)]
+    pairs = B * (C * P0 + C * (C + 1) // 2)                     # (query, key) pairs of the chunk
+    flops = pairs * 2 * dims.n_h * (dims.row + dims.d_c)         # 278,528 flop per pair at V2
+    achieved = flops / st[1] / 1e12
+    out = {
+        "metric": "MLA chunked-prefill tokens/s (chunk tokens), 1 MI355X",
+        "value": B * C / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 attention shape)",
+        "config": {"workload": f"chunked prefill: B={B} sequences x {P0} stored rows, chunk C={C}, bf16 paged "
+                               f"cache (64-row pages), DeepSeek-V2 shape", "batch": B, "chunk": C, "prefix": P0,
+                   "pseudo_sequences": B * C},
+        "kernels_us": {"tables+absorb_q+rope": st[0] * 1e6, "decode_attn": st[1] * 1e6,
+                       "combine+absorb_out": st[2] * 1e6, "step": ms * 1e3},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "decode_attn",
+                     "flops_per_launch": flops, "per_unit": f"278,528 flop per (query, key) pair x {pairs} pairs"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "

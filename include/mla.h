@@ -9,6 +9,7 @@
  * attention runs against the latents directly and the full keys/values are never formed.
  *
  * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
+ * (chunked prefill: mla_prefill_tables, then the same five calls over the pseudo-sequences)
  *
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers unless the comment says host. Tensors and workspaces must be
@@ -174,6 +175,21 @@ MLA_API size_t mla_absorb_out_workspace_bytes(const mla_dims* dims, int32_t B);
 MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
                           const void* W_uv, const void* W_o, void* workspace, size_t ws_bytes,
                           float* u, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_prefill_tables — chunked prefill through the decode calls.
+ * "DeepSeek-V2 from Scratch" section 6 gives attention for token t over positions 0..t. A chunk
+ * of C new tokens per sequence (positions p0[b] .. p0[b] + C - 1) is run as a batch of B * C
+ * causal pseudo-sequences: pseudo-sequence b * C + t is token t of sequence b's chunk, with length
+ * p0[b] + t + 1 and sequence b's pages. With these tables, the five calls of a decode step over
+ * B * C pseudo-sequences (h rows ordered the same way) append every chunk token's row at its
+ * position and give each token its causal attention output, exactly as C decode steps in turn.
+ *   cache: the paged cache (page_size > 0; its block_table is [B, max_pages] device int32).
+ *   p0: device int32 [B], rows already in the cache per sequence; p0[b] + C <= max_pages *
+ *       page_size and the pages covering those positions assigned (caller's contract).
+ *   seq_lens_out: device int32 [B * C]; block_table_out: device int32 [B * C, max_pages]. */
+MLA_API mla_status mla_prefill_tables(const mla_cache* cache, int32_t B, int32_t C, const int32_t* p0,
+                              int32_t* seq_lens_out, int32_t* block_table_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_cache_store — write given rows into a cache (prefix fill; not part of a decode step).

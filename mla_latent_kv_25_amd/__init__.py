@@ -4,7 +4,9 @@ The compute lives in libmla.so (HIP kernels for gfx950 behind the C ABI of inclu
 this package is its Python binding.
 """
 from .binding import (  # noqa: F401
-    BF16, F16, F32, FP8_E4M3, DecodeStep, Dims, LatentCache, MLAError, absorb_out, absorb_out_workspace_bytes,
-    absorb_q, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib, rope,
+    BF16, F16, F32, FP8_E4M3, DecodeStep, Dims, LatentCache, MLAError, PrefillStep, absorb_out,
+    absorb_out_workspace_bytes,
+    absorb_q, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib,
+    prefill_tables, rope,
     version,
 )

@@ -63,6 +63,7 @@ def lib():
         "mla_combine": (I32, [D, I32, I32, P, P, SZ, P, P, ST]),
         "mla_absorb_out_workspace_bytes": (SZ, [D, I32]),
         "mla_absorb_out": (I32, [D, I32, I32, P, P, P, P, SZ, P, ST]),
+        "mla_prefill_tables": (I32, [C, I32, I32, P, P, P, ST]),
         "mla_cache_store": (I32, [D, C, I32, P, I32, P, I64, ST]),
         "mla_status_str": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
@@ -78,7 +79,7 @@ def lib():
 
 EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_decode_workspace_bytes",
            "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
-           "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
+           "mla_prefill_tables", "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
 
 
 def _check(status: int):
@@ -197,6 +198,14 @@ def absorb_out(dims: Dims, o_lat, W_uv, W_o, workspace, u):
                                 _ptr(u, torch.float32, "u"), _stream()))
 
 
+def prefill_tables(cache: LatentCache, B: int, C: int, p0, seq_lens_out, block_table_out):
+    """Lengths and block tables of the B * C causal pseudo-sequences of a C-token prefill chunk."""
+    cc = cache.c()
+    _check(lib().mla_prefill_tables(ctypes.byref(cc), B, C, _ptr(p0, torch.int32, "p0"),
+                                    _ptr(seq_lens_out, torch.int32, "seq_lens_out"),
+                                    _ptr(block_table_out, torch.int32, "block_table_out"), _stream()))
+
+
 def cache_store(dims: Dims, cache: LatentCache, n_rows, max_rows: int, src, src_stride: int):
     cc = cache.c()
     _check(lib().mla_cache_store(ctypes.byref(dims), ctypes.byref(cc), n_rows.shape[0],
@@ -236,3 +245,26 @@ class DecodeStep:
         combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
         absorb_out(self.dims, self.o_lat, W["W_uv"], W["W_o"], self.ws_o, self.u)
         return self.u
+
+
+class PrefillStep:
+    """Chunked prefill: C new tokens per sequence (positions p0[b] .. p0[b] + C - 1) as B * C causal
+    pseudo-sequences sharing their sequence's pages (mla_prefill_tables), run through the five
+    decode calls. Every chunk token's row is appended, and each token gets its causal output u."""
+
+    def __init__(self, dims, B: int, C: int, max_pages: int, num_splits: int = 0, device="cuda",
+                 sm_scale: float = 0.0):
+        self.B, self.C = B, C
+        self.step = DecodeStep(dims, B * C, num_splits, device, sm_scale)
+        self.dims = self.step.dims
+        self.seq_lens = torch.empty(B * C, dtype=torch.int32, device=device)
+        self.block_table = torch.empty((B * C, max_pages), dtype=torch.int32, device=device)
+
+    def run(self, h_chunk, W, cache: LatentCache, p0):
+        """h_chunk [B, C, d] (weight dtype); cache: paged, holding p0[b] rows of sequence b."""
+        if cache.page_size <= 0:
+            raise MLAError("chunked prefill needs a paged cache")
+        prefill_tables(cache, self.B, self.C, p0, self.seq_lens, self.block_table)
+        view = LatentCache(cache.rows, cache.dtype, cache.t_cap, cache.scales, self.block_table, cache.page_size)
+        u = self.step.run(h_chunk.reshape(self.B * self.C, -1).contiguous(), W, view, self.seq_lens)
+        return u.view(self.B, self.C, -1)

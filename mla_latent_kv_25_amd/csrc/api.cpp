@@ -230,6 +230,23 @@ mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const
   return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
 }
 
+mla_status mla_prefill_tables(const mla_cache* cache, int32_t B, int32_t C, const int32_t* p0,
+                              int32_t* seq_lens_out, int32_t* block_table_out, hipStream_t stream) {
+  const char* fn = "mla_prefill_tables";
+  if (!cache) return fail(MLA_E_ARG, "%s: cache is NULL", fn);
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (C < 1) return fail(MLA_E_ARG, "%s: chunk length C must be >= 1", fn);
+  if ((int64_t)B * C > (int64_t)INT32_MAX / 2) return fail(MLA_E_ARG, "%s: B * C too large", fn);
+  if (cache->page_size <= 0 || !cache->block_table || cache->max_pages <= 0)
+    return fail(MLA_E_ARG, "%s: the cache must be paged (page_size > 0, block table, max_pages > 0)", fn);
+  if (B == 0) return ok();
+  if (!p0 || !seq_lens_out || !block_table_out) return fail(MLA_E_ARG, "%s: NULL pointer", fn);
+  if (misaligned4(p0, seq_lens_out, block_table_out, cache->block_table))
+    return fail(MLA_E_ARG, "%s: pointers must be 4-byte aligned", fn);
+  return hip_status(mla::launch_prefill_tables(B, C, cache->max_pages, p0, cache->block_table, seq_lens_out,
+                                               block_table_out, stream), fn);
+}
+
 mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t B, const int32_t* n_rows,
                            int32_t max_rows, const float* src, int64_t src_stride, hipStream_t stream) {
   const char* fn = "mla_cache_store";

@@ -126,6 +126,27 @@ __global__ __launch_bounds__(256) void k_cache_store(int rw, CacheArgs cache,
   }
 }
 
+// Chunked prefill as causal pseudo-sequences: pseudo-sequence b * C + t is token t of sequence
+// b's chunk; it attends to rows 0 .. p0[b] + t and shares sequence b's pages (block-table row
+// copied). One block per pseudo-sequence.
+__global__ __launch_bounds__(256) void k_prefill_tables(int C, int max_pages, const int32_t* __restrict__ p0,
+                                                         const int32_t* __restrict__ bt_in,
+                                                         int32_t* __restrict__ seq_lens_out,
+                                                         int32_t* __restrict__ bt_out) {
+  const int ps = blockIdx.x;
+  const int b = ps / C, t = ps - b * C;
+  if (threadIdx.x == 0) seq_lens_out[ps] = p0[b] + t + 1;
+  for (int j = threadIdx.x; j < max_pages; j += blockDim.x)
+    bt_out[(int64_t)ps * max_pages + j] = bt_in[(int64_t)b * max_pages + j];
+}
+
+hipError_t launch_prefill_tables(int B, int C, int max_pages, const int32_t* p0, const int32_t* bt_in,
+                                 int32_t* seq_lens_out, int32_t* bt_out, hipStream_t st) {
+  hipLaunchKernelGGL(k_prefill_tables, dim3((unsigned)(B * C)), dim3(256), 0, st, C, max_pages, p0, bt_in,
+                     seq_lens_out, bt_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float* q_pe, float* kv_new,
                        const CacheArgs* cache, hipStream_t st) {
   CacheArgs c = cache ? *cache : CacheArgs{};

@@ -39,6 +39,8 @@ AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B);
 
 hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float* q_pe, float* kv_new,
                        const CacheArgs* cache, hipStream_t st);
+hipError_t launch_prefill_tables(int B, int C, int max_pages, const int32_t* p0, const int32_t* bt_in,
+                                 int32_t* seq_lens_out, int32_t* bt_out, hipStream_t st);
 hipError_t launch_cache_store(const mla_dims& d, const CacheArgs& c, int B, const int32_t* n_rows,
                               int max_rows, const float* src, int64_t src_stride, hipStream_t st);
 

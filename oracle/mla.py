@@ -201,3 +201,19 @@ def decode_batch(W, h, prefixes, dims: OracleDims, cdtype, heads=None, want_u=Tr
     """decode_step_explicit over a batch; prefixes[b] are sequence b's stored rows."""
     return [decode_step_explicit(W, h[b], prefixes[b], dims, cdtype, heads=heads, want_u=want_u)
             for b in range(len(prefixes))]
+
+
+def prefill_chunk(W, H, prefix, dims: OracleDims, cdtype, want_u=True):
+    """Chunked prefill of one sequence: C new tokens H [C, d] after the stored rows `prefix`
+    [p0, d_c + d_r]. By the definition of causal attention ([Scratch] section 6: token t attends to
+    positions 0..t), token t of the chunk sits at position p0 + t and attends to the prefix and to
+    the chunk's tokens 0..t; each token's own row is stored (rounded to the cache type) before the
+    tokens after it read it. Written out as the decode steps of the chunk's tokens in order.
+    Returns the list of per-token results of decode_step_explicit."""
+    rows = np.asarray(prefix, dtype=np.float64).reshape(-1, dims.d_c + dims.d_r)
+    outs = []
+    for t in range(len(H)):
+        r = decode_step_explicit(W, np.asarray(H[t], dtype=np.float64), rows, dims, cdtype, want_u=want_u)
+        outs.append(r)
+        rows = np.vstack([rows, r["read_new"][None, :]])
+    return outs

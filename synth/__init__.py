@@ -5,4 +5,4 @@ This package only draws random numbers, casts them to storage types and lays the
 no projection, no rotary embedding, no quantisation and no attention.
 """
 from .configs import CONFIGS, Dims, RUNNING_DIMS, V2_DIMS, get_config  # noqa: F401
-from .gen import Case, make_case  # noqa: F401
+from .gen import Case, make_case, make_prefill_case  # noqa: F401

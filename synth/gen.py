@@ -49,6 +49,10 @@ class Case:
     rows32: Optional[torch.Tensor] = None
     block_table: Optional[torch.Tensor] = None   # [B, max_pages] int32, -1 = unused
     num_pages: int = 0
+    # chunked prefill (make_prefill_case): C new tokens per sequence after p0[b] stored rows
+    h_chunk: Optional[torch.Tensor] = None       # [B, C, d] storage dtype
+    p0: Optional[torch.Tensor] = None            # [B] int32
+    chunk: int = 0
 
     @property
     def B(self) -> int:
@@ -151,4 +155,20 @@ def make_case(cfg: Config, device="cpu", B: Optional[int] = None, T=None, seed: 
         case.rows32 = buf
     else:
         case.rows = buf
+    return case
+
+
+def make_prefill_case(cfg: Config, p0, C: int, device="cpu", seed: Optional[int] = None):
+    """A chunked-prefill case: sequence b holds p0[b] stored rows (the config's prefix-row draw,
+    paged layout) and receives C new tokens whose hidden states h_chunk [B, C, d] are drawn like
+    the decode step's h. Pages cover p0[b] + C rows."""
+    cfg = cfg.with_(layout="paged")
+    B = len(p0)
+    case = make_case(cfg, device=device, B=B, T=[int(p) + C for p in p0], seed=seed)
+    g = torch.Generator(device="cpu")
+    g.manual_seed((cfg.seed if seed is None else seed) * 104729 + 3)
+    wdt = TORCH_DTYPE[cfg.wdtype]
+    case.h_chunk = (torch.randn((B, C, cfg.dims.d), generator=g, dtype=torch.float32) * cfg.sigma_h).to(wdt).to(device)
+    case.p0 = torch.tensor([int(p) for p in p0], dtype=torch.int32, device=device)
+    case.chunk = C
     return case

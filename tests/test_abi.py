@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -129,6 +129,17 @@ def test_absorb_out_and_store_validation(L):
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 65, FAKE, 65, None) == 1  # > t_cap
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 10, FAKE, 5, None) == 1   # stride
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 0, None, 0, None, 0, None) == 0
+
+
+def test_prefill_tables_validation(L):
+    paged = _cache(page_size=64, t_cap=128, block_table=0x3000, max_pages=2, num_pages=4)
+    assert L.mla_prefill_tables(None, 2, 4, FAKE, FAKE, FAKE, None) == 1
+    assert L.mla_prefill_tables(ctypes.byref(_cache()), 2, 4, FAKE, FAKE, FAKE, None) == 1   # contiguous
+    assert b"paged" in L.mla_last_error()
+    assert L.mla_prefill_tables(ctypes.byref(paged), 2, 0, FAKE, FAKE, FAKE, None) == 1     # C >= 1
+    assert L.mla_prefill_tables(ctypes.byref(paged), 2, 4, None, FAKE, FAKE, None) == 1
+    assert L.mla_prefill_tables(ctypes.byref(paged), 2, 4, ctypes.c_void_p(0x1002), FAKE, FAKE, None) == 1
+    assert L.mla_prefill_tables(ctypes.byref(paged), 0, 4, None, None, None, None) == 0     # empty batch
 
 
 def test_alignment_validation(L):

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import (OracleDims, cache_counts, decode_step_absorbed, decode_step_explicit, head_slices,
-                    load_rows, rope, softmax, store_rows)
+                    load_rows, prefill_chunk, rope, softmax, store_rows)
 from synth import RUNNING_DIMS, V2_DIMS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -311,6 +311,40 @@ def test_stepwise_decode_equals_causal_attention():
         scale=1.0 / math.sqrt(d_h + d_r)).numpy()
     U = o.transpose(1, 0, 2).reshape(N, -1) @ W["W_o"].T
     np.testing.assert_allclose(np.array(us), U, rtol=1e-10, atol=1e-12)
+
+
+def test_prefill_chunk_equals_masked_attention():
+    """A chunk of C tokens after p0 stored rows equals attention computed at once over [prefix ;
+    chunk rows] with an offset causal mask (query t sees keys 0 .. p0 + t): torch SDPA with an
+    explicit boolean mask on explicitly built K/V."""
+    rng = np.random.default_rng(8)
+    dims = SMALL
+    W = _rand_weights(dims, rng, sw=0.6, kappa=2.0)
+    p0, C = 9, 6
+    prefix = rng.standard_normal((p0, dims.d_c + dims.d_r))
+    H = rng.standard_normal((C, dims.d))
+    outs = prefill_chunk(W, H, prefix, dims, "f32")
+    n_h, d_h, d_r = dims.n_h, dims.d_h, dims.d_r
+    pos = np.arange(p0, p0 + C)
+    cQ = H @ W["W_dq"].T
+    qC = (cQ @ W["W_uq"].T).reshape(C, n_h, d_h)
+    qR = np.stack([_rope_complex((cQ[t] @ W["W_qr"].T).reshape(n_h, d_r), pos[t], 10000.0) for t in range(C)])
+    Cn = (H @ W["W_dkv"].T).astype(np.float32).astype(np.float64)
+    KRn = np.stack([_rope_complex(W["W_kr"] @ H[t], pos[t], 10000.0) for t in range(C)]).astype(np.float32).astype(np.float64)
+    Call = np.vstack([prefix[:, : dims.d_c], Cn])
+    KRall = np.vstack([prefix[:, dims.d_c:], KRn])
+    N = p0 + C
+    kC = (Call @ W["W_uk"].T).reshape(N, n_h, d_h)
+    vC = (Call @ W["W_uv"].T).reshape(N, n_h, d_h)
+    q = np.concatenate([qC, qR], 2).transpose(1, 0, 2)                       # [n_h, C, d_h + d_r]
+    k = np.concatenate([kC, np.repeat(KRall[:, None, :], n_h, 1)], 2).transpose(1, 0, 2)
+    v = vC.transpose(1, 0, 2)
+    mask = torch.from_numpy(np.arange(N)[None, :] <= pos[:, None])          # [C, N]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask,
+        scale=1.0 / math.sqrt(d_h + d_r)).numpy()
+    U = o.transpose(1, 0, 2).reshape(C, -1) @ W["W_o"].T
+    np.testing.assert_allclose(np.array([r["u"] for r in outs]), U, rtol=1e-10, atol=1e-12)
 
 
 def test_appended_row_is_rounded_like_storage():
