@@ -70,3 +70,23 @@ def test_prefill_rows_match_decode_steps():
         torch.cuda.synchronize()
         assert rel_l2(u_pf[:, t].double().cpu().numpy(), u_t.double().cpu().numpy()) < 1e-5
     assert torch.equal(c1.rows, c2.rows)
+
+
+def test_prefill_benchmark_shape_sampled():
+    """The bench's prefill workload (B=16 x 2048 stored rows, C=64, bf16 paged, one range per CU):
+    sampled chunk tokens of two sequences against the oracle."""
+    key, P0, C, B = "3", 2048, 64, 16
+    case = make_prefill_case(get_config(key), [P0] * B, C, device="cuda")
+    cache = build_cache(case)
+    pf = mla.PrefillStep(case.dims, B, C, int(case.block_table.shape[1]), 0)
+    u = pf.run(case.h_chunk, case.weights, cache, case.p0)
+    torch.cuda.synchronize()
+    W = weights64(case)
+    od = OracleDims.of(case.dims)
+    for b in (0, B - 1):
+        prefix = oracle_prefix(case, b)[:P0]
+        H = case.h_chunk[b].double().cpu().numpy()
+        # tokens 0 and 1 of the chunk (token 1 reads token 0's appended row)
+        outs = prefill_chunk(W, H[:2], prefix, od, case.cfg.cdtype)
+        for t in range(2):
+            check_u(u[b, t].double().cpu().numpy(), outs[t]["u"], case.cfg.cdtype, f"prefill bench b={b} t={t}")
