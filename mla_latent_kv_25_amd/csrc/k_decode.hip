@@ -69,8 +69,10 @@ struct RangeStart {
 };
 __device__ __forceinline__ RangeStart locate_range(const int32_t* __restrict__ seq_lens, int B, int G, int p,
                                                    int lane) {
-  int64_t acc = 0;
-  for (int i = lane; i < B; i += 64) acc += seq_lens[i];
+  // the first 64 lengths are loaded once and serve both the total and the scan below
+  const int64_t v_first = lane < B ? (int64_t)seq_lens[lane] : 0;
+  int64_t acc = v_first;
+  for (int i = lane + 64; i < B; i += 64) acc += seq_lens[i];
   const int64_t total = wave_sum_i64(acc);
   RangeStart r;
   r.start = range_start(p, total, G);
@@ -80,7 +82,7 @@ __device__ __forceinline__ RangeStart locate_range(const int32_t* __restrict__ s
   int64_t base = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
     const int i = c0 + lane;
-    const int64_t v = i < B ? (int64_t)seq_lens[i] : 0;
+    const int64_t v = c0 == 0 ? v_first : (i < B ? (int64_t)seq_lens[i] : 0);
     const int64_t inc = wave_incl_scan_i64(v, lane);
     const uint64_t hit = __ballot(base + inc > r.start);
     if (hit) {
@@ -663,6 +665,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
 namespace v3 {
 constexpr int NBUF = 4;
 }
+#ifndef V3_EARLY_TILES
+#define V3_EARLY_TILES 1  // tiles whose copies are issued before the query loads
+#endif
 
 // Scores of one tile (as tile_scores) with between(ks) run after MFMA ks; the calls sit between
 // the volatile MFMA statements in program order (used to issue tile copies under the math).
@@ -710,6 +715,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
   int* const redo_flag = (int*)lds;
   float* const lds_l = (float*)(lds + 16);
   float (*const lds_m)[NH] = (float (*)[NH])(lds + 16 + NH * 4);
+  // staging of the float16 partial rows (per wave NH rows of 256 bytes + 16 bytes of padding,
+  // which spreads the row-wise writes over all banks), also on the idle tile ring
+  constexpr int OTR = 272;
+  static_assert(4096 + 4 * NH * OTR <= NBUF * TILEB, "partial staging exceeds the tile ring");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int p = range_for_block(blockIdx.x, G);
@@ -721,6 +730,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
   int b = rp.b;
   int64_t s0 = rp.s0, s1 = rp.s1;
   const int head = 32 * w + l32;
+  uint8_t* const otr = lds + 4096 + w * (NH * OTR);
 
   uint32_t kq[4];
   {
@@ -797,11 +807,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
       }
       return cp;
     };
-    auto copy = [&](const CopyPlan& cp, int i) __attribute__((always_inline)) {
+    // `partial`: the tile may end before its 32nd row (only a segment's last tile does); callers
+    // pass a constant so that full tiles carry no branch
+    auto copy = [&](const CopyPlan& cp, int i, bool partial) __attribute__((always_inline)) {
       uint32_t d2 = doff2[i >> 1];
       asm volatile("" : "+v"(d2));
       uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
-      if (cp.last < TT - 1) {  // only the last tile of a segment is partial
+      if (partial && cp.last < TT - 1) {
         const int t = (int)(off / ROWB);
         if (t > cp.last) off -= (uint32_t)(t - cp.last) * ROWB;
       }
@@ -811,13 +823,18 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
     auto issue_all = [&](int it) {
       const CopyPlan cp = plan_tile(it);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) copy(cp, i);
+      for (int i = 0; i < LOADS; ++i) copy(cp, i, true);
     };
     auto prime = [&]() {
 #pragma unroll 1
       for (int it = 0; it < 3 && it < ntiles; ++it) issue_all(it);
     };
-    prime();
+    // The first tiles go out ahead of the query loads (the query waits then also cover them);
+    // the rest of the prime follows once the query is in registers, so that it does not queue
+    // in front of the query.
+    constexpr int EARLY = V3_EARLY_TILES;
+#pragma unroll 1
+    for (int it = 0; it < EARLY && it < ntiles; ++it) issue_all(it);
 
     // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
     bf16x8 qf[KSTEPS];
@@ -836,7 +853,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
         v[6] = (__bf16)(c[2] * qscale); v[7] = (__bf16)(c[3] * qscale);
         qf[ks] = v;
       }
+      // every fragment converted before the remaining copies are issued (keeps the waits for the
+      // query loads in front of those copies)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
     }
+#pragma unroll 1
+    for (int it = EARLY; it < 3 && it < ntiles; ++it) issue_all(it);
     auto valid_of = [&](int it) -> int {
       const int64_t r = n - (int64_t)it * TT;
       return r < TT ? (int)r : TT;
@@ -980,9 +1003,15 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
           const uint8_t* tn = tile_buf(it + 1);
           if (it + 3 < ntiles) {
             const CopyPlan cp = plan_tile(it + 3);
-            S = tile_scores_copy(tn, kq, qf, [&](int ks) __attribute__((always_inline)) {
-              if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4);
-            });
+            if (cp.last < TT - 1) {
+              S = tile_scores_copy(tn, kq, qf, [&](int ks) __attribute__((always_inline)) {
+                if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4, true);
+              });
+            } else {
+              S = tile_scores_copy(tn, kq, qf, [&](int ks) __attribute__((always_inline)) {
+                if (ks % 4 == 1 && ks / 4 < LOADS) copy(cp, ks / 4, false);
+              });
+            }
           } else {
             S = tile_scores(tn, kq, qf);
           }
@@ -1030,7 +1059,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
       int e = 0;
       if (mx2 > 0.f) (void)frexpf(mx2, &e);
       const float f = ldexpf(inv_l, -e);
-      uint16_t* dst = o_part + (slot * NH + hr) * DC + 128 * w;
+      // this wave's 128 columns of head hr, staged in LDS as one 256-byte row (stride OTR)
+      uint8_t* dst = otr + hr * OTR;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -1038,12 +1068,24 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
           const f32x16& o = O[4 * cb + hb];
           const u32x2 v = {pack_f16x2(o[4 * r4 + 0] * f, o[4 * r4 + 1] * f),
                            pack_f16x2(o[4 * r4 + 2] * f, o[4 * r4 + 3] * f)};
-          *(u32x2*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
+          *(u32x2*)(dst + 64 * cb + 16 * r4 + 8 * g) = v;
         }
       if (w == 0 && g == 0) sc_part[slot * NH + hr] = ldexpf(1.f, e);
     }
+    // rows back out of LDS as whole 256-byte runs: 16 lanes per row, 4 rows per store (this
+    // wave's own staging area, so no barrier; LDS operations of one wave complete in order)
+    {
+      uint16_t* dst = o_part + slot * NH * DC + 128 * w;
+      const int rsub = lane >> 4, ch = lane & 15;
+#pragma unroll 8
+      for (int j = 0; j < NH / 4; ++j) {
+        const int r = 4 * j + rsub;
+        const u32x4 v = *(const u32x4*)(otr + r * OTR + 16 * ch);
+        *(u32x4*)(dst + (int64_t)r * DC + 8 * ch) = v;
+      }
+    }
     if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
-    __syncthreads();  // lds_l / lds_m are reused by the next segment
+    __syncthreads();  // lds_l / lds_m and the staging rows are reused by the next segment
 
     start = seg_end;
     if (start < end) {

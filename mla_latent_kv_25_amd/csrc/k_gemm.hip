@@ -21,7 +21,7 @@ namespace mla {
 static size_t al256h(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace gm {
-constexpr int MAXB = 128;      // batch rows per MFMA launch
+constexpr int MAXB = 128;      // columns per tile (batch rows) of the widest MFMA tile
 constexpr int MT = 128;        // output rows per workgroup (4 waves x 32)
 constexpr int KC = 64;         // k per pipeline stage
 constexpr int TARGET_WG = 256; // workgroups aimed for when choosing the K split
@@ -37,33 +37,37 @@ static int split_for(int mtiles, int S, int Z) {
 }
 static int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// column tiles of an N-column product (128 columns each)
+static int col_tiles(int N) { return cdiv(N, gm::MAXB); }
 struct QSplits { int sk1; };
-static QSplits q_splits(const mla_dims& d) { return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT), d.d / gm::KC, 1)}; }
+static QSplits q_splits(const mla_dims& d, int B) {
+  return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT) * col_tiles(B), d.d / gm::KC, 1)};
+}
 struct OSplits { int sk4, sk5; };
-// W^O runs on 256-row tiles when the batch chunk is at most 64 rows
-static bool o_wide(int nb) { return nb <= 64; }
-static OSplits o_splits(const mla_dims& d, int nb) {
+// W^O runs on 256-row tiles when the batch is at most 64 rows
+static bool o_wide(int B) { return B <= 64; }
+static OSplits o_splits(const mla_dims& d, int B) {
   // W^UV: one workgroup per (head, 64 rows); a K split would add a reduction pass
-  return {1, split_for(cdiv(d.d, o_wide(nb) ? 2 * gm::MT : gm::MT), d.n_h * d.d_h / gm::KC, 1)};
+  return {1, split_for(cdiv(d.d, o_wide(B) ? 2 * gm::MT : gm::MT) * col_tiles(B), d.n_h * d.d_h / gm::KC, 1)};
 }
 
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
   AbsorbQLayout L;
-  const int nb = B < gm::MAXB ? B : gm::MAXB;
+  const int sk1 = q_splits(d, B).sk1;
   L.off_cq = 0;
   L.off_qc = al256h((size_t)B * d.d_cq * 4);
   L.off_part = L.off_qc + al256h((size_t)B * d.n_h * d.d_h * 4);
-  L.part_floats = (size_t)q_splits(d).sk1 * nb * (d.d_cq + d.d_c + d.d_r);
+  L.part_floats = sk1 > 1 ? (size_t)sk1 * B * (d.d_cq + d.d_c + d.d_r) : 0;
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
 }
 AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B) {
   AbsorbOutLayout L;
-  const int nb = B < gm::MAXB ? B : gm::MAXB;
-  const OSplits sp = o_splits(d, nb);
+  const OSplits sp = o_splits(d, B);
   L.off_o = 0;
   L.off_part = al256h((size_t)B * d.n_h * d.d_h * 4);
-  const size_t p4 = (size_t)sp.sk4 * d.n_h * nb * d.d_h, p5 = (size_t)sp.sk5 * nb * d.d;
+  const size_t p4 = sp.sk4 > 1 ? (size_t)sp.sk4 * d.n_h * B * d.d_h : 0;
+  const size_t p5 = sp.sk5 > 1 ? (size_t)sp.sk5 * B * d.d : 0;
   L.part_floats = p4 > p5 ? p4 : p5;
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
@@ -101,7 +105,8 @@ __device__ __forceinline__ void wait_copies_barrier() {
 
 // ================================================================================================
 // Weight-streaming MFMA GEMM: Y[n][m] = sum_k W(m, k) X[n][k], W bf16 row-major (lda = K).
-// Workgroup = 32*MB output rows x all N <= 32*NB columns, over one K slice, one wave per SIMD. The
+// Workgroup = 32*MB output rows x 32*NB columns (a column tile; N beyond it takes more tiles),
+// over one K slice, one wave per SIMD. The
 // slice streams through an NS-deep ring of LDS stages (64 k each: the W tile and the matching X
 // columns) filled by direct global->LDS copies, up to NS-1 stages ahead of the MFMAs. LDS rows
 // are XOR-swizzled in 16-byte chunks so the MFMA fragment reads are conflict-free.
@@ -146,7 +151,7 @@ __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf1
 }
 
 template <int NB, bool XF32, int MB>
-__global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const void* __restrict__ Xv,
+__global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part,
                                                   int Mtot, int64_t zW, int64_t zX, int64_t zY) {
   using C = WCfg<NB, XF32, MB>;
@@ -155,7 +160,20 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * C::SB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int mt = blockIdx.x, ky = blockIdx.y, z = blockIdx.z, Z = gridDim.z;
+  // One column tile: blockIdx.x is the row tile. Several: workgroups are dealt round-robin to
+  // the 8 XCDs, so blockIdx.x is mapped to tile t = (x % 8) * (gridDim.x / 8) + x / 8 (gridDim.x
+  // is a multiple of 8) and t = row tile * ntiles + column tile; each XCD then runs consecutive
+  // column tiles of the same row tile, which read that W slice from its L2 rather than HBM.
+  int mt = blockIdx.x, nt = 0;
+  if (ntiles > 1) {
+    const int t = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    if (t >= ((Mtot + MT - 1) / MT) * ntiles) return;   // padding workgroup (uniform)
+    mt = t / ntiles;
+    nt = t - mt * ntiles;
+  }
+  const int ky = blockIdx.y, z = blockIdx.z, Z = gridDim.z;
+  const int n0 = nt * 32 * NB;                         // first column of this tile
+  const int NL = (N - n0) < 32 * NB ? (N - n0) : 32 * NB;
   const int m_base = mt * MT;
   const int s = seg_of(seg, m_base);
   const int r0 = m_base - seg.m0[s];                  // first tile row inside its segment
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
   const int ns = st1 - st0;
   constexpr int ESX = XF32 ? 4 : 2;
   const uint8_t* Wb = (const uint8_t*)seg.W[s] + ((int64_t)z * zW + (int64_t)r0 * K) * 2;
-  const uint8_t* Xb = (const uint8_t*)Xv + (int64_t)z * zX * ESX;
+  const uint8_t* Xb = (const uint8_t*)Xv + ((int64_t)z * zX + (int64_t)n0 * ldx) * ESX;
 
   // Copy plan: thread tid fills 16-byte LDS slots p = 256 i + tid. W slot p: row p / 8, physical
   // chunk p % 8, which holds logical chunk (p % 8) ^ ((row / 2) % 8). X slot (bf16): same with
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
       int row, c;
       if constexpr (XF32) { row = p >> 4; c = (p & 15) ^ (row & 15); }
       else { row = p >> 3; c = (p & 7) ^ ((row >> 1) & 7); }
-      if (row > N - 1) row = N - 1;
+      if (row > NL - 1) row = NL - 1;
       ofs[C::DW + i] = (uint32_t)((int64_t)row * ldx * ESX) + (uint32_t)(c << 4);
     }
   }
@@ -316,11 +334,11 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int K, const v
         const f32x4 x = reg[((ww * NB + jb) * 4 + r4) * 64 + ln];
         v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
       }
-      if (n >= N || r0 + mloc >= seg_rows) continue;
+      if (n >= NL || r0 + mloc >= seg_rows) continue;
       if (split_k > 1) {
-        *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m_base + mloc) = v;
+        *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n0 + n) * Mtot + m_base + mloc) = v;
       } else {
-        *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)n * seg.ldy[s] + r0 + mloc) = v;
+        *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)(n0 + n) * seg.ldy[s] + r0 + mloc) = v;
       }
     }
   }
@@ -536,12 +554,17 @@ static bool mfma_dims_ok(const mla_dims& d) {
 template <int NB, bool XF32, int MB>
 static void wgemm_nb(hipStream_t st, dim3 grid, const Seg& sg, int N, int K, const void* X, int64_t ldx,
                      int split_k, float* part, int Mtot, int64_t zW, int64_t zX, int64_t zY) {
-  hipLaunchKernelGGL((k_wgemm<NB, XF32, MB>), grid, dim3(256), 0, st, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  const int ntiles = cdiv(N, 32 * NB);
+  const int tiles = cdiv(Mtot, 32 * MB) * ntiles;
+  if (ntiles > 1) grid.x = (unsigned)((tiles + 7) & ~7);
+  hipLaunchKernelGGL((k_wgemm<NB, XF32, MB>), grid, dim3(256), 0, st, sg, N, ntiles, K, X, ldx, split_k, part, Mtot,
+                     zW, zX, zY);
 }
 
-// Y = W X over stacked segments (segment boundaries on multiples of the row tile), N <= gm::MAXB.
-// Row tiles of 32*mb rows: mb = 8 halves the X traffic per W byte (N <= 64 only), mb = 2 doubles
-// the workgroup count of short problems; otherwise 128 rows.
+// Y = W X over stacked segments (segment boundaries on multiples of the row tile). Row tiles of
+// 32*mb rows: mb = 8 halves the X traffic per W byte (N <= 64 only), mb = 2 doubles the workgroup
+// count of short problems; otherwise 128 rows. N above 128 runs as 128-column tiles in the same
+// launch.
 static int tile_mb(int mb, int N) { return (mb == 8 && N > 64) ? 4 : mb; }
 template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
@@ -578,23 +601,23 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
   const int rw = d.d_c + d.d_r;
   const int nhdh = d.n_h * d.d_h;
   if (wdt == MLA_BF16 && mfma_dims_ok(d)) {
+    // stage 1: [c^Q | c^KV | k^R raw] = [W^DQ; W^DKV; W^KR] h
+    Seg s1{};
+    s1.W[0] = W_dq; s1.W[1] = W_dkv; s1.W[2] = W_kr;
+    s1.Y[0] = cq; s1.ldy[0] = d.d_cq;
+    s1.Y[1] = kv_new; s1.ldy[1] = rw;
+    s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
+    s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
+    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+    // stage 2: [q^C | q^R raw] = [W^UQ; W^QR] c^Q
+    Seg s2{};
+    s2.W[0] = W_uq; s2.W[1] = W_qr;
+    s2.Y[0] = qc; s2.ldy[0] = nhdh;
+    s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
+    s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
+    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
     for (int b0 = 0; b0 < B; b0 += gm::MAXB) {
       const int nb = B - b0 < gm::MAXB ? B - b0 : gm::MAXB;
-      // stage 1: [c^Q | c^KV | k^R raw] = [W^DQ; W^DKV; W^KR] h
-      Seg s1{};
-      s1.W[0] = W_dq; s1.W[1] = W_dkv; s1.W[2] = W_kr;
-      s1.Y[0] = cq + (int64_t)b0 * d.d_cq; s1.ldy[0] = d.d_cq;
-      s1.Y[1] = kv_new + (int64_t)b0 * rw; s1.ldy[1] = rw;
-      s1.Y[2] = kv_new + (int64_t)b0 * rw + d.d_c; s1.ldy[2] = rw;
-      s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
-      mfma_gemm<false>(st, s1, nb, d.d, (const uint16_t*)h + (int64_t)b0 * d.d, d.d, q_splits(d).sk1, part, 1, 0, 0, 0);
-      // stage 2: [q^C | q^R raw] = [W^UQ; W^QR] c^Q
-      Seg s2{};
-      s2.W[0] = W_uq; s2.W[1] = W_qr;
-      s2.Y[0] = qc + (int64_t)b0 * nhdh; s2.ldy[0] = nhdh;
-      s2.Y[1] = q_pe + (int64_t)b0 * d.n_h * d.d_r; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
-      s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
-      mfma_gemm<true>(st, s2, nb, d.d_cq, cq + (int64_t)b0 * d.d_cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
       // stage 3: q_lat_i = (W^UK_i)^T q^C_i
       dim3 g3(d.d_c / absq::TC, d.n_h);
       const float* qcb = qc + (int64_t)b0 * nhdh;
@@ -626,21 +649,18 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
   float* part = (float*)((char*)ws + L.off_part);
   const int nhdh = d.n_h * d.d_h;
   if (wdt == MLA_BF16 && mfma_dims_ok(d)) {
-    for (int b0 = 0; b0 < B; b0 += gm::MAXB) {
-      const int nb = B - b0 < gm::MAXB ? B - b0 : gm::MAXB;
-      // o_i = W^UV_i o_lat_i, batched over heads (z): rows of W^UV_i are outputs
-      Seg s4{};
-      s4.W[0] = W_uv; s4.Y[0] = o + (int64_t)b0 * nhdh; s4.ldy[0] = nhdh;
-      s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
-      const OSplits sp = o_splits(d, nb);
-      mfma_gemm<true>(st, s4, nb, d.d_c, o_lat + (int64_t)b0 * d.n_h * d.d_c, (int64_t)d.n_h * d.d_c, sp.sk4, part,
-                      d.n_h, (int64_t)d.d_h * d.d_c, d.d_c, d.d_h, 2);
-      // u = W^O [o_1; ...; o_nh]
-      Seg s5{};
-      s5.W[0] = W_o; s5.Y[0] = u + (int64_t)b0 * d.d; s5.ldy[0] = d.d;
-      s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-      mfma_gemm<true>(st, s5, nb, nhdh, o + (int64_t)b0 * nhdh, nhdh, sp.sk5, part, 1, 0, 0, 0, o_wide(nb) ? 8 : 4);
-    }
+    // o_i = W^UV_i o_lat_i, batched over heads (z): rows of W^UV_i are outputs
+    Seg s4{};
+    s4.W[0] = W_uv; s4.Y[0] = o; s4.ldy[0] = nhdh;
+    s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
+    const OSplits sp = o_splits(d, B);
+    mfma_gemm<true>(st, s4, B, d.d_c, o_lat, (int64_t)d.n_h * d.d_c, sp.sk4, part, d.n_h, (int64_t)d.d_h * d.d_c,
+                    d.d_c, d.d_h, 2);
+    // u = W^O [o_1; ...; o_nh]
+    Seg s5{};
+    s5.W[0] = W_o; s5.Y[0] = u; s5.ldy[0] = d.d;
+    s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
+    mfma_gemm<true>(st, s5, B, nhdh, o, nhdh, sp.sk5, part, 1, 0, 0, 0, o_wide(B) ? 8 : 4);
     return hipGetLastError();
   }
   valu_any(wdt, false, false, st, d.d_h, B, d.d_c, W_uv, d.d_c, (int64_t)d.d_h * d.d_c, o_lat,

@@ -102,10 +102,11 @@ def test_stage_outputs():
             assert e < (1e-5 if key == "0" else 2e-4)
 
 
-@pytest.mark.parametrize("B", [33, 100, 130])
+@pytest.mark.parametrize("B", [33, 100, 130, 300])
 def test_stage_outputs_wide_batch(B):
     """Projection stages at batch widths that use every column-block count of the MFMA GEMMs
-    (33: two blocks with a ragged one, 100: four, 130: two launches of 128 + 2 rows)."""
+    (33: two blocks with a ragged one, 100: four, 130: two 128-column tiles in one launch, the
+    second holding 2 rows; 300: three tiles, a ragged 44-row one, with K split over the tiles)."""
     case = _case("2", B, [5] * B)
     d = mla.Dims.of(case.dims)
     step = mla.DecodeStep(case.dims, B, 0)
