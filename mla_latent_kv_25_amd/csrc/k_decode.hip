@@ -1353,6 +1353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int64_t total = cu[B];
   const int64_t s0 = cu[b], s1 = cu[b + 1];
   const int c0 = blockIdx.z * dcc;
+  const bool f16 = *fmt == 2;
   float* dst = o_lat + ((int64_t)b * n_h + h0) * d_c + c0;
   if (s1 <= s0) {  // empty sequence (outside the contract): defined output
     for (int e = tid; e < nh * dcc; e += 256) dst[(e / dcc) * d_c + e % dcc] = 0.f;
@@ -1374,28 +1375,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
   __syncthreads();
   const int np = sh_np;
-  const bool f16 = *fmt == 2;
-  // every (piece, head) lse and scale, loaded by the whole block in one pass
-  for (int e = tid; e < np * nh; e += 256) {
-    const int i = e / nh, hh = e - i * nh;
-    const int64_t r = (int64_t)slots[i] * n_h + h0 + hh;
-    lse_s[i * ch + hh] = lse_part[r];
-    sc_s[i * ch + hh] = f16 ? sc_part[r] : 1.f;
+  // Fast path for float16 partials and a block of 4096 outputs (two 8-element groups per
+  // thread): the rows of the first PF pieces are requested before the weights are built, so that
+  // their latency overlaps the lse loads.
+  constexpr int PF = 4;
+  const bool fast = f16 && nh * dcc == 4096;
+  const _Float16* srcp = (const _Float16*)o_part + (int64_t)h0 * d_c + c0;
+  const int64_t pst = (int64_t)n_h * d_c;
+  // every (piece, head) lse and scale, loaded by the whole block in one pass; then the weights
+  auto build_weights = [&]() __attribute__((always_inline)) {
+    for (int e = tid; e < np * nh; e += 256) {
+      const int i = e / nh, hh = e - i * nh;
+      const int64_t r = (int64_t)slots[i] * n_h + h0 + hh;
+      lse_s[i * ch + hh] = lse_part[r];
+      sc_s[i * ch + hh] = f16 ? sc_part[r] : 1.f;
+    }
+    __syncthreads();
+    // weights: wave w handles heads w, w+4, ...
+    for (int hh = w; hh < nh; hh += 4) {
+      float M = -__builtin_inff();
+      for (int i = lane; i < np; i += 64) M = fmaxf(M, lse_s[i * ch + hh]);
+      M = wave_max(M);
+      float sum = 0.f;
+      for (int i = lane; i < np; i += 64) sum += __expf(lse_s[i * ch + hh] - M);
+      sum = wave_sum(sum);
+      const float inv = 1.f / sum;
+      for (int i = lane; i < np; i += 64) wts[i * ch + hh] = __expf(lse_s[i * ch + hh] - M) * inv * sc_s[i * ch + hh];
+      if (lse_out && lane == 0 && blockIdx.z == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
+    }
+    __syncthreads();
+  };
+  if (fast) {  // same order of the sum as combine_sum: piece by piece
+    const int npf = np < PF ? np : PF;
+    int off[2], hhv[2];
+    f16x8 xp[PF][2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int e = 8 * (tid + 256 * v);
+      hhv[v] = e / dcc;
+      off[v] = hhv[v] * d_c + (e - hhv[v] * dcc);
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      if (k < npf) {
+        const int64_t sb = (int64_t)slots[k] * pst;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) xp[k][v] = *(const f16x8*)(srcp + sb + off[v]);
+      }
+    build_weights();
+    f32x4 acc[2][2] = {};
+    auto add = [&](int k, int v, const f16x8& x) __attribute__((always_inline)) {
+      const float wk = wts[k * ch + hhv[v]];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[v][0][j] += wk * (float)x[j];
+        acc[v][1][j] += wk * (float)x[4 + j];
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      if (k < npf) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) add(k, v, xp[k][v]);
+      }
+    for (int k = PF; k < np; ++k) {
+      const int64_t sb = (int64_t)slots[k] * pst;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) add(k, v, *(const f16x8*)(srcp + sb + off[v]));
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      *(f32x4*)(dst + off[v]) = acc[v][0];
+      *(f32x4*)(dst + off[v] + 4) = acc[v][1];
+    }
+    return;
   }
-  __syncthreads();
-  // weights: wave w handles heads w, w+4, ...
-  for (int hh = w; hh < nh; hh += 4) {
-    float M = -__builtin_inff();
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, lse_s[i * ch + hh]);
-    M = wave_max(M);
-    float sum = 0.f;
-    for (int i = lane; i < np; i += 64) sum += __expf(lse_s[i * ch + hh] - M);
-    sum = wave_sum(sum);
-    const float inv = 1.f / sum;
-    for (int i = lane; i < np; i += 64) wts[i * ch + hh] = __expf(lse_s[i * ch + hh] - M) * inv * sc_s[i * ch + hh];
-    if (lse_out && lane == 0 && blockIdx.z == 0) lse_out[(int64_t)b * n_h + h0 + hh] = M + __logf(sum);
-  }
-  __syncthreads();
+  build_weights();
   if (f16) combine_sum((const _Float16*)o_part, n_h, d_c, h0, nh, c0, dcc, np, slots, wts, ch, dst, red);
   else combine_sum((const float*)o_part, n_h, d_c, h0, nh, c0, dcc, np, slots, wts, ch, dst, red);
 }
