@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="C",
                     help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
                          "(a separate JSON line; the default run is the decode step)")
+    ap.add_argument("--precombined", action="store_true",
+                    help="the pre-combined absorption variant: W~^Q and W~^O built once, then one product each "
+                         "in place of the two-step projections (a separate JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -203,7 +206,10 @@ def main():
     case = make_case(cfg, device="cuda")
     B = case.B
     caches = [build_cache(mla, case) for _ in range(max(1, args.rotate))]
-    step = mla.DecodeStep(dims, B, args.splits)
+    if args.precombined:
+        step = mla.PrecombinedStep(dims, B, args.splits, case.weights)
+    else:
+        step = mla.DecodeStep(dims, B, args.splits)
     torch.cuda.synchronize()
     W, h, seq_lens = case.weights, case.h, case.seq_lens
     d = step.dims
@@ -214,11 +220,17 @@ def main():
     wsz = {k: v.numel() * v.element_size() for k, v in case.weights.items()}
     wq_bytes = sum(wsz[k] for k in ("W_dq", "W_uq", "W_qr", "W_dkv", "W_kr", "W_uk"))
     wo_bytes = wsz["W_uv"] + wsz["W_o"]
+    if args.precombined:
+        wq_bytes += step.Wq_pre.numel() * step.Wq_pre.element_size() - wsz["W_uq"] - wsz["W_uk"]
+        wo_bytes = step.Wo_pre.numel() * step.Wo_pre.element_size()
 
     def one_step(cache, ev=None):
         if ev is not None:
             ev[0].record()
-        mla.absorb_q(d, h, W, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+        if args.precombined:
+            mla.absorb_q_pre(d, h, W, step.Wq_pre, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+        else:
+            mla.absorb_q(d, h, W, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
         if ev is not None:
             ev[1].record()
         mla.rope(d, seq_lens, step.q_pe, step.kv_new, cache)
@@ -230,7 +242,10 @@ def main():
         mla.combine(d, args.splits, seq_lens, step.ws_d, step.o_lat, step.lse)
         if ev is not None:
             ev[4].record()
-        mla.absorb_out(d, step.o_lat, W["W_uv"], W["W_o"], step.ws_o, step.u)
+        if args.precombined:
+            mla.absorb_out_pre(d, step.o_lat, step.Wo_pre, step.ws_op, step.u)
+        else:
+            mla.absorb_out(d, step.o_lat, W["W_uv"], W["W_o"], step.ws_o, step.u)
         if ev is not None:
             ev[5].record()
 
@@ -293,17 +308,20 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.cdtype == "bf16" else cfg.cdtype,
-        "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 attention shape)",
+        "data": "synthetic (seeded; random-init weights of the "
+                + ("DeepSeek-V2 attention shape)" if dims.n_h == 128 else "running-model shape)"),
         "config": {"workload": f"config {cfg.key}: {cfg.title}", "batch": B, "seq_len": int(seq_lens.max()),
                    "sum_context_tokens": sigma_T, "cache_dtype": cfg.cdtype, "layout": cfg.layout,
                    "n_h": dims.n_h, "d_c": dims.d_c, "d_r": dims.d_r, "d": dims.d,
                    "decode_splits": args.splits or "one per CU", "cache_copies_cycled": len(caches),
-                   "hip_graph": bool(graphs)},
+                   "hip_graph": bool(graphs),
+                   "absorption": "pre-combined" if args.precombined else "two-step"},
         "latent_cache_gbps": cache_bytes / (t_dec + t_comb) / 1e9,
         "latent_cache_pct_hbm_peak": 100.0 * cache_bytes / (t_dec + t_comb) / 1e9 / HBM_PEAK_GBPS,
         "kernels_us": {"absorb_q": stage[0] * 1e6, "rope_append": stage[1] * 1e6, "decode_attn": t_dec * 1e6,
                        "combine": t_comb * 1e6, "absorb_out": stage[4] * 1e6, "step": ms_step * 1e3},
         "weights_gbps": {"absorb_q": wq_bytes / stage[0] / 1e9, "absorb_out": wo_bytes / stage[4] / 1e9},
+        "weight_bytes": {"absorb_q": wq_bytes, "absorb_out": wo_bytes},
         "attn_mfma_tflops": flops_attn / t_dec / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": DECODE_TRAFFIC_BYTES.get(cfg.key),

@@ -9,7 +9,9 @@
  * attention runs against the latents directly and the full keys/values are never formed.
  *
  * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
- * (chunked prefill: mla_prefill_tables, then the same five calls over the pseudo-sequences)
+ * (chunked prefill: mla_prefill_tables, then the same five calls over the pseudo-sequences;
+ *  pre-combined absorption: mla_precombine once, then mla_absorb_q_pre / mla_absorb_out_pre in
+ *  place of mla_absorb_q / mla_absorb_out)
  *
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers unless the comment says host. Tensors and workspaces must be
@@ -190,6 +192,41 @@ MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
  *   seq_lens_out: device int32 [B * C]; block_table_out: device int32 [B * C, max_pages]. */
 MLA_API mla_status mla_prefill_tables(const mla_cache* cache, int32_t B, int32_t C, const int32_t* p0,
                               int32_t* seq_lens_out, int32_t* block_table_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Pre-combined absorption — the alternative form of the two absorbed projections.
+ * "DeepSeek-V2 from Scratch" section 5.1 merges W^UQ_i and W^UK_i into one matrix
+ * W~^Q_i = (W^UK_i)^T W^UQ_i (d_c x d_cq) that maps c^Q straight to the absorbed query, and
+ * section 5.2 merges W^UV_i and W^O_i into W~^O_i = W^O_i W^UV_i (d x d_c) that maps the
+ * attention-weighted latent straight to the output. The results equal the two-step form up to
+ * rounding; the weight bytes differ (at the DeepSeek-V2 shape W~^Q is 3x and W~^O 3.6x the bytes
+ * of the factors they replace, at the running model's shape W~^Q is smaller).
+ *
+ * mla_precombine — build the stacked matrices once from the factors (float32 accumulation, one
+ * rounding to wdtype):
+ *   Wq_pre [n_h*d_c, d_cq]: row i*d_c + c is column c of (W^UK_i)^T W^UQ_i, i.e.
+ *       Wq_pre[i*d_c + c][k] = sum_e W_uk[i*d_h + e][c] * W_uq[i*d_h + e][k];
+ *   Wo_pre [d, n_h*d_c]:    Wo_pre[m][i*d_c + c] = sum_e W_o[m][i*d_h + e] * W_uv[i*d_h + e][c].
+ * Either output may be NULL (then it is not built, and its factors may be NULL). Outputs are in
+ * wdtype and caller-owned. */
+MLA_API mla_status mla_precombine(const mla_dims* dims, int32_t wdtype, const void* W_uq, const void* W_uk,
+                          const void* W_uv, const void* W_o, void* Wq_pre, void* Wo_pre, hipStream_t stream);
+
+/* mla_absorb_q_pre — mla_absorb_q with W~^Q: q_lat = Wq_pre c^Q in one product (W_uq and W_uk
+ * are not read). Same outputs, layouts and workspace size (mla_absorb_q_workspace_bytes). */
+MLA_API mla_status mla_absorb_q_pre(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h,
+                            const void* W_dq, const void* Wq_pre, const void* W_qr, const void* W_dkv,
+                            const void* W_kr, void* workspace, size_t ws_bytes, float* q_lat,
+                            float* q_pe, float* kv_new, hipStream_t stream);
+
+/* mla_absorb_out_pre — u = Wo_pre [o_lat_1; ...; o_lat_nh] in one product (the two-step
+ * mla_absorb_out with W~^O). o_lat [B, n_h, d_c] float32; u [B, d] float32. The workspace
+ * (K-split partial sums) needs mla_absorb_out_pre_workspace_bytes(dims, B) bytes, which may be
+ * 0 (then workspace may be NULL). */
+MLA_API size_t mla_absorb_out_pre_workspace_bytes(const mla_dims* dims, int32_t B);
+MLA_API mla_status mla_absorb_out_pre(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
+                              const void* Wo_pre, void* workspace, size_t ws_bytes, float* u,
+                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_cache_store — write given rows into a cache (prefix fill; not part of a decode step).

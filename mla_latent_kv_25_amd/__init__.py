@@ -4,9 +4,9 @@ The compute lives in libmla.so (HIP kernels for gfx950 behind the C ABI of inclu
 this package is its Python binding.
 """
 from .binding import (  # noqa: F401
-    BF16, F16, F32, FP8_E4M3, DecodeStep, Dims, LatentCache, MLAError, PrefillStep, absorb_out,
-    absorb_out_workspace_bytes,
-    absorb_q, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib,
-    prefill_tables, rope,
+    BF16, F16, F32, FP8_E4M3, DecodeStep, Dims, LatentCache, MLAError, PrecombinedStep, PrefillStep, absorb_out,
+    absorb_out_pre, absorb_out_pre_workspace_bytes, absorb_out_workspace_bytes,
+    absorb_q, absorb_q_pre, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib,
+    precombine, prefill_tables, rope,
     version,
 )

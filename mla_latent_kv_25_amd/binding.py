@@ -64,6 +64,10 @@ def lib():
         "mla_absorb_out_workspace_bytes": (SZ, [D, I32]),
         "mla_absorb_out": (I32, [D, I32, I32, P, P, P, P, SZ, P, ST]),
         "mla_prefill_tables": (I32, [C, I32, I32, P, P, P, ST]),
+        "mla_precombine": (I32, [D, I32, P, P, P, P, P, P, ST]),
+        "mla_absorb_q_pre": (I32, [D, I32, I32, P, P, P, P, P, P, P, SZ, P, P, P, ST]),
+        "mla_absorb_out_pre_workspace_bytes": (SZ, [D, I32]),
+        "mla_absorb_out_pre": (I32, [D, I32, I32, P, P, P, SZ, P, ST]),
         "mla_cache_store": (I32, [D, C, I32, P, I32, P, I64, ST]),
         "mla_status_str": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
@@ -79,7 +83,8 @@ def lib():
 
 EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_decode_workspace_bytes",
            "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
-           "mla_prefill_tables", "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
+           "mla_prefill_tables", "mla_precombine", "mla_absorb_q_pre", "mla_absorb_out_pre_workspace_bytes",
+           "mla_absorb_out_pre", "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
 
 
 def _check(status: int):
@@ -198,6 +203,39 @@ def absorb_out(dims: Dims, o_lat, W_uv, W_o, workspace, u):
                                 _ptr(u, torch.float32, "u"), _stream()))
 
 
+def precombine(dims: Dims, W, Wq_pre=None, Wo_pre=None):
+    """Build the pre-combined W~^Q [n_h*d_c, d_cq] and / or W~^O [d, n_h*d_c] (weight dtype) from
+    W["W_uq"], W["W_uk"] / W["W_uv"], W["W_o"]."""
+    dt = W["W_uq"].dtype
+    _check(lib().mla_precombine(ctypes.byref(dims), DTYPE_CODE[dt],
+                                *[_ptr(W[k], dt, k) for k in ("W_uq", "W_uk", "W_uv", "W_o")],
+                                _ptr(Wq_pre, dt, "Wq_pre"), _ptr(Wo_pre, dt, "Wo_pre"), _stream()))
+
+
+def absorb_q_pre(dims: Dims, h, W, Wq_pre, workspace, q_lat, q_pe, kv_new):
+    """absorb_q with the pre-combined W~^Q (W_uq and W_uk unused)."""
+    wdt = DTYPE_CODE[h.dtype]
+    _check(lib().mla_absorb_q_pre(ctypes.byref(dims), h.shape[0], wdt, _ptr(h, name="h"),
+                                  _ptr(W["W_dq"], h.dtype, "W_dq"), _ptr(Wq_pre, h.dtype, "Wq_pre"),
+                                  _ptr(W["W_qr"], h.dtype, "W_qr"), _ptr(W["W_dkv"], h.dtype, "W_dkv"),
+                                  _ptr(W["W_kr"], h.dtype, "W_kr"),
+                                  _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                  _ptr(q_lat, torch.float32, "q_lat"), _ptr(q_pe, torch.float32, "q_pe"),
+                                  _ptr(kv_new, torch.float32, "kv_new"), _stream()))
+
+
+def absorb_out_pre_workspace_bytes(dims: Dims, B: int) -> int:
+    return lib().mla_absorb_out_pre_workspace_bytes(ctypes.byref(dims), B)
+
+
+def absorb_out_pre(dims: Dims, o_lat, Wo_pre, workspace, u):
+    wdt = DTYPE_CODE[Wo_pre.dtype]
+    _check(lib().mla_absorb_out_pre(ctypes.byref(dims), o_lat.shape[0], wdt, _ptr(o_lat, torch.float32, "o_lat"),
+                                    _ptr(Wo_pre, name="Wo_pre"), _ptr(workspace, name="workspace"),
+                                    workspace.numel() * workspace.element_size(), _ptr(u, torch.float32, "u"),
+                                    _stream()))
+
+
 def prefill_tables(cache: LatentCache, B: int, C: int, p0, seq_lens_out, block_table_out):
     """Lengths and block tables of the B * C causal pseudo-sequences of a C-token prefill chunk."""
     cc = cache.c()
@@ -244,6 +282,28 @@ class DecodeStep:
         decode_attn(self.dims, self.q_lat, self.q_pe, cache, seq_lens, self.num_splits, self.ws_d)
         combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
         absorb_out(self.dims, self.o_lat, W["W_uv"], W["W_o"], self.ws_o, self.u)
+        return self.u
+
+
+class PrecombinedStep(DecodeStep):
+    """The decode step in the pre-combined form: W~^Q and W~^O are built once (precombine), then
+    each step runs absorb_q_pre -> rope -> decode_attn -> combine -> absorb_out_pre."""
+
+    def __init__(self, dims, B: int, num_splits: int, W, device="cuda", sm_scale: float = 0.0):
+        super().__init__(dims, B, num_splits, device, sm_scale)
+        dt = W["W_uq"].dtype
+        self.Wq_pre = torch.empty((dims.n_h * dims.d_c, dims.d_cq), dtype=dt, device=device)
+        self.Wo_pre = torch.empty((dims.d, dims.n_h * dims.d_c), dtype=dt, device=device)
+        precombine(self.dims, W, self.Wq_pre, self.Wo_pre)
+        self.ws_op = torch.empty(max(1, absorb_out_pre_workspace_bytes(self.dims, B)), dtype=torch.uint8,
+                                 device=device)
+
+    def run(self, h, W, cache: LatentCache, seq_lens):
+        absorb_q_pre(self.dims, h, W, self.Wq_pre, self.ws_q, self.q_lat, self.q_pe, self.kv_new)
+        rope(self.dims, seq_lens, self.q_pe, self.kv_new, cache)
+        decode_attn(self.dims, self.q_lat, self.q_pe, cache, seq_lens, self.num_splits, self.ws_d)
+        combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
+        absorb_out_pre(self.dims, self.o_lat, self.Wo_pre, self.ws_op, self.u)
         return self.u
 
 

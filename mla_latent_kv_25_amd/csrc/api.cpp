@@ -230,6 +230,61 @@ mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const
   return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
 }
 
+mla_status mla_precombine(const mla_dims* dims, int32_t wdtype, const void* W_uq, const void* W_uk,
+                          const void* W_uv, const void* W_o, void* Wq_pre, void* Wo_pre, hipStream_t stream) {
+  const char* fn = "mla_precombine";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (!Wq_pre && !Wo_pre) return ok();
+  if (Wq_pre && (!W_uq || !W_uk)) return fail(MLA_E_ARG, "%s: Wq_pre needs W_uq and W_uk", fn);
+  if (Wo_pre && (!W_uv || !W_o)) return fail(MLA_E_ARG, "%s: Wo_pre needs W_uv and W_o", fn);
+  if (misaligned(W_uq, W_uk, W_uv, W_o, Wq_pre, Wo_pre)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(mla::launch_precombine(*dims, wdtype, W_uq, W_uk, W_uv, W_o, Wq_pre, Wo_pre, stream), fn);
+}
+
+mla_status mla_absorb_q_pre(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h, const void* W_dq,
+                            const void* Wq_pre, const void* W_qr, const void* W_dkv, const void* W_kr,
+                            void* workspace, size_t ws_bytes, float* q_lat, float* q_pe, float* kv_new,
+                            hipStream_t stream) {
+  const char* fn = "mla_absorb_q_pre";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (B == 0) return ok();
+  if (!h || !W_dq || !Wq_pre || !W_qr || !W_dkv || !W_kr || !q_lat || !q_pe || !kv_new)
+    return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(h, W_dq, Wq_pre, W_qr, W_dkv, W_kr, q_lat, q_pe, kv_new, workspace))
+    return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  if (!workspace || ws_bytes < mla_absorb_q_workspace_bytes(dims, B))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_q_workspace_bytes(dims, B));
+  return hip_status(mla::launch_absorb_q_pre(*dims, B, wdtype, h, W_dq, Wq_pre, W_qr, W_dkv, W_kr, workspace, q_lat,
+                                             q_pe, kv_new, stream),
+                    fn);
+}
+
+size_t mla_absorb_out_pre_workspace_bytes(const mla_dims* dims, int32_t B) {
+  if (!dims || B <= 0) return 0;
+  return mla::absorb_out_pre_layout(*dims, B).bytes;
+}
+
+mla_status mla_absorb_out_pre(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
+                              const void* Wo_pre, void* workspace, size_t ws_bytes, float* u, hipStream_t stream) {
+  const char* fn = "mla_absorb_out_pre";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (B == 0) return ok();
+  if (!o_lat || !Wo_pre || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(o_lat, Wo_pre, u, workspace)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = mla_absorb_out_pre_workspace_bytes(dims, B);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  return hip_status(mla::launch_absorb_out_pre(*dims, B, wdtype, o_lat, Wo_pre, workspace, u, stream), fn);
+}
+
 mla_status mla_prefill_tables(const mla_cache* cache, int32_t B, int32_t C, const int32_t* p0,
                               int32_t* seq_lens_out, int32_t* block_table_out, hipStream_t stream) {
   const char* fn = "mla_prefill_tables";

@@ -73,6 +73,20 @@ AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B) {
   return L;
 }
 
+// u = Wo_pre [o_lat] in one product (pre-combined form): only the K-split partials
+static OSplits o_pre_splits(const mla_dims& d, int B) {
+  return {1, split_for(cdiv(d.d, o_wide(B) ? 2 * gm::MT : gm::MT) * col_tiles(B), d.n_h * d.d_c / gm::KC, 1)};
+}
+AbsorbOutLayout absorb_out_pre_layout(const mla_dims& d, int B) {
+  AbsorbOutLayout L;
+  const int sk = o_pre_splits(d, B).sk5;
+  L.off_o = 0;
+  L.off_part = 0;
+  L.part_floats = sk > 1 ? (size_t)sk * B * d.d : 0;
+  L.bytes = al256h(L.part_floats * 4);
+  return L;
+}
+
 // ------------------------------------------------------------------ segment table
 // Up to 3 weight matrices stacked along M that share the same activation X (e.g. W^DQ, W^DKV,
 // W^KR all multiply h). Segment s owns rows [m0[s], m0[s+1]) of the stacked output.
@@ -666,6 +680,146 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
   valu_any(wdt, false, false, st, d.d_h, B, d.d_c, W_uv, d.d_c, (int64_t)d.d_h * d.d_c, o_lat,
            (int64_t)d.n_h * d.d_c, d.d_c, o, nhdh, d.d_h, d.n_h);
   valu_any(wdt, false, false, st, d.d, B, nhdh, W_o, nhdh, 0, o, nhdh, 0, u, d.d, 0, 1);
+  return hipGetLastError();
+}
+
+// ================================================================================================
+// Pre-combined absorbed matrices ("DeepSeek-V2 from Scratch" section 5.1: W~^Q_i = (W^UK_i)^T W^UQ_i;
+// section 5.2: W~^O_i = W^O_i W^UV_i), built once from the factors:
+//   C_z(r, c) = sum_{e < K} A_z(r, e) B_z(e, c),  A_z(r, e) = A[z*azs + r*ars + e*aks],
+//   B_z(e, c) = B[z*bzs + e*bks + c],  C_z(r, c) = C[z*czs + r*crs + c],
+// float32 accumulation, one rounding to the weight type on the store. A plain LDS-tiled VALU
+// kernel: 64 x 64 outputs per workgroup (4 x 4 per thread), K in chunks of 16. It runs once per
+// set of weights, outside the decode step.
+template <int DT>
+__global__ __launch_bounds__(256) void k_precombine(int R, int Cc, int K, const void* __restrict__ Av, int64_t azs,
+                                                    int64_t ars, int64_t aks, const void* __restrict__ Bv,
+                                                    int64_t bzs, int64_t bks, void* __restrict__ Cv, int64_t czs,
+                                                    int64_t crs) {
+  using E = Elem<DT>;
+  __shared__ float As[16][65];
+  __shared__ float Bs[16][65];
+  const int tid = threadIdx.x, z = blockIdx.z;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const typename E::T* A = (const typename E::T*)Av + (int64_t)z * azs;
+  const typename E::T* Bp = (const typename E::T*)Bv + (int64_t)z * bzs;
+  const int tr = tid >> 4, tc = tid & 15;  // rows tr + 16 i, columns tc + 16 j
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = tid; e < 16 * 64; e += 256) {
+      const int kk = e >> 6, rr = e & 63;
+      const int r = r0 + rr, k = k0 + kk;
+      As[kk][rr] = (r < R && k < K) ? E::ld(A, (int64_t)r * ars + (int64_t)k * aks) : 0.f;
+      const int c = c0 + rr;
+      Bs[kk][rr] = (c < Cc && k < K) ? E::ld(Bp, (int64_t)k * bks + c) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][tr + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tc + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + tr + 16 * i, c = c0 + tc + 16 * j;
+      if (r >= R || c >= Cc) continue;
+      const int64_t o = (int64_t)z * czs + (int64_t)r * crs + c;
+      if constexpr (DT == MLA_F32) ((float*)Cv)[o] = acc[i][j];
+      else if constexpr (DT == MLA_F16) ((uint16_t*)Cv)[o] = f32_to_f16_bits(acc[i][j]);
+      else ((uint16_t*)Cv)[o] = f32_to_bf16_bits(acc[i][j]);
+    }
+}
+
+template <int DT>
+static void precombine_dt(const mla_dims& d, const void* W_uq, const void* W_uk, const void* W_uv, const void* W_o,
+                          void* Wq_pre, void* Wo_pre, hipStream_t st) {
+  if (Wq_pre) {  // rows i*d_c + c, columns k: sum_e W_uk[i*d_h + e][c] W_uq[i*d_h + e][k]
+    dim3 g(cdiv(d.d_c, 64), cdiv(d.d_cq, 64), d.n_h);
+    hipLaunchKernelGGL(k_precombine<DT>, g, dim3(256), 0, st, d.d_c, d.d_cq, d.d_h, W_uk, (int64_t)d.d_h * d.d_c,
+                       (int64_t)1, (int64_t)d.d_c, W_uq, (int64_t)d.d_h * d.d_cq, (int64_t)d.d_cq, Wq_pre,
+                       (int64_t)d.d_c * d.d_cq, (int64_t)d.d_cq);
+  }
+  if (Wo_pre) {  // rows m, columns i*d_c + c: sum_e W_o[m][i*d_h + e] W_uv[i*d_h + e][c]
+    dim3 g(cdiv(d.d, 64), cdiv(d.d_c, 64), d.n_h);
+    hipLaunchKernelGGL(k_precombine<DT>, g, dim3(256), 0, st, d.d, d.d_c, d.d_h, W_o, (int64_t)d.d_h,
+                       (int64_t)d.n_h * d.d_h, (int64_t)1, W_uv, (int64_t)d.d_h * d.d_c, (int64_t)d.d_c, Wo_pre,
+                       (int64_t)d.d_c, (int64_t)d.n_h * d.d_c);
+  }
+}
+
+hipError_t launch_precombine(const mla_dims& d, int wdt, const void* W_uq, const void* W_uk, const void* W_uv,
+                             const void* W_o, void* Wq_pre, void* Wo_pre, hipStream_t st) {
+  if (wdt == MLA_F32) precombine_dt<MLA_F32>(d, W_uq, W_uk, W_uv, W_o, Wq_pre, Wo_pre, st);
+  else if (wdt == MLA_F16) precombine_dt<MLA_F16>(d, W_uq, W_uk, W_uv, W_o, Wq_pre, Wo_pre, st);
+  else precombine_dt<MLA_BF16>(d, W_uq, W_uk, W_uv, W_o, Wq_pre, Wo_pre, st);
+  return hipGetLastError();
+}
+
+// MFMA shapes of the pre-combined products: stage 1 as in the two-step form, then
+// [W~^Q; W^QR] c^Q (segment boundary n_h*d_c) and W~^O [o_lat] (K = n_h*d_c).
+static bool mfma_pre_dims_ok(const mla_dims& d) {
+  return d.d % 256 == 0 && d.d_cq % 256 == 0 && d.d_c % 128 == 0 && d.d_r % 64 == 0 && (d.n_h * d.d_c) % 256 == 0 &&
+         (d.n_h * d.d_r) % 64 == 0;
+}
+
+hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h, const void* W_dq,
+                               const void* Wq_pre, const void* W_qr, const void* W_dkv, const void* W_kr, void* ws,
+                               float* q_lat, float* q_pe, float* kv_new, hipStream_t st) {
+  AbsorbQLayout L = absorb_q_layout(d, B);
+  float* cq = (float*)((char*)ws + L.off_cq);
+  float* part = (float*)((char*)ws + L.off_part);
+  const int rw = d.d_c + d.d_r;
+  const int nhdc = d.n_h * d.d_c;
+  if (wdt == MLA_BF16 && mfma_pre_dims_ok(d)) {
+    // stage 1: [c^Q | c^KV | k^R raw] = [W^DQ; W^DKV; W^KR] h (as in the two-step form)
+    Seg s1{};
+    s1.W[0] = W_dq; s1.W[1] = W_dkv; s1.W[2] = W_kr;
+    s1.Y[0] = cq; s1.ldy[0] = d.d_cq;
+    s1.Y[1] = kv_new; s1.ldy[1] = rw;
+    s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
+    s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
+    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+    // stage 2: [q~ | q^R raw] = [W~^Q; W^QR] c^Q, one product
+    Seg s2{};
+    s2.W[0] = Wq_pre; s2.W[1] = W_qr;
+    s2.Y[0] = q_lat; s2.ldy[0] = nhdc;
+    s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
+    s2.m0[0] = 0; s2.m0[1] = nhdc; s2.m0[2] = nhdc + d.n_h * d.d_r; s2.nseg = 2;
+    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
+    return hipGetLastError();
+  }
+  valu_any(wdt, true, false, st, d.d_cq, B, d.d, W_dq, d.d, 0, h, d.d, 0, cq, d.d_cq, 0, 1);
+  valu_any(wdt, true, false, st, d.d_c, B, d.d, W_dkv, d.d, 0, h, d.d, 0, kv_new, rw, 0, 1);
+  valu_any(wdt, true, false, st, d.d_r, B, d.d, W_kr, d.d, 0, h, d.d, 0, kv_new + d.d_c, rw, 0, 1);
+  valu_any(wdt, false, false, st, nhdc, B, d.d_cq, Wq_pre, d.d_cq, 0, cq, d.d_cq, 0, q_lat, nhdc, 0, 1);
+  valu_any(wdt, false, false, st, d.n_h * d.d_r, B, d.d_cq, W_qr, d.d_cq, 0, cq, d.d_cq, 0, q_pe,
+           (int64_t)d.n_h * d.d_r, 0, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_out_pre(const mla_dims& d, int B, int wdt, const float* o_lat, const void* Wo_pre, void* ws,
+                                 float* u, hipStream_t st) {
+  const int nhdc = d.n_h * d.d_c;
+  if (wdt == MLA_BF16 && mfma_pre_dims_ok(d)) {
+    Seg s{};
+    s.W[0] = Wo_pre; s.Y[0] = u; s.ldy[0] = d.d;
+    s.m0[0] = 0; s.m0[1] = d.d; s.nseg = 1;
+    mfma_gemm<true>(st, s, B, nhdc, o_lat, nhdc, o_pre_splits(d, B).sk5, (float*)ws, 1, 0, 0, 0,
+                    o_wide(B) ? 8 : 4);
+    return hipGetLastError();
+  }
+  valu_any(wdt, false, false, st, d.d, B, nhdc, Wo_pre, nhdc, 0, o_lat, nhdc, 0, u, d.d, 0, 1);
   return hipGetLastError();
 }
 

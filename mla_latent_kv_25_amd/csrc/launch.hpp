@@ -36,6 +36,7 @@ struct AbsorbQLayout { size_t off_cq, off_qc, off_part, part_floats, bytes; };
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B);
 struct AbsorbOutLayout { size_t off_o, off_part, part_floats, bytes; };
 AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B);
+AbsorbOutLayout absorb_out_pre_layout(const mla_dims& d, int B);
 
 hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float* q_pe, float* kv_new,
                        const CacheArgs* cache, hipStream_t st);
@@ -58,6 +59,15 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdtype, const void* h, 
                            hipStream_t st);
 hipError_t launch_absorb_out(const mla_dims& d, int B, int wdtype, const float* o_lat, const void* W_uv,
                              const void* W_o, void* ws, float* u, hipStream_t st);
+
+// Pre-combined absorption (W~^Q, W~^O): building the matrices and the two products that use them.
+hipError_t launch_precombine(const mla_dims& d, int wdt, const void* W_uq, const void* W_uk, const void* W_uv,
+                             const void* W_o, void* Wq_pre, void* Wo_pre, hipStream_t st);
+hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h, const void* W_dq,
+                               const void* Wq_pre, const void* W_qr, const void* W_dkv, const void* W_kr, void* ws,
+                               float* q_lat, float* q_pe, float* kv_new, hipStream_t st);
+hipError_t launch_absorb_out_pre(const mla_dims& d, int B, int wdt, const float* o_lat, const void* Wo_pre, void* ws,
+                                 float* u, hipStream_t st);
 
 int device_cu_count();
 

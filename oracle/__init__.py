@@ -9,6 +9,6 @@ from .encodings import (  # noqa: F401
 )
 from .mla import (  # noqa: F401
     OracleDims, softmax, rope, decode_step_explicit, decode_step_absorbed, decode_batch, prefill_chunk,
-    head_slices, absorbed_query, output_projection,
+    head_slices, absorbed_query, output_projection, precombined_heads, precombined_weights, decode_step_precombined,
 )
 from .counts import cache_counts  # noqa: F401

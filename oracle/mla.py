@@ -197,6 +197,48 @@ def output_projection(W, o_lat, dims: OracleDims):
     return W["W_o"] @ o.reshape(-1)
 
 
+def precombined_heads(W, dims: OracleDims, rnd=None):
+    """Per-head pre-combined matrices: [Scratch] section 5.1, W~^Q_i = (W^UK_i)^T W^UQ_i (d_c x d_cq),
+    and section 5.2, W~^O_i = W^O_i W^UV_i (d x d_c). rnd: optional rounding applied to each matrix
+    (the variant stores them in the weight type). Returns [(W~^Q_i, W~^O_i) for i < n_h]."""
+    Wuq, _, Wuk, Wuv, Wo = head_slices(W, dims)
+    r = (lambda x: x) if rnd is None else rnd
+    return [(r(Wuk[i].T @ Wuq[i]), r(Wo[i] @ Wuv[i])) for i in range(dims.n_h)]
+
+
+def precombined_weights(W, dims: OracleDims, rnd=None):
+    """The per-head matrices stacked as the library stores them: Wq_pre [n_h * d_c, d_cq] with row
+    block i = W~^Q_i, Wo_pre [d, n_h * d_c] with column block i = W~^O_i."""
+    pre = precombined_heads(W, dims, rnd)
+    return np.concatenate([q for q, _ in pre], axis=0), np.concatenate([o for _, o in pre], axis=1)
+
+
+def decode_step_precombined(W, pre, h, prefix, dims: OracleDims, cdtype):
+    """One decode step in the pre-combined form, head by head: q~_i = W~^Q_i c^Q scores the
+    latents, and u = sum_i W~^O_i o_lat_i. pre: precombined_heads(...) (possibly rounded). The
+    rotary query and the appended row are as in new_token."""
+    prefix = np.asarray(prefix, dtype=np.float64).reshape(-1, dims.d_c + dims.d_r)
+    T = prefix.shape[0] + 1
+    _, qR, _, _, read = new_token(W, h, T - 1, dims, cdtype)
+    cQ = W["W_dq"] @ h
+    rows = np.vstack([prefix, read[None, :]])
+    C, KR = rows[:, : dims.d_c], rows[:, dims.d_c:]
+    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    u = np.zeros(dims.d)
+    q_lat = np.zeros((dims.n_h, dims.d_c))
+    o_lat = np.zeros((dims.n_h, dims.d_c))
+    lse = np.zeros(dims.n_h)
+    for i, (Wq_i, Wo_i) in enumerate(pre):
+        q_lat[i] = Wq_i @ cQ                                    # q~_i = W~^Q_i c^Q
+        s = (C @ q_lat[i] + KR @ qR[i]) * scale
+        a = softmax(s)
+        m = s.max()
+        lse[i] = m + np.log(np.exp(s - m).sum())
+        o_lat[i] = a @ C
+        u += Wo_i @ o_lat[i]                                    # W~^O_i o_lat_i
+    return dict(u=u, o_lat=o_lat, lse=lse, q_lat=q_lat)
+
+
 def decode_batch(W, h, prefixes, dims: OracleDims, cdtype, heads=None, want_u=True):
     """decode_step_explicit over a batch; prefixes[b] are sequence b's stored rows."""
     return [decode_step_explicit(W, h[b], prefixes[b], dims, cdtype, heads=heads, want_u=want_u)

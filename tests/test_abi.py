@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -129,6 +129,31 @@ def test_absorb_out_and_store_validation(L):
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 65, FAKE, 65, None) == 1  # > t_cap
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 10, FAKE, 5, None) == 1   # stride
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 0, None, 0, None, 0, None) == 0
+
+
+def test_precombined_validation(L):
+    d = _dims()
+    odd = ctypes.c_void_p(0x1004)
+    assert L.mla_precombine(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.mla_precombine(ctypes.byref(d), 7, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # dtype
+    assert L.mla_precombine(ctypes.byref(d), 0, None, None, None, None, None, None, None) == 0   # nothing asked
+    assert L.mla_precombine(ctypes.byref(d), 0, None, FAKE, None, None, FAKE, None, None) == 1   # W_uq missing
+    assert b"W_uq" in L.mla_last_error()
+    assert L.mla_precombine(ctypes.byref(d), 0, None, None, FAKE, None, None, FAKE, None) == 1   # W_o missing
+    assert L.mla_precombine(ctypes.byref(d), 0, FAKE, FAKE, None, None, odd, None, None) == 1
+    assert b"aligned" in L.mla_last_error()
+    need_q = L.mla_absorb_q_workspace_bytes(ctypes.byref(d), 2)
+    args = [FAKE] * 6
+    assert L.mla_absorb_q_pre(ctypes.byref(d), 2, 0, *args[:2], None, *args[:3], FAKE, need_q, FAKE, FAKE, FAKE,
+                              None) == 1                                                        # Wq_pre NULL
+    assert L.mla_absorb_q_pre(ctypes.byref(d), 2, 0, *args, FAKE, need_q - 1, FAKE, FAKE, FAKE, None) == 3
+    assert L.mla_absorb_q_pre(ctypes.byref(d), 0, 0, *[None] * 6, None, 0, None, None, None, None) == 0
+    need_o = L.mla_absorb_out_pre_workspace_bytes(ctypes.byref(d), 2)
+    assert need_o > 0
+    assert L.mla_absorb_out_pre(ctypes.byref(d), 2, 0, None, FAKE, FAKE, need_o, FAKE, None) == 1
+    assert L.mla_absorb_out_pre(ctypes.byref(d), 2, 0, FAKE, FAKE, FAKE, need_o - 1, FAKE, None) == 3
+    assert L.mla_absorb_out_pre(ctypes.byref(d), 2, 3, FAKE, FAKE, FAKE, need_o, FAKE, None) == 1  # fp8 weights
+    assert L.mla_absorb_out_pre(ctypes.byref(d), 0, 0, None, None, None, 0, None, None) == 0
 
 
 def test_prefill_tables_validation(L):

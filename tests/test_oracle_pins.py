@@ -12,8 +12,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (OracleDims, cache_counts, decode_step_absorbed, decode_step_explicit, head_slices,
-                    load_rows, prefill_chunk, rope, softmax, store_rows)
+from oracle import (OracleDims, cache_counts, decode_step_absorbed, decode_step_explicit, decode_step_precombined,
+                    head_slices, load_rows, precombined_heads, precombined_weights, prefill_chunk, rope, softmax,
+                    store_rows)
 from synth import RUNNING_DIMS, V2_DIMS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -171,6 +172,54 @@ def test_explicit_equals_absorbed(dims, T, cdtype):
     for k in ("u", "o_lat", "lse"):
         err = np.linalg.norm(e[k] - a[k]) / np.linalg.norm(a[k])
         assert err < 1e-10, (k, err)
+
+
+@pytest.mark.parametrize("dims,T,cdtype", [
+    (SMALL, 1, "f32"), (SMALL, 9, "bf16"), (OracleDims.of(RUNNING_DIMS), 33, "f16"),
+    (OracleDims.of(V2_DIMS), 4, "bf16"),
+])
+def test_precombined_equals_explicit(dims, T, cdtype):
+    """The pre-combined form ([Scratch] sections 5.1-5.2: W~^Q_i = (W^UK_i)^T W^UQ_i and
+    W~^O_i = W^O_i W^UV_i, stacked by head) with exact float64 matrices gives the explicit step's
+    u, o_lat and lse to 1e-10: a transposed factor, a head block out of place or a wrong stacking
+    axis breaks it."""
+    rng = np.random.default_rng(3 * T + dims.d)
+    W = _rand_weights(dims, rng, sw=1.0 / math.sqrt(dims.d), kappa=3.0)
+    h = rng.standard_normal(dims.d)
+    stored, sc = store_rows(rng.standard_normal((T - 1, dims.d_c + dims.d_r)), cdtype)
+    prefix = load_rows(stored, cdtype, sc)
+    if dims.d <= 512:
+        Wq_pre, Wo_pre = precombined_weights(W, dims)
+        assert Wq_pre.shape == (dims.n_h * dims.d_c, dims.d_cq) and Wo_pre.shape == (dims.d, dims.n_h * dims.d_c)
+        # the stacked layout: row block i of Wq_pre is W~^Q_i, column block i of Wo_pre is W~^O_i
+        _, _, Wuk, Wuv, Wo = head_slices(W, dims)
+        Wuq = W["W_uq"].reshape(dims.n_h, dims.d_h, dims.d_cq)
+        i = dims.n_h - 1
+        np.testing.assert_allclose(Wq_pre[i * dims.d_c:(i + 1) * dims.d_c], Wuk[i].T @ Wuq[i], rtol=1e-12)
+        np.testing.assert_allclose(Wo_pre[:, i * dims.d_c:(i + 1) * dims.d_c], Wo[i] @ Wuv[i], rtol=1e-12)
+    e = decode_step_explicit(W, h, prefix, dims, cdtype)
+    p = decode_step_precombined(W, precombined_heads(W, dims), h, prefix, dims, cdtype)
+    for k in ("u", "o_lat", "lse"):
+        err = np.linalg.norm(e[k] - p[k]) / np.linalg.norm(e[k])
+        assert err < 1e-10, (k, err)
+
+
+def test_precombined_weight_sizes():
+    """Element counts of the pre-combined matrices against the factors they replace, from the
+    pages' two shapes: at DeepSeek-V2 W~^Q is 3x and W~^O 3.6x the factors' elements; at the
+    running model W~^Q is the smaller one."""
+    def counts(D):
+        wq = D.n_h * D.d_c * D.d_cq
+        wo = D.d * D.n_h * D.d_c
+        two_q = D.n_h * D.d_h * D.d_cq + D.n_h * D.d_h * D.d_c      # W^UQ + W^UK
+        two_o = D.d * D.n_h * D.d_h + D.n_h * D.d_h * D.d_c         # W^O + W^UV
+        return wq, wo, two_q, two_o
+    wq, wo, tq, to = counts(V2_DIMS)
+    assert (wq, tq) == (100_663_296, 33_554_432) and wq == 3 * tq
+    assert (wo, to) == (335_544_320, 92_274_688) and abs(wo / to - 3.636) < 1e-3
+    wq, wo, tq, to = counts(RUNNING_DIMS)
+    assert (wq, tq) == (98_304, 114_688) and wq < tq
+    assert (wo, to) == (524_288, 327_680) and wo > to
 
 
 # ---------------------------------------------------------------- closed forms
