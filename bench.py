@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # HBM bytes per decode_attn launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), both scaled by
 # a plain copy of known size; recorded in profiles/decode_attn_config2_hbm_counters.md for the
 # decode kernel as it stands. Workloads without a recorded measurement report null.
-DECODE_TRAFFIC_BYTES = {"2": 158748 * 1024 * 2 + 37380 * 1024}
+DECODE_TRAFFIC_BYTES = {"2": 158755 * 1024 * 2 + 39169 * 1024}
 
 
 def parse():

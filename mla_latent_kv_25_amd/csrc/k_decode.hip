@@ -1099,10 +1099,33 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
 // ================================================================================================
 // Generic kernel (any cache dtype, small dims): float32 arithmetic throughout. Used for the
 // running model and float32 caches. Limits: n_h*(d_c+d_r) <= 16384, d_c+d_r <= 512, n_h <= 64,
-// n_h*d_c <= 4096.
+// n_h*d_c <= 4096. Tiles of 32 tokens: wave w fetches rows w, w+4, ... of the next tile into
+// registers while the current tile is processed from LDS (rows padded to an odd stride, so the
+// per-token score reads hit distinct banks).
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its global loads
+// (__syncthreads() also waits for every outstanding global load, which would drain the next
+// tile's prefetch at each barrier).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 namespace gen {
 constexpr int TT = 32;
 constexpr int OPT = 16;  // outputs per thread
+}
+
+// Raw stored bits of one element, and their value (fp8: times the row's scale). Loads keep the raw
+// bits so that no conversion waits on a load before the next ones are issued.
+template <int CDT>
+__device__ __forceinline__ uint32_t cache_bits(const CacheArgs& c, int64_t ridx, int rw, int e) {
+  if constexpr (CDT == MLA_F32) return ((const uint32_t*)c.rows)[ridx * rw + e];
+  else if constexpr (CDT == MLA_F16 || CDT == MLA_BF16) return ((const uint16_t*)c.rows)[ridx * rw + e];
+  else return ((const uint8_t*)c.rows)[ridx * rw + e];
+}
+template <int CDT>
+__device__ __forceinline__ float bits_value(uint32_t x, float sc) {
+  if constexpr (CDT == MLA_F32) return __builtin_bit_cast(float, x);
+  else if constexpr (CDT == MLA_F16) return f16_bits_to_f32((uint16_t)x);
+  else if constexpr (CDT == MLA_BF16) return bf16_bits_to_f32((uint16_t)x);
+  else return e4m3_to_f32(x) * sc;
 }
 
 template <int CDT>
@@ -1113,7 +1136,7 @@ __device__ __forceinline__ float cache_elem(const CacheArgs& c, int64_t ridx, in
   else return e4m3_to_f32(((const uint8_t*)c.rows)[ridx * rw + e]) * c.scales[ridx];
 }
 
-template <int CDT>
+template <int CDT, int EPL, bool PAGED>
 __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_r,
                                                         const float* __restrict__ q_lat,
                                                         const float* __restrict__ q_pe, CacheArgs cache,
@@ -1122,11 +1145,14 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
                                                         float qscale, float* __restrict__ lse_part,
                                                         float* __restrict__ o_part) {
   using namespace gen;
-  extern __shared__ float sm[];
+  extern __shared__ __attribute__((aligned(16))) float sm[];
   const int rw = d_c + d_r;
+  // padded row stride of the tile in LDS: a multiple of 4 floats whose quarter is odd (rw is a
+  // multiple of 8), so 16 consecutive rows read at one offset hit 16 distinct 16-byte bank groups
+  const int rwp = rw + 4;
   float* qs = sm;                       // [n_h][rw]
-  float* ts = qs + n_h * rw;            // [TT][rw]
-  float* ss = ts + TT * rw;             // [n_h][TT]
+  float* ts = qs + n_h * rw;            // [TT][rwp]
+  float* ss = ts + TT * rwp;            // [n_h][TT]
   float* mrun = ss + n_h * TT;          // [n_h]
   float* lrun = mrun + n_h;             // [n_h]
   float* alf = lrun + n_h;              // [n_h]
@@ -1156,25 +1182,64 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
       qs[i] = (e < d_c ? q_lat[((int64_t)b * n_h + h) * d_c + e] : q_pe[((int64_t)b * n_h + h) * d_r + e - d_c]) * qscale;
     }
     for (int h = tid; h < n_h; h += 256) { mrun[h] = -__builtin_inff(); lrun[h] = 0.f; }
-    float O[OPT];
+    constexpr int OPT4 = OPT / 4;
+    const int nout4 = nout / 4;
+    f32x4 O[OPT4];
 #pragma unroll
-    for (int k = 0; k < OPT; ++k) O[k] = 0.f;
-    __syncthreads();
+    for (int k = 0; k < OPT4; ++k) O[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // rows of one tile in registers: row w + 4m, elements lane + 64j (rows past the segment
+    // re-read its last row; their scores are masked)
+    // EPL = element groups of 64 per row (rw <= 64 * EPL)
+    constexpr int RPW = TT / 4;
+    uint32_t v[RPW][EPL];
+    float vsc[RPW];
+    auto fetch = [&](int64_t tb) __attribute__((always_inline)) {
+      const int vt = (int)((t1 - tb) < TT ? (t1 - tb) : TT);
+      int64_t ridx[RPW];
+#pragma unroll
+      for (int m = 0; m < RPW; ++m) {
+        const int64_t j = tb + (w + 4 * m < vt ? w + 4 * m : vt - 1);
+        if constexpr (PAGED) ridx[m] = row_index(cache, b, j);
+        else ridx[m] = (int64_t)b * cache.t_cap + j;
+      }
+      // every load is issued (indices past the row clamp to its last element), none behind a branch
+#pragma unroll
+      for (int m = 0; m < RPW; ++m) {
+        if constexpr (CDT == MLA_FP8_E4M3) vsc[m] = cache.scales[ridx[m]];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = lane + 64 * j;
+          v[m][j] = cache_bits<CDT>(cache, ridx[m], rw, e < rw ? e : rw - 1);
+        }
+      }
+    };
+    fetch(t0);
+    lds_barrier();
     for (int64_t tb = t0; tb < t1; tb += TT) {
       const int valid = (int)((t1 - tb) < TT ? (t1 - tb) : TT);
-      for (int i = tid; i < TT * rw; i += 256) {
-        int t = i / rw, e = i % rw;
-        int64_t tok = tb + (t < valid ? t : valid - 1);
-        ts[i] = cache_elem<CDT>(cache, row_index(cache, b, tok), rw, e);
-      }
-      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < RPW; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = lane + 64 * j;
+          if (e < rw) ts[(w + 4 * m) * rwp + e] = bits_value<CDT>(v[m][j], CDT == MLA_FP8_E4M3 ? vsc[m] : 1.f);
+        }
+      lds_barrier();
+      if (tb + TT < t1) fetch(tb + TT);  // in flight while this tile is processed
+      // scores: one (head, token) pair per thread, four independent partial sums
       for (int i = tid; i < n_h * TT; i += 256) {
-        int h = i / TT, t = i % TT;
-        float acc = 0.f;
-        for (int e = 0; e < rw; ++e) acc += qs[h * rw + e] * ts[t * rw + e];
-        ss[i] = t < valid ? acc : -__builtin_inff();
+        const int h = i / TT, t = i % TT;
+        const f32x4* qv = (const f32x4*)(qs + h * rw);
+        const f32x4* xv = (const f32x4*)(ts + t * rwp);
+        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int e4 = 0; e4 < rw / 4; ++e4) {
+          const f32x4 q = qv[e4], x = xv[e4];
+          a4[0] += q[0] * x[0]; a4[1] += q[1] * x[1]; a4[2] += q[2] * x[2]; a4[3] += q[3] * x[3];
+        }
+        ss[i] = t < valid ? (a4[0] + a4[1]) + (a4[2] + a4[3]) : -__builtin_inff();
       }
-      __syncthreads();
+      lds_barrier();
       for (int h = w; h < n_h; h += 4) {
         float v = lane < TT ? ss[h * TT + lane] : -__builtin_inff();
         float mx = wave_max(v);
@@ -1189,25 +1254,32 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
           mrun[h] = m_new;
         }
       }
-      __syncthreads();
+      lds_barrier();
+      // values: four consecutive columns of one head per thread and group
 #pragma unroll
-      for (int k = 0; k < OPT; ++k) {
-        int idx = tid + 256 * k;
-        if (idx < nout) {
-          int h = idx / d_c, c = idx % d_c;
-          float acc = O[k] * alf[h];
-          for (int t = 0; t < valid; ++t) acc += ss[h * TT + t] * ts[t * rw + c];
+      for (int k = 0; k < OPT4; ++k) {
+        const int i4 = tid + 256 * k;
+        if (i4 < nout4) {
+          const int h = (4 * i4) / d_c, c = 4 * i4 - h * d_c;
+          const float a = alf[h];
+          f32x4 acc = {O[k][0] * a, O[k][1] * a, O[k][2] * a, O[k][3] * a};
+#pragma unroll 4
+          for (int t = 0; t < valid; ++t) {
+            const float pt = ss[h * TT + t];
+            const f32x4 x = *(const f32x4*)(ts + t * rwp + c);
+            acc[0] += pt * x[0]; acc[1] += pt * x[1]; acc[2] += pt * x[2]; acc[3] += pt * x[3];
+          }
           O[k] = acc;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
 #pragma unroll
-    for (int k = 0; k < OPT; ++k) {
-      int idx = tid + 256 * k;
-      if (idx < nout) {
-        int h = idx / d_c;
-        o_part[slot * nout + idx] = O[k] / lrun[h];
+    for (int k = 0; k < OPT4; ++k) {
+      const int i4 = tid + 256 * k;
+      if (i4 < nout4) {
+        const float inv = 1.f / lrun[(4 * i4) / d_c];
+        *(f32x4*)(o_part + slot * nout + 4 * i4) = f32x4{O[k][0] * inv, O[k][1] * inv, O[k][2] * inv, O[k][3] * inv};
       }
     }
     for (int h = tid; h < n_h; h += 256)
@@ -1491,25 +1563,23 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
 #undef MLA_V3
   } else {
     const int rw = d.d_c + d.d_r;
-    size_t smem = (size_t)(d.n_h * rw + gen::TT * rw + d.n_h * gen::TT + 3 * d.n_h) * 4;
+    size_t smem = (size_t)(d.n_h * rw + gen::TT * (rw + 4) + d.n_h * gen::TT + 3 * d.n_h) * 4;
+    const bool paged = c.page_size > 0;
+    const bool narrow = rw <= 192;  // running-model rows (160 elements)
+#define MLA_GEN(CDT, EPL, PG)                                                                              \
+  hipLaunchKernelGGL((k_decode_generic<CDT, EPL, PG>), dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r, q_lat, q_pe, \
+                     c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part)
+#define MLA_GEN_DT(CDT)                                    \
+  if (narrow) { if (paged) MLA_GEN(CDT, 3, true); else MLA_GEN(CDT, 3, false); } \
+  else { if (paged) MLA_GEN(CDT, 8, true); else MLA_GEN(CDT, 8, false); }
     switch (c.dtype) {
-      case MLA_F32:
-        hipLaunchKernelGGL(k_decode_generic<MLA_F32>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
-        break;
-      case MLA_F16:
-        hipLaunchKernelGGL(k_decode_generic<MLA_F16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
-        break;
-      case MLA_BF16:
-        hipLaunchKernelGGL(k_decode_generic<MLA_BF16>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c, d.d_r,
-                           q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
-        break;
-      default:
-        hipLaunchKernelGGL(k_decode_generic<MLA_FP8_E4M3>, dim3(G), dim3(256), smem, st, d.n_h, d.d_c,
-                           d.d_r, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, lse_part, o_part);
-        break;
+      case MLA_F32: MLA_GEN_DT(MLA_F32); break;
+      case MLA_F16: MLA_GEN_DT(MLA_F16); break;
+      case MLA_BF16: MLA_GEN_DT(MLA_BF16); break;
+      default: MLA_GEN_DT(MLA_FP8_E4M3); break;
     }
+#undef MLA_GEN_DT
+#undef MLA_GEN
   }
   return hipGetLastError();
 }

@@ -485,6 +485,9 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
 // float32 VALU GEMM for float32 / float16 / bf16 weights of any shape:
 //   Y[n][m] = sum_k A(m, k) X[n][k],  A(m, k) = TRANS ? W[k*lda + m] : W[m*lda + k].
 // Tile 64 (m) x 16 (n) per 256 threads, k in steps of 32 through LDS.
+// Barrier for LDS hand-offs only (waits for this wave's LDS operations, not its global loads).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int ADT, int XDT, bool TRANS>
 __global__ __launch_bounds__(256) void k_gemm_valu(int M, int N, int K, const void* __restrict__ Wv,
                                                    int64_t lda, int64_t zW, const void* __restrict__ Xv,
@@ -498,28 +501,48 @@ __global__ __launch_bounds__(256) void k_gemm_valu(int M, int N, int K, const vo
   const typename Elem<XDT>::T* X = (const typename Elem<XDT>::T*)Xv + (int64_t)z * zX;
   const int mi = tid & 63, nq = tid >> 6;  // thread: row mi, columns nq*4 .. nq*4+3
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    for (int e = tid; e < 64 * 32; e += 256) {
+  // the next k-chunk's elements are fetched into registers while the current one is used from
+  // LDS; barriers wait for LDS only, so those loads stay in flight
+  float wv[8], xv[2];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = tid + 256 * q;
       int mm, kk;
       if (TRANS) { mm = e & 63; kk = e >> 6; } else { kk = e & 31; mm = e >> 5; }
       const int m = m0 + mm, k = k0 + kk;
-      float v = 0.f;
-      if (m < M && k < K) v = Elem<ADT>::ld(W, TRANS ? (int64_t)k * lda + m : (int64_t)m * lda + k);
-      Ws[mm][kk] = v;
+      wv[q] = (m < M && k < K) ? Elem<ADT>::ld(W, TRANS ? (int64_t)k * lda + m : (int64_t)m * lda + k) : 0.f;
     }
-    for (int e = tid; e < 16 * 32; e += 256) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q;
       const int nn = e >> 5, kk = e & 31;
       const int n = n0 + nn, k = k0 + kk;
-      Xs[nn][kk] = (n < N && k < K) ? Elem<XDT>::ld(X, (int64_t)n * ldx + k) : 0.f;
+      xv[q] = (n < N && k < K) ? Elem<XDT>::ld(X, (int64_t)n * ldx + k) : 0.f;
     }
-    __syncthreads();
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = tid + 256 * q;
+      if (TRANS) Ws[e & 63][e >> 6] = wv[q];
+      else Ws[e >> 5][e & 31] = wv[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q;
+      Xs[e >> 5][e & 31] = xv[q];
+    }
+    lds_sync();
+    if (k0 + 32 < K) fetch(k0 + 32);
 #pragma unroll 8
     for (int kk = 0; kk < 32; ++kk) {
       const float a = Ws[mi][kk];
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] += a * Xs[nq * 4 + q][kk];
     }
-    __syncthreads();
+    lds_sync();
   }
   const int m = m0 + mi;
   if (m >= M) return;
