@@ -549,22 +549,46 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         // fp8: codes widened to bf16 in registers on the way into LDS; scales per token.
         u32x2 r8[LOADS];
         float scv = 0.f;
+        // Row chunks of tile it: a uniform base plus the packed 32-bit per-lane offsets (rows
+        // past the segment re-read its last row); no per-chunk 64-bit addresses are kept, so
+        // nothing spills and the loads stay in flight until store() needs them.
         auto load = [&](int it) {
           const int64_t tt0 = t0 + (int64_t)it * TT;
-          const int64_t tlast = (tt0 + TT - 1 < t1 - 1) ? tt0 + TT - 1 : t1 - 1;
-          rows.tile(tt0, tlast);
-          const uint8_t* rows_b = (const uint8_t*)cache.rows;
+          const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+          uint32_t off[LOADS];
 #pragma unroll
           for (int i = 0; i < LOADS; ++i) {
-            const int f = i * 256 + tid, t = f / CHUNKS;
-            int64_t tok = tt0 + t;
-            if (tok > t1 - 1) tok = t1 - 1;
-            r8[i] = *(const u32x2*)(rows_b + rows.row(tok) * RW + (swz(t, f - t * CHUNKS) << 3));
+            uint32_t d2 = doff2[i >> 1];
+            asm volatile("" : "+v"(d2));
+            off[i] = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
+            if (last < TT - 1) {
+              const int t = (int)(off[i] / RW);
+              if (t > last) off[i] -= (uint32_t)(t - last) * RW;
+            }
           }
+          // page ids of the tile (scalar loads) before anything that locates rows
+          if constexpr (PAGED) rows.tile(tt0, tt0 + last);
+          // the token scale first: a wait for it (in issue order) then leaves the chunks in flight.
+          // The lane offset is made opaque so that the compiler keeps no loop-carried 64-bit
+          // per-lane token counter (it spilled one, and its reload drained the chunk loads).
           if (tid < TT) {
-            int64_t tok = tt0 + tid;
-            if (tok > t1 - 1) tok = t1 - 1;
-            scv = cache.scales[rows.row(tok)];
+            int dt = tid < last ? tid : last;
+            asm volatile("" : "+v"(dt));
+            scv = cache.scales[rows.row(tt0 + dt)];
+          }
+          if constexpr (!PAGED) {
+            const uint8_t* base = rows_b + (rows.base_row + tt0) * RW;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) r8[i] = *(const u32x2*)(base + off[i]);
+          } else {
+            // a 32-row tile spans at most two pages: rows before `split` live in the first one
+            const int ps = 1 << rows.ps_shift;
+            const int s_in = (int)(tt0 & (ps - 1));
+            const uint32_t split = (uint32_t)(ps - s_in) * RW;
+            const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * RW;
+            const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * RW - (int64_t)split;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) r8[i] = *(const u32x2*)((off[i] < split ? B0 : B1) + off[i]);
           }
         };
         auto store = [&](int it) {
