@@ -406,6 +406,11 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
   const int g = lane >> 5, l32 = lane & 31;
   const int i = blockIdx.y;              // head
   const int c0 = blockIdx.x * TC;        // column tile
+  // blockIdx.z: batch rows [32 NB z, 32 NB (z + 1)) (one launch covers any N)
+  const int nz = 32 * NB * (int)blockIdx.z;
+  N -= nz;
+  qC += (int64_t)nz * n_h * DH;
+  q_lat += (int64_t)nz * n_h * d_c;
   {
     // W^UK[i*128 .. +128][c0 .. c0+128]: 2048 16-byte pieces, 8 per thread;
     // q^C[n][i*128 .. +128] for n < 32 NB: 32 NB * 32 pieces, 4 NB per thread
@@ -653,17 +658,13 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
     s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
     mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
-    for (int b0 = 0; b0 < B; b0 += gm::MAXB) {
-      const int nb = B - b0 < gm::MAXB ? B - b0 : gm::MAXB;
-      // stage 3: q_lat_i = (W^UK_i)^T q^C_i
-      dim3 g3(d.d_c / absq::TC, d.n_h);
-      const float* qcb = qc + (int64_t)b0 * nhdh;
-      float* qlb = q_lat + (int64_t)b0 * d.n_h * d.d_c;
-      if (nb <= 32) hipLaunchKernelGGL(k_absorb_uk<1>, g3, dim3(256), 0, st, d.n_h, d.d_c, nb, (const uint16_t*)W_uk, qcb, qlb);
-      else if (nb <= 64) hipLaunchKernelGGL(k_absorb_uk<2>, g3, dim3(256), 0, st, d.n_h, d.d_c, nb, (const uint16_t*)W_uk, qcb, qlb);
-      else if (nb <= 96) hipLaunchKernelGGL(k_absorb_uk<3>, g3, dim3(256), 0, st, d.n_h, d.d_c, nb, (const uint16_t*)W_uk, qcb, qlb);
-      else hipLaunchKernelGGL(k_absorb_uk<4>, g3, dim3(256), 0, st, d.n_h, d.d_c, nb, (const uint16_t*)W_uk, qcb, qlb);
-    }
+    // stage 3: q_lat_i = (W^UK_i)^T q^C_i, batch rows in chunks of up to 128 along grid z
+    dim3 g3(d.d_c / absq::TC, d.n_h, cdiv(B, gm::MAXB));
+    const uint16_t* wuk = (const uint16_t*)W_uk;
+    if (B <= 32) hipLaunchKernelGGL(k_absorb_uk<1>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
+    else if (B <= 64) hipLaunchKernelGGL(k_absorb_uk<2>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
+    else if (B <= 96) hipLaunchKernelGGL(k_absorb_uk<3>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
+    else hipLaunchKernelGGL(k_absorb_uk<4>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
     return hipGetLastError();
   }
   // VALU path (any dims, float32/float16/bf16 weights)
