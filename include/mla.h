@@ -76,11 +76,27 @@ typedef enum {
 
 /* Model dimensions (the pages' notation). rope_base: rotary frequency base (10000 on the
  * pages' configs). sm_scale <= 0 selects 1/sqrt(d_h + d_r), the scale of "DeepSeek-V2 from
- * Scratch" section 4.4. Requirements: all dims > 0, d_r even, d_c and d_r multiples of 8. */
+ * Scratch" section 4.4. Requirements: all dims > 0, d_r even, d_c and d_r multiples of 8.
+ *
+ * Long-context extension of the decoupled RoPE (the DeepSeek-V2 review page, "4. Pre-Training":
+ * YaRN applied to k^R to extend the context from 4K to 128K; the page gives no formula, so the
+ * YaRN method is taken as published, with its parameters supplied here). yarn_factor <= 1 turns
+ * it off (plain RoPE). With yarn_factor s > 1, pair m's frequency theta_m = rope_base^(-2m/d_r)
+ * becomes
+ *     theta'_m = (1 - g) * theta_m / s + g * theta_m,
+ *     r = yarn_orig_len * theta_m / (2 pi)   (turns of pair m over the original context),
+ *     g = 0 for r < yarn_alpha, 1 for r > yarn_beta, (r - yarn_alpha) / (yarn_beta - yarn_alpha)
+ *         in between,
+ * for q^R and k^R alike, and the default score scale (sm_scale <= 0) is multiplied by
+ * (0.1 ln s + 1)^2, the method's attention temperature. */
 typedef struct {
   int32_t d, n_h, d_h, d_c, d_cq, d_r;
   double rope_base;
   float sm_scale;
+  float yarn_factor;      /* s; <= 1: off */
+  int32_t yarn_orig_len;  /* original context length (tokens), >= 1 when s > 1 */
+  float yarn_alpha;       /* ramp start (turns), >= 0 */
+  float yarn_beta;        /* ramp end (turns), > yarn_alpha */
 } mla_dims;
 
 /* Latent cache of one layer. Row width is d_c + d_r elements: [c^KV | k^R].
@@ -124,7 +140,8 @@ MLA_API mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype,
  * "DeepSeek-V2 from Scratch" section 3.1 (a position-dependent rotation whose query-key dot
  * product depends only on the offset), sections 4.1-4.2 (q^R per head, one k^R shared by all
  * heads) and section 4.5 (k^R is cached already rotated). Pairs (x[2m], x[2m+1]) are rotated by
- * angle pos * rope_base^(-2m/d_r), computed in float64.
+ * angle pos * theta_m, theta_m = rope_base^(-2m/d_r) (or its YaRN form, see mla_dims), computed
+ * in float64.
  *   seq_lens: device int32 [B]; pos_b = seq_lens[b] - 1.
  *   q_pe [B, n_h, d_r] and the k^R part of kv_new [B, d_c + d_r] are rotated IN PLACE.
  *   cache: if non-NULL, row [c^KV | k^R] of each sequence is written to slot pos_b, rounded to

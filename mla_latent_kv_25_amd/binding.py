@@ -27,11 +27,16 @@ class MLAError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_r", ctypes.c_int32),
-                ("rope_base", ctypes.c_double), ("sm_scale", ctypes.c_float)]
+                ("rope_base", ctypes.c_double), ("sm_scale", ctypes.c_float),
+                ("yarn_factor", ctypes.c_float), ("yarn_orig_len", ctypes.c_int32),
+                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float)]
 
     @classmethod
     def of(cls, dims, sm_scale: float = 0.0) -> "Dims":
-        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base), sm_scale)
+        """From any object with the dimension attributes; YaRN fields are optional (off)."""
+        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base), sm_scale,
+                   float(getattr(dims, "yarn_factor", 1.0)), int(getattr(dims, "yarn_orig_len", 0)),
+                   float(getattr(dims, "yarn_alpha", 0.0)), float(getattr(dims, "yarn_beta", 0.0)))
 
 
 class CCache(ctypes.Structure):

@@ -54,6 +54,12 @@ mla_status check_dims(const mla_dims* d, const char* fn) {
   if (d->d_r % 8 != 0 || d->d_c % 8 != 0) return fail(MLA_E_ARG, "%s: d_c and d_r must be multiples of 8", fn);
   if (!(d->rope_base > 1.0) || !std::isfinite(d->rope_base)) return fail(MLA_E_ARG, "%s: rope_base must be > 1", fn);
   if (!std::isfinite(d->sm_scale)) return fail(MLA_E_ARG, "%s: sm_scale must be finite", fn);
+  if (!std::isfinite(d->yarn_factor)) return fail(MLA_E_ARG, "%s: yarn_factor must be finite", fn);
+  if (d->yarn_factor > 1.f) {
+    if (d->yarn_orig_len < 1) return fail(MLA_E_ARG, "%s: yarn_orig_len must be >= 1", fn);
+    if (!(d->yarn_alpha >= 0.f) || !(d->yarn_beta > d->yarn_alpha) || !std::isfinite(d->yarn_beta))
+      return fail(MLA_E_ARG, "%s: YaRN ramp needs 0 <= yarn_alpha < yarn_beta", fn);
+  }
   return MLA_OK;
 }
 
@@ -86,7 +92,13 @@ mla_status check_cache(const mla_cache* c, const char* fn, mla::CacheArgs* out) 
 }
 
 float resolve_scale(const mla_dims* d) {
-  return d->sm_scale > 0.f ? d->sm_scale : (float)(1.0 / std::sqrt((double)(d->d_h + d->d_r)));
+  if (d->sm_scale > 0.f) return d->sm_scale;
+  double t = 1.0;  // YaRN attention temperature on the default scale
+  if (d->yarn_factor > 1.f) {
+    const double m = 0.1 * std::log((double)d->yarn_factor) + 1.0;
+    t = m * m;
+  }
+  return (float)(t / std::sqrt((double)(d->d_h + d->d_r)));
 }
 
 }  // namespace

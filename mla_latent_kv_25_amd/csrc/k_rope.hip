@@ -4,7 +4,9 @@
 // every head has its own rotary query q^R_i, all heads share one rotary key k^R; section 4.5: k^R
 // is stored already rotated next to the latent c^KV. Pairs (x[2m], x[2m+1]) turn by
 // pos * base^(-2m/d_r); angles are formed and evaluated in float64 so that positions up to 2^17
-// keep full float32 accuracy in the rotated values.
+// keep full float32 accuracy in the rotated values. The DeepSeek-V2 review page ("4. Pre-Training")
+// extends the context of k^R with YaRN; with a factor s > 1 each pair's frequency is blended
+// between theta / s and theta by the published ramp over its turns in the original context.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,7 +49,21 @@ __device__ void store_row_block(const CacheArgs& c, int64_t ridx, const float* v
 // Grid (B, 1 + head blocks): blockIdx.y == 0 rotates k^R and appends the row; block y > 0
 // rotates the queries of heads [(y-1) * RH, y * RH). Each block forms the cos/sin table itself.
 constexpr int RH = 32;
-__global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, double base,
+// Rotary frequency of pair m: base^(-2m/d_r), or its YaRN blend when s > 1 (the pair's turns
+// over the original context, r = L theta / 2pi, pick theta / s below alpha, theta above beta and a
+// linear mix in between).
+struct RopeFreq {
+  double base, s, L, alpha, beta;
+  __device__ double operator()(int m, int d_r) const {
+    const double theta = pow(base, -2.0 * (double)m / (double)d_r);
+    if (!(s > 1.0)) return theta;
+    const double r = L * theta * 0.15915494309189533577;  // 1 / (2 pi)
+    const double g = r < alpha ? 0.0 : (r > beta ? 1.0 : (r - alpha) / (beta - alpha));
+    return (1.0 - g) * theta / s + g * theta;
+  }
+};
+
+__global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, RopeFreq freq,
                                                       const int32_t* __restrict__ seq_lens,
                                                       float* __restrict__ q_pe, float* __restrict__ kv_new,
                                                       CacheArgs cache, int write_cache) {
@@ -62,8 +78,7 @@ __global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, 
   const int tid = threadIdx.x;
   const int pos = seq_lens[b] - 1;
   for (int m = tid; m < half; m += blockDim.x) {
-    double theta = pow(base, -2.0 * (double)m / (double)d_r);
-    double ang = (double)pos * theta;
+    double ang = (double)pos * freq(m, d_r);
     double s, c;
     sincos(ang, &s, &c);
     cs[m] = (float)c;
@@ -151,7 +166,9 @@ hipError_t launch_rope(const mla_dims& d, int B, const int32_t* seq_lens, float*
                        const CacheArgs* cache, hipStream_t st) {
   CacheArgs c = cache ? *cache : CacheArgs{};
   size_t smem = (size_t)(d.d_r + d.d_c + d.d_r + 4) * sizeof(float);
-  hipLaunchKernelGGL(k_rope_append, dim3(B, 1 + (d.n_h + RH - 1) / RH), dim3(256), smem, st, d.n_h, d.d_c, d.d_r, d.rope_base,
+  const RopeFreq freq{d.rope_base, d.yarn_factor > 1.f ? (double)d.yarn_factor : 1.0, (double)d.yarn_orig_len,
+                      (double)d.yarn_alpha, (double)d.yarn_beta};
+  hipLaunchKernelGGL(k_rope_append, dim3(B, 1 + (d.n_h + RH - 1) / RH), dim3(256), smem, st, d.n_h, d.d_c, d.d_r, freq,
                      seq_lens, q_pe, kv_new, c, cache ? 1 : 0);
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@ from .encodings import (  # noqa: F401
     quantize_row_e4m3, quantize_rows_e4m3, store_rows, load_rows,
 )
 from .mla import (  # noqa: F401
-    OracleDims, softmax, rope, decode_step_explicit, decode_step_absorbed, decode_batch, prefill_chunk,
+    OracleDims, softmax, rope, rope_frequencies, score_scale, decode_step_explicit, decode_step_absorbed, decode_batch, prefill_chunk,
     head_slices, absorbed_query, output_projection, precombined_heads, precombined_weights, decode_step_precombined,
 )
 from .counts import cache_counts  # noqa: F401

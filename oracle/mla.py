@@ -41,10 +41,54 @@ class OracleDims:
     d_cq: int
     d_r: int
     rope_base: float = 10000.0
+    # YaRN extension of the decoupled RoPE: factor s (<= 1: off), original context length L and
+    # the ramp bounds alpha < beta, in turns over L
+    yarn_factor: float = 1.0
+    yarn_orig_len: int = 0
+    yarn_alpha: float = 0.0
+    yarn_beta: float = 0.0
 
     @classmethod
     def of(cls, dims) -> "OracleDims":
-        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base))
+        return cls(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_r, float(dims.rope_base),
+                   float(getattr(dims, "yarn_factor", 1.0)), int(getattr(dims, "yarn_orig_len", 0)),
+                   float(getattr(dims, "yarn_alpha", 0.0)), float(getattr(dims, "yarn_beta", 0.0)))
+
+    @property
+    def yarn(self):
+        """(s, L, alpha, beta) when the extension is on, else None."""
+        if self.yarn_factor <= 1.0:
+            return None
+        return (self.yarn_factor, self.yarn_orig_len, self.yarn_alpha, self.yarn_beta)
+
+
+def rope_frequencies(n, base=10000.0, yarn=None):
+    """Rotation frequency of each of the n/2 pairs: base^(-2m/n) (the textbook RoPE frequencies).
+
+    With yarn = (s, L, alpha, beta): the DeepSeek-V2 review page ("4. Pre-Training") extends the
+    context of the decoupled key with YaRN and gives no formula, so the method is taken as
+    published. A pair whose wavelength lambda = 2 pi / theta fits r = L / lambda times into the
+    original context L is interpolated by 1/s if r < alpha, kept if r > beta, and blended linearly
+    in r in between: theta' = (1 - gamma) theta / s + gamma theta."""
+    m = np.arange(n // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * m / n)
+    if yarn is None or yarn[0] <= 1.0:
+        return theta
+    s, L, alpha, beta = (float(v) for v in yarn)
+    wavelength = 2.0 * np.pi / theta
+    turns = L / wavelength
+    gamma = np.clip((turns - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / s + gamma * theta
+
+
+def score_scale(dims):
+    """Softmax scale of the scores: 1/sqrt(d_h + d_h^R) ([Scratch] section 4.4), times YaRN's
+    attention temperature (0.1 ln s + 1)^2 when the extension is on (the published method)."""
+    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    y = getattr(dims, "yarn", None)
+    if y is not None:
+        scale *= (0.1 * np.log(y[0]) + 1.0) ** 2
+    return scale
 
 
 def softmax(z, axis=-1):
@@ -55,17 +99,16 @@ def softmax(z, axis=-1):
     return e / np.sum(e, axis=axis, keepdims=True)
 
 
-def rope(x, pos, base=10000.0):
+def rope(x, pos, base=10000.0, yarn=None):
     """Rotary embedding of the last axis of x (even length) at integer position `pos`.
 
     [Scratch] section 3.1 defines RoPE only as a position-dependent rotation whose query-key dot
     product depends on the position difference; the pair layout and frequencies are the
-    textbook ones (see the module docstring)."""
+    textbook ones (see the module docstring), optionally YaRN-extended (rope_frequencies)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     assert n % 2 == 0
-    m = np.arange(n // 2, dtype=np.float64)
-    theta = np.power(float(base), -2.0 * m / n)
+    theta = rope_frequencies(n, base, yarn)
     ang = float(pos) * theta
     c, s = np.cos(ang), np.sin(ang)
     x0 = x[..., 0::2]
@@ -95,9 +138,9 @@ def new_token(W, h, pos, dims: OracleDims, cdtype):
     computed (float64), and the row as stored (payload, scale) and as read back (float64)."""
     cQ = W["W_dq"] @ h                                         # c^Q = W^DQ h
     qC = (W["W_uq"] @ cQ).reshape(dims.n_h, dims.d_h)          # q^C = W^UQ c^Q, split by head
-    qR = rope((W["W_qr"] @ cQ).reshape(dims.n_h, dims.d_r), pos, dims.rope_base)
+    qR = rope((W["W_qr"] @ cQ).reshape(dims.n_h, dims.d_r), pos, dims.rope_base, dims.yarn)
     cKV = W["W_dkv"] @ h                                       # c^KV = W^DKV h   (cached)
-    kR = rope(W["W_kr"] @ h, pos, dims.rope_base)             # k^R = RoPE(W^KR h) (cached)
+    kR = rope(W["W_kr"] @ h, pos, dims.rope_base, dims.yarn)  # k^R = RoPE(W^KR h) (cached)
     row = np.concatenate([cKV, kR])                            # row layout: latent, then k^R
     payload, scale = store_rows(row[None, :], cdtype)
     read = load_rows(payload, cdtype, scale)[0]
@@ -123,7 +166,7 @@ def decode_step_explicit(W, h, prefix, dims: OracleDims, cdtype, heads=None, wan
     heads = list(range(dims.n_h)) if heads is None else list(heads)
     if want_u:
         assert len(heads) == dims.n_h
-    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    scale = score_scale(dims)
 
     # pass 1: scores s[j, i] = [q^C_i ; q^R_i] . [k^C_{j,i} ; k^R_j] / sqrt(d_h + d_r)
     S = np.empty((T, len(heads)))
@@ -165,7 +208,7 @@ def decode_step_absorbed(W, h, prefix, dims: OracleDims, cdtype):
     rows = np.vstack([prefix, read[None, :]])
     C, KR = rows[:, : dims.d_c], rows[:, dims.d_c:]
     Wuq, Wqr, Wuk, Wuv, Wo = head_slices(W, dims)
-    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    scale = score_scale(dims)
     u = np.zeros(dims.d)
     o_lat = np.zeros((dims.n_h, dims.d_c))
     lse = np.zeros(dims.n_h)
@@ -223,7 +266,7 @@ def decode_step_precombined(W, pre, h, prefix, dims: OracleDims, cdtype):
     cQ = W["W_dq"] @ h
     rows = np.vstack([prefix, read[None, :]])
     C, KR = rows[:, : dims.d_c], rows[:, dims.d_c:]
-    scale = 1.0 / np.sqrt(dims.d_h + dims.d_r)
+    scale = score_scale(dims)
     u = np.zeros(dims.d)
     q_lat = np.zeros((dims.n_h, dims.d_c))
     o_lat = np.zeros((dims.n_h, dims.d_c))

@@ -19,6 +19,11 @@ class Dims:
     d_cq: int     # query latent width (d_c')
     d_r: int      # decoupled rotary width (d_h^R)
     rope_base: float = 10000.0
+    # YaRN extension of the decoupled RoPE (factor <= 1: off); parameters are the caller's
+    yarn_factor: float = 1.0
+    yarn_orig_len: int = 0
+    yarn_alpha: float = 0.0
+    yarn_beta: float = 0.0
 
     @property
     def row(self) -> int:

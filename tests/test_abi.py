@@ -52,7 +52,10 @@ def test_status_strings(L):
 def test_dims_validation(L):
     assert L.mla_rope(None, 1, None, None, None, None, None) == 1
     assert b"dims is NULL" in L.mla_last_error()
-    for bad in (dict(n_h=0), dict(d_r=30), dict(d_c=100), dict(rope_base=1.0), dict(d=-5)):
+    for bad in (dict(n_h=0), dict(d_r=30), dict(d_c=100), dict(rope_base=1.0), dict(d=-5),
+                dict(yarn_factor=40.0, yarn_orig_len=0, yarn_alpha=1.0, yarn_beta=32.0),
+                dict(yarn_factor=40.0, yarn_orig_len=4096, yarn_alpha=32.0, yarn_beta=1.0),
+                dict(yarn_factor=float("nan"))):
         d = _dims(**bad)
         assert L.mla_rope(ctypes.byref(d), 1, FAKE, FAKE, FAKE, None, None) == 1, bad
 

@@ -13,8 +13,8 @@ import pytest
 import torch
 
 from oracle import (OracleDims, cache_counts, decode_step_absorbed, decode_step_explicit, decode_step_precombined,
-                    head_slices, load_rows, precombined_heads, precombined_weights, prefill_chunk, rope, softmax,
-                    store_rows)
+                    head_slices, load_rows, precombined_heads, precombined_weights, prefill_chunk, rope,
+                    rope_frequencies, softmax, store_rows)
 from synth import RUNNING_DIMS, V2_DIMS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -425,3 +425,69 @@ def test_stage_helpers_agree_with_explicit_step():
     m = s.max(0)
     np.testing.assert_allclose(m + np.log(np.exp(s - m).sum(0)), e["lse"], rtol=1e-12)
     np.testing.assert_allclose(output_projection(W, e["o_lat"], dims), e["u"], rtol=1e-11)
+
+
+# ---------------------------------------------------------------- YaRN-extended rotary frequencies
+YARN = (40.0, 4096, 1.0, 32.0)   # factor s, original context L, ramp bounds alpha < beta (turns)
+
+
+def test_yarn_factor_one_is_plain_rope():
+    """s = 1 leaves every frequency (and so every rotation) as plain RoPE."""
+    for n in (32, 64):
+        np.testing.assert_array_equal(rope_frequencies(n, 10000.0, (1.0, 4096, 1.0, 32.0)),
+                                      rope_frequencies(n, 10000.0))
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(64)
+    np.testing.assert_array_equal(rope(x, 1234, 10000.0, (1.0, 4096, 1.0, 32.0)), rope(x, 1234, 10000.0))
+
+
+def test_yarn_interpolates_slow_pairs_and_keeps_fast_ones():
+    """Pairs turning fewer than alpha times over the original context are position-interpolated:
+    their rotation at position s*p equals plain RoPE's at p. Pairs turning more than beta times are
+    untouched. Pairs in between turn at a rate strictly between the two. All three kinds occur at
+    d_r = 64 with L = 4096."""
+    s, L, a, b = YARN
+    n = 64
+    plain = rope_frequencies(n, 10000.0)
+    turns = L * plain / (2 * np.pi)
+    slow, fast = turns < a, turns > b
+    mid = ~slow & ~fast
+    assert slow.any() and fast.any() and mid.any()
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(n)
+    for p in (0, 3, 517, 4000):
+        y_ext = rope(x, s * p, 10000.0, YARN)
+        y_pln = rope(x, p, 10000.0)
+        y_now = rope(x, p, 10000.0, YARN)
+        for m in np.nonzero(slow)[0]:
+            np.testing.assert_allclose(y_ext[2 * m:2 * m + 2], y_pln[2 * m:2 * m + 2], rtol=1e-9, atol=1e-9)
+        for m in np.nonzero(fast)[0]:
+            np.testing.assert_allclose(y_now[2 * m:2 * m + 2], y_pln[2 * m:2 * m + 2], rtol=1e-12, atol=1e-12)
+    ext = rope_frequencies(n, 10000.0, YARN)
+    assert np.all(ext[mid] < plain[mid]) and np.all(ext[mid] > plain[mid] / s)
+
+
+def test_yarn_keeps_relative_position_property():
+    """Scores after the extension still depend only on the offset between query and key."""
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for t, j, delta in ((10, 3, 1000), (4095, 17, 60000), (5, 5, 131000)):
+        lhs = rope(q, t, 10000.0, YARN) @ rope(k, j, 10000.0, YARN)
+        rhs = rope(q, t + delta, 10000.0, YARN) @ rope(k, j + delta, 10000.0, YARN)
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+
+
+def test_yarn_explicit_equals_absorbed():
+    """Both formulations agree with the extension on (frequencies and score scale shared)."""
+    from dataclasses import replace
+    dims = replace(OracleDims.of(V2_DIMS), yarn_factor=YARN[0], yarn_orig_len=YARN[1], yarn_alpha=YARN[2],
+                   yarn_beta=YARN[3])
+    rng = np.random.default_rng(10)
+    W = _rand_weights(dims, rng, sw=1.0 / math.sqrt(dims.d), kappa=3.0)
+    h = rng.standard_normal(dims.d)
+    stored, sc = store_rows(rng.standard_normal((6, dims.d_c + dims.d_r)), "bf16")
+    prefix = load_rows(stored, "bf16", sc)
+    e = decode_step_explicit(W, h, prefix, dims, "bf16")
+    a = decode_step_absorbed(W, h, prefix, dims, "bf16")
+    for key in ("u", "o_lat", "lse"):
+        assert np.linalg.norm(e[key] - a[key]) / np.linalg.norm(a[key]) < 1e-10, key
