@@ -128,14 +128,16 @@ __device__ __forceinline__ int range_for_block(int bid, int G) {
 
 
 // ================================================================================================
-// MFMA kernel for the DeepSeek-V2 shape: n_h = 128, d_c = 512, d_r = 64 (row = 576).
-// One workgroup = 4 waves; wave w owns heads [32w, 32w + 32). All heads share each latent tile,
-// staged once in LDS. Per 32-token tile and wave:
-//   S^T[32 tok x 32 heads] = K[32 x 576] Q^T            (36 MFMA 32x32x16, K rows via ds_read_b128)
-//   online softmax in float32 (base-2, scale folded into Q)
-//   O^T[512 x 32 heads] += V^T[512 x 32 tok] P^T        (32 MFMA, V^T via ds_read_b64_tr_b16)
-// The S^T accumulator layout (lane: head, registers: tokens) is exactly the B-operand layout of
-// the P^T product, so probabilities never leave registers.
+// MFMA kernels for the DeepSeek-V2 shape: n_h = 128, d_c = 512, d_r = 64 (row = 576). One
+// workgroup = 4 waves; all heads share each latent tile, staged once in LDS as bf16 rows. Per
+// 32-token tile:
+//   S^T[32 tok x 32 heads] = K[32 x 576] Q^T for wave w's heads [32w, 32w + 32)
+//       (36 MFMA 32x32x16, K rows via ds_read_b128; Q in registers, scale folded in)
+//   softmax in float32 (base 2) against a fixed per-head reference
+//   O^T[128 columns of wave w x 128 heads] += V^T P^T (32 MFMA, V^T via ds_read_b64_tr_b16,
+//       P of all heads through LDS)
+// This section holds the shared pieces and the fp8 e4m3 kernel (codes widened to bf16 on their
+// way into LDS); the bf16 kernel below pipelines the same steps.
 namespace v2 {
 constexpr int NH = 128, DC = 512, DR = 64, RW = 576;
 constexpr int TT = 32;                     // tokens per tile
@@ -261,8 +263,8 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
   return s;
 }
 
-template <int CDT, bool PAGED>
-__global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ q_lat,
+template <bool PAGED>
+__global__ __launch_bounds__(256, 1) void k_decode_fp8(const float* __restrict__ q_lat,
                                                       const float* __restrict__ q_pe, CacheArgs cache,
                                                       const int32_t* __restrict__ seq_lens, int B, int G,
                                                       int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
@@ -270,15 +272,14 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
   using namespace v2;
-  constexpr bool FP8 = CDT == MLA_FP8_E4M3;
-  constexpr int NBUF = FP8 ? 2 : 4;  // bf16: three tiles (108 KB) in flight behind the one in use
+  constexpr int NBUF = 2;  // the tile in use and the next one (converted from registers)
   // Softmax reference: per head, the maximum of the segment's first tile. Later probabilities are
   // exp2(s - m_ref) <= 2^HEAD (fine in float32/bf16), so the accumulators are never rescaled. A
   // score above m_ref + HEAD makes the workgroup run the segment once more with the segment's
   // true maximum as the reference (exact; at most one re-run).
   constexpr float HEAD = 64.f;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
-  __shared__ float lds_sc[FP8 ? NBUF : 1][TT];
+  __shared__ float lds_sc[NBUF][TT];
   __shared__ __attribute__((aligned(16))) uint8_t lds_p[NH * TT * 2];  // P of the current tile, [head][token]
   __shared__ float lds_l[NH];                                           // softmax denominators
   __shared__ float lds_m[4][NH];                                        // per-wave max |O| per head
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int f = i * 256 + tid, t = f / CHUNKS;
-    const uint32_t o = (uint32_t)(t * (FP8 ? RW : ROWB) + (swz(t, f - t * CHUNKS) << (FP8 ? 3 : 4)));
+    const uint32_t o = (uint32_t)(t * RW + (swz(t, f - t * CHUNKS) << 3));
     doff2[i >> 1] |= o << (16 * (i & 1));
   }
   auto doff = [&](int i) -> uint32_t { return (doff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
@@ -352,54 +353,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
 
     const int64_t n = t1 - t0;
     const int ntiles = (int)((n + TT - 1) / TT);
-    // bf16: 16-byte chunks go straight from HBM into LDS (tile it -> buffer it % NBUF).
     const uint8_t* rows_b = (const uint8_t*)cache.rows;
-    auto issue = [&](int it) {
-      const int64_t tt0 = t0 + (int64_t)it * TT;
-      const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB + w * 1024));
-      // the packed offsets are re-read through an opaque copy at every call, so the compiler
-      // neither precomputes per-call offset sets (which it would have to spill) nor hoists them
-      uint32_t d2[(LOADS + 1) / 2];
-#pragma unroll
-      for (int i = 0; i < (LOADS + 1) / 2; ++i) {
-        d2[i] = doff2[i];
-        asm volatile("" : "+v"(d2[i]));
-      }
-      uint32_t off[LOADS];
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        off[i] = (d2[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-        if (last < TT - 1) {  // partial tile: rows past the segment re-read its last row
-          const int t = (int)(off[i] / ROWB);
-          if (t > last) off[i] -= (uint32_t)(t - last) * ROWB;
-        }
-      }
-      if constexpr (!PAGED) {
-        const uint8_t* base = rows_b + (rows.base_row + tt0) * ROWB;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) dma16_s(base, off[i], dst + i * 4096);
-      } else {
-        // a 32-row tile spans at most two pages: rows before `split` live in the first one
-        rows.tile(tt0, tt0 + last);
-        const int ps = 1 << rows.ps_shift;
-        const int s_in = (int)(tt0 & (ps - 1));
-        const uint32_t split = (uint32_t)(ps - s_in) * ROWB;
-        const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * ROWB;
-        const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * ROWB - (int64_t)split;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) dma16((off[i] < split ? B0 : B1) + off[i], dst + i * 4096);
-      }
-    };
-    // the first three tiles are requested before the query is read, so both latencies overlap
-    auto prime = [&]() {
-      if constexpr (!FP8) {
-#pragma unroll 1
-        for (int it = 0; it < 3 && it < ntiles; ++it) issue(it);
-      }
-    };
-    prime();
 
     // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
     bf16x8 qf[KSTEPS];
@@ -441,10 +395,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         f32x16 s = tile_scores(tile, kq, qf);
         // register r holds token 8(r/4) + 4g + r%4 of the tile; lane holds head `head`
         float mx = -__builtin_inff();
-        if constexpr (FP8) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
-        }
+        for (int r = 0; r < 16; ++r) s[r] *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
         if (valid < TT) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -464,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         for (int r = 0; r < 16; ++r) {
           float e = __builtin_amdgcn_exp2f(fminf(s[r] - m_ref, HEAD));
           rs += e;
-          if constexpr (FP8) e *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
+          e *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
           if (r < 8) pk0[r] = (__bf16)e; else pk1[r - 8] = (__bf16)e;
         }
         rs += __shfl_xor(rs, 32, 64);
@@ -536,17 +488,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
         }
       };
 
-    if constexpr (!FP8) {
-        if (pass > 0) prime();
-        for (int it = 0; it < ntiles; ++it) {
-          if (it + 2 < ntiles) vm_wait_barrier<2 * LOADS>();
-          else if (it + 1 < ntiles) vm_wait_barrier<LOADS>();
-          else vm_wait_barrier<0>();
-          if (it + 3 < ntiles) issue(it + 3);
-          compute(lds + (it % NBUF) * TILEB, nullptr, valid_of(it));
-        }
-      } else {
-        // fp8: codes widened to bf16 in registers on the way into LDS; scales per token.
+      {
+        // codes widened to bf16 in registers on the way into LDS; scales per token.
         u32x2 r8[LOADS];
         float scv = 0.f;
         // Row chunks of tile it: a uniform base plus the packed 32-bit per-lane offsets (rows
@@ -677,8 +620,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_v2(const float* __restrict__ 
 }
 
 // ================================================================================================
-// MFMA kernel for bf16 caches at the DeepSeek-V2 shape. Same work split, tile staging, LDS
-// layout and fragment layouts as the kernel above, with the memory traffic spread over the math:
+// MFMA kernel for bf16 caches at the DeepSeek-V2 shape. Same work split, LDS tile layout and
+// fragment layouts as the kernel above; tiles go straight from HBM into LDS (global->LDS copies),
+// and the memory traffic is spread over the math:
 // per iteration `it` (tiles it+1.. it+3 in flight),
 //   scores of tile it (36 MFMAs) with the nine copies of tile it+3 slotted between them, so the
 //   four waves do not all queue 36 KB of copies at the same instant,
@@ -1575,15 +1519,15 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   const float qscale = sm_scale * 1.44269504088896340736f;  // log2(e)
   if (mfma) {
     const bool paged = c.page_size > 0;
-#define MLA_V2(CDT, PG) \
-    hipLaunchKernelGGL((k_decode_v2<CDT, PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
+#define MLA_FP8(PG) \
+    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
 #define MLA_V3(PG) \
     hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
     if (c.dtype == MLA_BF16) { if (paged) MLA_V3(true); else MLA_V3(false); }
-    else { if (paged) MLA_V2(MLA_FP8_E4M3, true); else MLA_V2(MLA_FP8_E4M3, false); }
-#undef MLA_V2
+    else { if (paged) MLA_FP8(true); else MLA_FP8(false); }
+#undef MLA_FP8
 #undef MLA_V3
   } else {
     const int rw = d.d_c + d.d_r;
