@@ -1208,18 +1208,28 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
         ss[i] = t < valid ? (a4[0] + a4[1]) + (a4[2] + a4[3]) : -__builtin_inff();
       }
       lds_barrier();
-      for (int h = w; h < n_h; h += 4) {
-        float v = lane < TT ? ss[h * TT + lane] : -__builtin_inff();
-        float mx = wave_max(v);
-        float m_new = fmaxf(mrun[h], mx);
-        float e = exp2f(v - m_new);
-        float sum = wave_sum(e);
-        if (lane < TT) ss[h * TT + lane] = e;
-        if (lane == 0) {
-          float a = exp2f(mrun[h] - m_new);
-          alf[h] = a;
-          lrun[h] = lrun[h] * a + sum;
-          mrun[h] = m_new;
+      // online softmax: each half-wave takes one head (32 lanes = the tile's 32 tokens), so a
+      // round covers 8 heads with 5-step reductions
+      for (int h0 = 0; h0 < n_h; h0 += 8) {
+        const int h = h0 + 2 * w + (lane >> 5), t = lane & 31;
+        if (h < n_h) {
+          const float v = ss[h * TT + t];
+          float mx = v;
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+          const float m_old = mrun[h];
+          const float m_new = fmaxf(m_old, mx);
+          const float e = exp2f(v - m_new);
+          float sum = e;
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+          ss[h * TT + t] = e;
+          if (t == 0) {
+            const float a = exp2f(m_old - m_new);
+            alf[h] = a;
+            lrun[h] = lrun[h] * a + sum;
+            mrun[h] = m_new;
+          }
         }
       }
       lds_barrier();
