@@ -166,7 +166,9 @@ MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_
  * a relative rounding of at most 2^-11 per element, below the bf16 rounding of the operands.
  *   q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] (rotated): float32.
  *   seq_lens: device int32 [B] (including the current token, already appended).
- *   workspace: at least mla_decode_workspace_bytes(dims, B, num_splits) bytes. */
+ *   workspace: at least mla_decode_workspace_bytes(dims, B, num_splits) bytes. At the MFMA
+ *   shape it also holds the query in the fp8 kernel's form (per head: scaled by a power of two
+ *   and split into two e4m3 parts), written by this call before the attention kernel reads it. */
 MLA_API size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t num_splits);
 MLA_API mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, const float* q_pe,
                            const mla_cache* cache, const int32_t* seq_lens, int32_t num_splits,

@@ -27,6 +27,14 @@ DecodeLayout decode_layout(const mla_dims& d, int B, int G) {
   L.off_sc = al256(L.off_lse + (size_t)L.n_pieces * d.n_h * 4);
   L.off_o = al256(L.off_sc + (size_t)L.n_pieces * d.n_h * 4);
   L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;  // sized for float32 partials
+  // MFMA shape: the query in the fp8 kernel's form (two e4m3 parts per element, 1152 bytes per
+  // head) and its per-head power-of-two factor
+  L.off_q8 = L.off_fh = 0;
+  if (d.n_h == 128 && d.d_c == 512 && d.d_r == 64) {
+    L.off_q8 = al256(L.bytes);
+    L.off_fh = al256(L.off_q8 + (size_t)B * d.n_h * 1152);
+    L.bytes = L.off_fh + (size_t)B * d.n_h * 4;
+  }
   return L;
 }
 
@@ -129,15 +137,18 @@ __device__ __forceinline__ int range_for_block(int bid, int G) {
 
 // ================================================================================================
 // MFMA kernels for the DeepSeek-V2 shape: n_h = 128, d_c = 512, d_r = 64 (row = 576). One
-// workgroup = 4 waves; all heads share each latent tile, staged once in LDS as bf16 rows. Per
-// 32-token tile:
+// workgroup = 4 waves; all heads share each latent tile, staged once in LDS. Per 32-token tile:
 //   S^T[32 tok x 32 heads] = K[32 x 576] Q^T for wave w's heads [32w, 32w + 32)
-//       (36 MFMA 32x32x16, K rows via ds_read_b128; Q in registers, scale folded in)
+//       (K rows read from LDS; Q in registers, scale folded in)
 //   softmax in float32 (base 2) against a fixed per-head reference
-//   O^T[128 columns of wave w x 128 heads] += V^T P^T (32 MFMA, V^T via ds_read_b64_tr_b16,
-//       P of all heads through LDS)
-// This section holds the shared pieces and the fp8 e4m3 kernel (codes widened to bf16 on their
-// way into LDS); the bf16 kernel below pipelines the same steps.
+//   O^T[128 columns of wave w x 128 heads] += V^T P^T (32 MFMA 32x32x16 bf16, V^T via
+//       transposing LDS reads, P of all heads through LDS)
+// Softmax reference: per head, the maximum of the segment's first tile. Later probabilities are
+// exp2(s - m_ref), so the accumulators are never rescaled; a score more than HEAD (64) above
+// m_ref makes the workgroup run the segment once more with a reference at (or just above) the
+// segment's true maximum (exact; at most one re-run).
+// This section holds the shared pieces; the bf16 kernel (rows as bf16 in LDS) and the fp8 kernel
+// (rows as e4m3 codes in LDS) follow.
 namespace v2 {
 constexpr int NH = 128, DC = 512, DR = 64, RW = 576;
 constexpr int TT = 32;                     // tokens per tile
@@ -263,373 +274,17 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
   return s;
 }
 
-template <bool PAGED>
-__global__ __launch_bounds__(256, 1) void k_decode_fp8(const float* __restrict__ q_lat,
-                                                      const float* __restrict__ q_pe, CacheArgs cache,
-                                                      const int32_t* __restrict__ seq_lens, int B, int G,
-                                                      int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
-                                                      float qscale, float* __restrict__ lse_part,
-                                                      float* __restrict__ sc_part,
-                                                      uint16_t* __restrict__ o_part) {
-  using namespace v2;
-  constexpr int NBUF = 2;  // the tile in use and the next one (converted from registers)
-  // Softmax reference: per head, the maximum of the segment's first tile. Later probabilities are
-  // exp2(s - m_ref) <= 2^HEAD (fine in float32/bf16), so the accumulators are never rescaled. A
-  // score above m_ref + HEAD makes the workgroup run the segment once more with the segment's
-  // true maximum as the reference (exact; at most one re-run).
-  constexpr float HEAD = 64.f;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * TILEB];
-  __shared__ float lds_sc[NBUF][TT];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_p[NH * TT * 2];  // P of the current tile, [head][token]
-  __shared__ float lds_l[NH];                                           // softmax denominators
-  __shared__ float lds_m[4][NH];                                        // per-wave max |O| per head
-  __shared__ int redo_flag;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int p = range_for_block(blockIdx.x, G);
-  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 2, cu_out, fmt_out, lane);
-  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
-  int64_t start = rp.start;
-  const int64_t end = rp.end;
-  if (start >= end) return;
-  int b = rp.b;
-  int64_t s0 = rp.s0, s1 = rp.s1;
-  const int head = 32 * w + l32;
-
-  // Per-lane LDS byte offsets inside a tile. The swizzle only permutes the low 3 bits of a chunk
-  // index, so every read is one of a few per-lane bases plus a compile-time immediate.
-  //  K rows (scores): chunk c = 2ks + g of row l32 -> base kq[ks & 3] + 128 * (ks >> 2)
-  uint32_t kq[4];
-  {
-    const int kx = swz_key(l32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kq[j] = l32 * ROWB + (((2 * j + g) ^ kx) << 4);
-  }
-  //  V^T (transposed reads): rows ta = 16kk + 4g + j16/4 and ta + 8, chunk 4cb + cst
-  //  -> base vq[kk][row a/b][cb & 1] + 128 * (cb >> 1)
-  uint32_t vq[2][2][2];
-  {
-    const int j16 = lane & 15, h2 = (lane >> 4) & 1;
-    const int cst = 2 * h2 + ((j16 & 3) >> 1);
-    const int sub = (j16 & 1) * 8;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int ab = 0; ab < 2; ++ab) {
-        const int t = 16 * kk + 4 * g + (j16 >> 2) + 8 * ab;
-        const int key = swz_key(t);
-#pragma unroll
-        for (int par = 0; par < 2; ++par) vq[kk][ab][par] = t * ROWB + sub + (((4 * par + cst) ^ key) << 4);
-      }
-  }
-
-  // Tile staging: thread tid copies chunks f = 256 i + tid (i < 9) of the tile; chunk f is LDS
-  // bytes [16 f, 16 f + 16) = row f / 72, swizzled position f % 72. doff[i] is the byte offset of
-  // its source inside the tile's rows (row * row_bytes + source chunk * chunk_bytes).
-  // Offsets are < 2^16, so they are kept packed two per register.
-  uint32_t doff2[(LOADS + 1) / 2];
-#pragma unroll
-  for (int i = 0; i < (LOADS + 1) / 2; ++i) doff2[i] = 0;
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int f = i * 256 + tid, t = f / CHUNKS;
-    const uint32_t o = (uint32_t)(t * RW + (swz(t, f - t * CHUNKS) << 3));
-    doff2[i >> 1] |= o << (16 * (i & 1));
-  }
-  auto doff = [&](int i) -> uint32_t { return (doff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
-
-  while (start < end) {
-    if (s1 <= start) {  // an empty sequence: move on
-      ++b;
-      s0 = s1;
-      s1 = s0 + seq_lens[b];
-      continue;
-    }
-    const int64_t seg_end = end < s1 ? end : s1;
-    const int64_t t0 = start - s0, t1 = seg_end - s0;
-    const int64_t slot = (int64_t)p + b;
-    Rows<PAGED> rows;
-    rows.init(cache, b);
-
-    const int64_t n = t1 - t0;
-    const int ntiles = (int)((n + TT - 1) / TT);
-    const uint8_t* rows_b = (const uint8_t*)cache.rows;
-
-    // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
-    bf16x8 qf[KSTEPS];
-    {
-      const float* ql = q_lat + ((int64_t)b * NH + head) * DC;
-      const float* qp = q_pe + ((int64_t)b * NH + head) * DR;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int f0 = 16 * ks + 8 * g;
-        const float* src = f0 < DC ? ql + f0 : qp + (f0 - DC);
-        f32x4 a = *(const f32x4*)src, c = *(const f32x4*)(src + 4);
-        bf16x8 v;
-        v[0] = (__bf16)(a[0] * qscale); v[1] = (__bf16)(a[1] * qscale);
-        v[2] = (__bf16)(a[2] * qscale); v[3] = (__bf16)(a[3] * qscale);
-        v[4] = (__bf16)(c[0] * qscale); v[5] = (__bf16)(c[1] * qscale);
-        v[6] = (__bf16)(c[2] * qscale); v[7] = (__bf16)(c[3] * qscale);
-        qf[ks] = v;
-      }
-    }
-
-    auto valid_of = [&](int it) -> int {
-      const int64_t r = n - (int64_t)it * TT;
-      return r < TT ? (int)r : TT;
-    };
-
-    f32x16 O[CB];
-    float m_ref = -__builtin_inff(), m_seg = -__builtin_inff(), l_run = 0.f;
-    bool have_ref = false;
-
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) O[cb] = f32x16{};
-      l_run = 0.f;
-      if (tid == 0) redo_flag = 0;
-      bool over = false;
-
-      // ---- one tile: scores, probabilities against the reference, weighted latent sum
-      auto compute = [&](const uint8_t* tile, const float* sc, int valid) __attribute__((always_inline)) {
-        f32x16 s = tile_scores(tile, kq, qf);
-        // register r holds token 8(r/4) + 4g + r%4 of the tile; lane holds head `head`
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
-        if (valid < TT) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tk = 8 * (r >> 2) + 4 * g + (r & 3);
-            s[r] = tk < valid ? s[r] : -__builtin_inff();
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (!have_ref) { m_ref = mx; have_ref = true; }
-        m_seg = fmaxf(m_seg, mx);
-        over |= mx > m_ref + HEAD;
-        float rs = 0.f;
-        bf16x8 pk0, pk1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(fminf(s[r] - m_ref, HEAD));
-          rs += e;
-          e *= sc[8 * (r >> 2) + 4 * g + (r & 3)];
-          if (r < 8) pk0[r] = (__bf16)e; else pk1[r - 8] = (__bf16)e;
-        }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run += rs;
-        // Publish P: head row `head` of lds_p holds the tile's 32 probabilities as four 16-byte
-        // chunks; chunk 2kk + g is this lane's pk<kk> (tokens 16kk + 8(j/4) + 4g + j%4 for slot
-        // j), stored at chunk position (2kk + g) ^ ((head / 4) % 4) (conflict-free reads below).
-        {
-          const int key = (head >> 2) & 3;
-          uint8_t* prow = lds_p + head * 64;
-          *(bf16x8*)(prow + ((g ^ key) << 4)) = pk0;
-          *(bf16x8*)(prow + (((2 + g) ^ key) << 4)) = pk1;
-        }
-        __syncthreads();
-        // O^T[128 columns of this wave x 128 heads] += V^T P^T: 32 MFMAs ordered (kk, hb, cb).
-        // A = V^T fragment of columns 128w + 32cb (two transposing LDS reads; the four of one kk
-        // are live together), B = P fragment of heads 32hb.. (one LDS read, one MFMA group
-        // ahead). O stays in AGPRs. Loads are placed in program order around the volatile MFMAs.
-        uint32_t vb[2][2][2];
-        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 256u * w;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-            for (int par = 0; par < 2; ++par) {
-              vb[kk][ab][par] = tb + vq[kk][ab][par];
-              asm volatile("" : "+v"(vb[kk][ab][par]));
-            }
-        auto ldv = [&](int kk, int cb) __attribute__((always_inline)) -> u32x4 {
-          const uint32_t ia = vb[kk][0][cb & 1] + 128u * (cb >> 1);
-          const uint32_t ib = vb[kk][1][cb & 1] + 128u * (cb >> 1);
-          const u32x2 x0 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ia));
-          const u32x2 x1 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)ib));
-          return u32x4{x0.x, x0.y, x1.x, x1.y};
-        };
-        auto ldp = [&](int kk, int hb) __attribute__((always_inline)) -> bf16x8 {
-          const int hr = 32 * hb + l32;
-          return *(const bf16x8*)(lds_p + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
-        };
-        u32x4 av[4];
-        bf16x8 pbc, pbn;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) av[cb] = ldv(0, cb);
-        pbc = ldp(0, 0);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) {
-            const bool last_group = kk == 1 && hb == 3;
-            if (!last_group) pbn = ldp(hb == 3 ? kk + 1 : kk, hb == 3 ? 0 : hb + 1);
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-              if (last_group && cb == 3) {
-                // the last MFMA is followed by 24 wait states so any later read of O is safe
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
-              } else {
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
-              }
-              // the next kk's A fragment replaces this one after its last use
-              if (kk == 0 && hb == 3) av[cb] = ldv(1, cb);
-            }
-            pbc = pbn;
-          }
-        }
-      };
-
-      {
-        // codes widened to bf16 in registers on the way into LDS; scales per token.
-        u32x2 r8[LOADS];
-        float scv = 0.f;
-        // Row chunks of tile it: a uniform base plus the packed 32-bit per-lane offsets (rows
-        // past the segment re-read its last row); no per-chunk 64-bit addresses are kept, so
-        // nothing spills and the loads stay in flight until store() needs them.
-        auto load = [&](int it) {
-          const int64_t tt0 = t0 + (int64_t)it * TT;
-          const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
-          uint32_t off[LOADS];
-#pragma unroll
-          for (int i = 0; i < LOADS; ++i) {
-            uint32_t d2 = doff2[i >> 1];
-            asm volatile("" : "+v"(d2));
-            off[i] = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
-            if (last < TT - 1) {
-              const int t = (int)(off[i] / RW);
-              if (t > last) off[i] -= (uint32_t)(t - last) * RW;
-            }
-          }
-          // page ids of the tile (scalar loads) before anything that locates rows
-          if constexpr (PAGED) rows.tile(tt0, tt0 + last);
-          // the token scale first: a wait for it (in issue order) then leaves the chunks in flight.
-          // The lane offset is made opaque so that the compiler keeps no loop-carried 64-bit
-          // per-lane token counter (it spilled one, and its reload drained the chunk loads).
-          if (tid < TT) {
-            int dt = tid < last ? tid : last;
-            asm volatile("" : "+v"(dt));
-            scv = cache.scales[rows.row(tt0 + dt)];
-          }
-          if constexpr (!PAGED) {
-            const uint8_t* base = rows_b + (rows.base_row + tt0) * RW;
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) r8[i] = *(const u32x2*)(base + off[i]);
-          } else {
-            // a 32-row tile spans at most two pages: rows before `split` live in the first one
-            const int ps = 1 << rows.ps_shift;
-            const int s_in = (int)(tt0 & (ps - 1));
-            const uint32_t split = (uint32_t)(ps - s_in) * RW;
-            const uint8_t* B0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * RW;
-            const uint8_t* B1 = rows_b + (int64_t)rows.pg1 * ps * RW - (int64_t)split;
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) r8[i] = *(const u32x2*)((off[i] < split ? B0 : B1) + off[i]);
-          }
-        };
-        auto store = [&](int it) {
-          uint8_t* dst = lds + (it % NBUF) * TILEB;
-#pragma unroll
-          for (int i = 0; i < LOADS; ++i) {
-            // OCP e4m3 -> bf16 is exact; the hardware pair conversion (scale 1: the per-token
-            // scale is applied to the scores and probabilities instead) takes the codes of
-            // one 16-bit half, low byte first
-            u32x4 o;
-            const uint32_t lo = r8[i].x, hi = r8[i].y;
-            o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-            o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-            o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-            o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-            *(u32x4*)(dst + (size_t)(i * 256 + tid) * 16) = o;
-          }
-          if (tid < TT) lds_sc[it % NBUF][tid] = scv;
-        };
-        __syncthreads();
-        load(0);
-        store(0);
-        if (ntiles > 1) load(1);
-        __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-          compute(lds + (it % NBUF) * TILEB, lds_sc[it % NBUF], valid_of(it));
-          if (it + 1 < ntiles) store(it + 1);
-          if (it + 2 < ntiles) load(it + 2);
-          __syncthreads();
-        }
-      }
-      // does any head of the workgroup need the second pass?
-      if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) redo_flag = 1;
-      __syncthreads();
-      const int redo = redo_flag;
-      __syncthreads();
-      if (!redo) break;
-      m_ref = m_seg;  // exact maximum of the segment for every head of every wave
-    }
-
-    // ---- normalised partial and its log-sum-exp (natural log). The partial row of a head is a
-    // convex combination of cached rows; it is stored as float16 after scaling by a power of
-    // two 2^-e that brings its largest magnitude into [0.5, 1); 2^e goes to the scale array.
-    if (g == 0) lds_l[head] = l_run;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      float m = 0.f;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(O[4 * cb + hb][r]));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      if (g == 0) lds_m[w][32 * hb + l32] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      const int hr = 32 * hb + l32;
-      const float inv_l = 1.f / lds_l[hr];
-      const float mx = fmaxf(fmaxf(lds_m[0][hr], lds_m[1][hr]), fmaxf(lds_m[2][hr], lds_m[3][hr])) * inv_l;
-      int e = 0;
-      if (mx > 0.f) (void)frexpf(mx, &e);
-      const float f = ldexpf(inv_l, -e);
-      uint16_t* dst = o_part + (slot * NH + hr) * DC + 128 * w;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x16& o = O[4 * cb + hb];
-          const u32x2 v = {pack_f16x2(o[4 * r4 + 0] * f, o[4 * r4 + 1] * f),
-                           pack_f16x2(o[4 * r4 + 2] * f, o[4 * r4 + 3] * f)};
-          *(u32x2*)(dst + 32 * cb + 8 * r4 + 4 * g) = v;
-        }
-      if (w == 0 && g == 0) sc_part[slot * NH + hr] = ldexpf(1.f, e);
-    }
-    if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
-    __syncthreads();  // lds_l / lds_m are reused by the next segment
-
-    start = seg_end;
-    if (start < end) {
-      ++b;
-      s0 = s1;
-      s1 = s0 + seq_lens[b];
-    }
-  }
-}
-
 // ================================================================================================
-// MFMA kernel for bf16 caches at the DeepSeek-V2 shape. Same work split, LDS tile layout and
-// fragment layouts as the kernel above; tiles go straight from HBM into LDS (global->LDS copies),
-// and the memory traffic is spread over the math:
+// MFMA kernel for bf16 caches at the DeepSeek-V2 shape: 36 MFMA 32x32x16 per tile for the
+// scores (K rows via ds_read_b128), V^T via ds_read_b64_tr_b16. Tiles go straight from HBM into
+// LDS (global->LDS copies), and the memory traffic is spread over the math:
 // per iteration `it` (tiles it+1.. it+3 in flight),
 //   scores of tile it (36 MFMAs) with the nine copies of tile it+3 slotted between them, so the
 //   four waves do not all queue 36 KB of copies at the same instant,
 //   softmax of tile it; P published to LDS; barrier,
 //   O^T[128 columns of wave w x 128 heads] += V^T P^T (32 MFMAs, P of all heads from LDS).
 // The softmax keeps per-lane (half-head) maxima and sums: no cross-lane traffic per tile; the
-// two halves of a head are joined once per segment. Reference maximum as in the kernel above.
+// two halves of a head are joined once per segment.
 namespace v3 {
 constexpr int NBUF = 4;
 }
@@ -1054,6 +709,603 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
     }
     if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
     __syncthreads();  // lds_l / lds_m and the staging rows are reused by the next segment
+
+    start = seg_end;
+    if (start < end) {
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+    }
+  }
+}
+
+// ================================================================================================
+// MFMA kernel for fp8 e4m3 caches at the DeepSeek-V2 shape. Rows stay fp8 in LDS, so a tile is
+// half the bytes of a bf16 tile both in HBM and in LDS. Work split, pipeline (one barrier per
+// tile, P double-buffered, copies slotted between the score MFMAs), softmax reference and
+// epilogue are those of the bf16 kernel above; what differs:
+//   scores: fp8 MFMA 32x32x64 straight on the codes. The query of each head is scaled by a power
+//     of two 2^e_h (its largest element lands in [128, 256)) and split into two e4m3 parts
+//     q = q_hi + q_lo (about 8 significant bits, like bf16); S = K q_hi + K q_lo is two MFMAs per
+//     64-wide k block, and the true score is S * scale_token * 2^-e_h.
+//   PV: V^T fragments come from transposing 8-bit LDS reads (8 tokens of one column per lane),
+//     widened to bf16 in registers; the token scale is folded into P (P = p * scale_token).
+//   tiles: 32 rows of 576 bytes plus the 32 token scales, copied straight into LDS; a 7-buffer
+//     ring keeps up to 5 tiles in flight.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+namespace f8 {
+constexpr int RB = 576;                    // bytes of one fp8 row
+constexpr int CH = RB / 16;                // 16-byte chunks per row (36)
+constexpr int ROWSB = v2::TT * RB;         // 18432
+constexpr int SCB = 512;                   // two 256-byte token-scale slots
+constexpr int TILEB = ROWSB + SCB;         // 18944
+constexpr int NBUF = 7;
+constexpr int AHEAD = NBUF - 2;            // tiles in flight besides the two being computed on
+constexpr int LOADS = 5;                   // copy instructions per wave per tile
+constexpr int KB = RB / 64;                // 64-wide k blocks (9)
+constexpr int PB = v2::NH * v2::TT * 2;    // bytes of P of one tile
+constexpr int LDS_BYTES = NBUF * TILEB + 2 * PB;
+}  // namespace f8
+
+// 16-byte chunk c of fp8 tile row t sits at chunk position (c & ~3) | ((c & 3) ^ key8(t)) (rows of
+// 36 chunks, so the XOR stays inside the aligned group of 4). With rows 576 bytes apart, row t
+// starts at bank group 4t mod 16; the key separates rows t, t+4, t+8, t+12, so the 16 rows of a
+// 16-lane score read and the 8 rows x 2 chunks of a 32-lane transposing read hit distinct groups.
+__device__ __forceinline__ int key8(int t) { return (t >> 2) & 3; }
+
+// 4-byte global -> LDS copy per lane (LDS destination: wave-uniform `lds_addr` + 4 * lane).
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+// Scores of one fp8 tile: S^T[32 tok x 32 heads] over the 9 k blocks, two MFMAs per block (q_hi,
+// q_lo). K fragment of block kb: 32 bytes of row l32 at k = 32g.. (chunks 4kb + 2g, 4kb + 2g + 1),
+// read LA blocks ahead. between(j) runs after MFMA j (0..17). The leading s_nop covers a VALU
+// write of the query registers right before; the trailing ones the MFMA-result -> VALU-read wait.
+template <typename F>
+__device__ __forceinline__ f32x16 tile_scores8(const uint8_t* tile, const uint32_t (&kq)[2],
+                                               const i32x8 (&qh)[f8::KB], const i32x8 (&ql)[f8::KB],
+                                               F&& between) {
+  constexpr int KB = f8::KB, LA = 2;
+  i32x8 a[KB];
+  auto lda = [&](int kb) __attribute__((always_inline)) -> i32x8 {
+    const u32x4 x = *(const u32x4*)(tile + kq[0] + 64 * kb);
+    const u32x4 y = *(const u32x4*)(tile + kq[1] + 64 * kb);
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
+#pragma unroll
+  for (int j = 0; j < LA; ++j) a[j] = lda(j);
+  f32x16 s;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=v"(s) : "v"(a[0]), "v"(qh[0]));
+  between(0);
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a[0]), "v"(ql[0]));
+  between(1);
+  a[LA] = lda(LA);
+#pragma unroll
+  for (int kb = 1; kb < KB; ++kb) {
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a[kb]), "v"(qh[kb]));
+    between(2 * kb);
+    if (kb == KB - 1) {
+      asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+v"(s) : "v"(a[kb]), "v"(ql[kb]));
+    } else {
+      asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a[kb]), "v"(ql[kb]));
+    }
+    between(2 * kb + 1);
+    if (kb + LA < KB) a[kb + LA] = lda(kb + LA);
+  }
+  return s;
+}
+
+// 8 e4m3 codes -> 8 bf16 (exact); the hardware pair conversion takes the codes of one 16-bit half
+__device__ __forceinline__ bf16x8 widen8(u32x2 r) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The query of every (sequence, head) in the fp8 kernel's form, once per call instead of once per
+// workgroup: x = q * sm_scale * log2(e) * 2^e_h with the head's largest |x| in [128, 256), split
+// into e4m3 parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi), both exact-range). Layout per head:
+// [k block (9)][g (2)][hi 32 bytes | lo 32 bytes], i.e. the B-operand bytes of lane half g; the
+// head's 2^-e_h goes to fh. One wave per head, four f32 elements per lane and step.
+__global__ __launch_bounds__(256) void k_q8(const float* __restrict__ q_lat, const float* __restrict__ q_pe,
+                                            float qscale, int nheads, uint8_t* __restrict__ q8,
+                                            float* __restrict__ fh) {
+  using namespace v2;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= nheads) return;
+  const float* ql = q_lat + (int64_t)wv * DC;
+  const float* qp = q_pe + (int64_t)wv * DR;
+  constexpr int QUADS = RW / 4;  // 144
+  f32x4 v[3];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int k = 4 * (lane + 64 * i);
+    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (k < 4 * QUADS) v[i] = k < DC ? *(const f32x4*)(ql + k) : *(const f32x4*)(qp + (k - DC));
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx *= qscale;
+  int e = 0;
+  if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+  const float qs = ldexpf(qscale, 8 - e);
+  uint8_t* dst0 = q8 + (int64_t)wv * 1152;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int k = 4 * (lane + 64 * i);
+    if (k >= 4 * QUADS) break;
+    const f32x4 x = v[i] * qs;
+    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], 0, false);
+    lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], lw, true);
+    uint8_t* dst = dst0 + ((k >> 6) * 2 + ((k >> 5) & 1)) * 64 + (k & 31);
+    *(int*)dst = hw;
+    *(int*)(dst + 32) = lw;
+  }
+  if (lane == 0) fh[wv] = ldexpf(1.f, e - 8);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict__ q8,
+                                                      const float* __restrict__ fh_in, CacheArgs cache,
+                                                      const int32_t* __restrict__ seq_lens, int B, int G,
+                                                      int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
+                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ sc_part,
+                                                      uint16_t* __restrict__ o_part) {
+  using namespace v2;
+  using f8::RB;
+  using f8::TILEB;
+  using f8::ROWSB;
+  using f8::KB;
+  constexpr int NBUF = f8::NBUF, AHEAD = f8::AHEAD, LOADS8 = f8::LOADS, PB = f8::PB;
+  constexpr float HEAD = 64.f;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[f8::LDS_BYTES];
+  uint8_t* const lds_p = lds + NBUF * TILEB;  // P of two consecutive tiles
+  int* const redo_flag = (int*)lds;
+  float* const lds_l = (float*)(lds + 16);
+  float (*const lds_m)[NH] = (float (*)[NH])(lds + 16 + NH * 4);
+  constexpr int OTR = 272;
+  static_assert(4096 + 4 * NH * OTR <= f8::LDS_BYTES, "partial staging exceeds the tile ring");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int p = range_for_block(blockIdx.x, G);
+  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 2, cu_out, fmt_out, lane);
+  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
+  int64_t start = rp.start;
+  const int64_t end = rp.end;
+  if (start >= end) return;
+  int b = rp.b;
+  int64_t s0 = rp.s0, s1 = rp.s1;
+  const int head = 32 * w + l32;
+  uint8_t* const otr = lds + 4096 + w * (NH * OTR);
+
+  // K fragments: chunks 4kb + 2g + h of row l32 -> kq[h] + 64 kb
+  uint32_t kq[2];
+  {
+    const int kx = key8(l32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kq[h] = l32 * RB + (((2 * g + h) ^ kx) << 4);
+  }
+  // V^T fragments (transposing 8-bit reads): in each 16-lane group, lanes 2r and 2r+1 address row
+  // 16kk + 8(r/4) + 4g + r%4 at columns 128w + 32cb + 16h2 + 8(lane & 1), and lane c of the group
+  // receives column c of the 8 rows in row order: slot j = token 16kk + 8(j/4) + 4g + j%4, the
+  // token order of P's B operand. Chunk 8w + 4(cb/2) + 2(cb%2) + h2 -> vq[kk][cb%2] + 64(cb/2).
+  uint32_t vq[2][2];
+  {
+    const int j16 = lane & 15, h2 = (lane >> 4) & 1, r = j16 >> 1;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int t = 16 * kk + 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        vq[kk][par] = t * RB + (((2 * par + h2) ^ key8(t)) << 4) + 8 * (j16 & 1);
+    }
+  }
+  // Copies: wave w moves row chunks R = w + 4i (i < 4) and, for w < 2, R = 16 + w; waves 2 and 3
+  // copy the 32 token scales (each into its own slot, so that every wave issues 5 copies per
+  // tile). Row chunk R, lane L fills LDS chunk 64R + L = row t, position pos: source chunk
+  // (pos & ~3) | ((pos & 3) ^ key8(t)) of row t. Offsets are < 2^16: two per register.
+  uint32_t doff2[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < LOADS8; ++i) {
+    const int R = i < 4 ? w + 4 * i : 16 + w;
+    if (R < 18) {
+      const int f = 64 * R + lane, t = f / f8::CH, pos = f - t * f8::CH;
+      const uint32_t o = (uint32_t)(t * RB + (((pos & ~3) | ((pos & 3) ^ key8(t))) << 4));
+      doff2[i >> 1] |= o << (16 * (i & 1));
+    }
+  }
+
+  while (start < end) {
+    if (s1 <= start) {  // an empty sequence: move on
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+      continue;
+    }
+    const int64_t seg_end = end < s1 ? end : s1;
+    const int64_t t0 = start - s0, t1 = seg_end - s0;
+    const int64_t slot = (int64_t)p + b;
+    Rows<PAGED> rows;
+    rows.init(cache, b);
+    const int64_t n = t1 - t0;
+    const int ntiles = (int)((n + TT - 1) / TT);
+    const uint8_t* rows_b = (const uint8_t*)cache.rows;
+
+    struct CopyPlan {
+      const uint8_t* b0;
+      const uint8_t* b1;
+      const float* sc0;
+      int64_t tt0;
+      uint32_t split, dst;
+      int last;
+    };
+    auto plan_tile = [&](int it) -> CopyPlan {
+      CopyPlan cp;
+      const int64_t tt0 = t0 + (int64_t)it * TT;
+      cp.tt0 = tt0;
+      cp.last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+      cp.dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB));
+      if constexpr (!PAGED) {
+        cp.b0 = rows_b + (rows.base_row + tt0) * RB;
+        cp.b1 = cp.b0;
+        cp.sc0 = cache.scales + rows.base_row + tt0;
+        cp.split = 0xffffffffu;
+      } else {
+        rows.tile(tt0, tt0 + cp.last);
+        const int ps = 1 << rows.ps_shift;
+        const int s_in = (int)(tt0 & (ps - 1));
+        cp.split = (uint32_t)(ps - s_in) * RB;
+        cp.b0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * RB;
+        cp.b1 = rows_b + (int64_t)rows.pg1 * ps * RB - (int64_t)cp.split;
+        cp.sc0 = cache.scales;
+      }
+      return cp;
+    };
+    // copy i of this wave for the planned tile; `partial` as in the bf16 kernel
+    auto copy = [&](const CopyPlan& cp, int i, bool partial) __attribute__((always_inline)) {
+      if (i < 4 || wu < 2) {
+        uint32_t d2 = doff2[i >> 1];
+        asm volatile("" : "+v"(d2));
+        uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
+        if (partial && cp.last < TT - 1) {
+          const int t = (int)(off / RB);
+          if (t > cp.last) off -= (uint32_t)(t - cp.last) * RB;
+        }
+        const uint32_t dst = cp.dst + 1024u * (uint32_t)(i < 4 ? wu + 4 * i : 16 + wu);
+        if constexpr (!PAGED) dma16_s(cp.b0, off, dst);
+        else dma16((off < cp.split ? cp.b0 : cp.b1) + off, dst);
+      } else {
+        const int tk = l32 < cp.last ? l32 : cp.last;
+        const uint32_t dst = cp.dst + (uint32_t)ROWSB + 256u * (uint32_t)(wu - 2);
+        if constexpr (!PAGED) dma4_s(cp.sc0, 4u * (uint32_t)tk, dst);
+        else dma4(cp.sc0 + rows.row(cp.tt0 + tk), dst);
+      }
+    };
+    auto issue_all = [&](int it) {
+      const CopyPlan cp = plan_tile(it);
+#pragma unroll
+      for (int i = 0; i < LOADS8; ++i) copy(cp, i, true);
+    };
+    constexpr int EARLY = 2;
+#pragma unroll 1
+    for (int it = 0; it < EARLY && it < ntiles; ++it) issue_all(it);
+
+    // ---- absorbed query of this wave's 32 heads as two e4m3 parts (k_q8's layout: the B-operand
+    // bytes of lane half g, k = 32g..32g+31 of each 64-wide block)
+    i32x8 qh[KB], ql[KB];
+    float fh;  // 2^-e_h
+    {
+      const u32x4* src = (const u32x4*)(q8 + ((int64_t)b * NH + head) * 1152 + 64 * g);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 x0 = src[8 * kb], x1 = src[8 * kb + 1], y0 = src[8 * kb + 2], y1 = src[8 * kb + 3];
+        qh[kb] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        ql[kb] = i32x8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+      }
+      fh = fh_in[(int64_t)b * NH + head];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(qh[kb]), "+v"(ql[kb]));
+      asm volatile("" : "+v"(fh));
+    }
+    auto prime = [&](int from) {
+#pragma unroll 1
+      for (int it = from; it < AHEAD + 1 && it < ntiles; ++it) issue_all(it);
+    };
+    prime(EARLY);
+    auto valid_of = [&](int it) -> int {
+      const int64_t r = n - (int64_t)it * TT;
+      return r < TT ? (int)r : TT;
+    };
+    // wait until tile `need` has landed, given that tiles up to `issued` have been requested
+    auto wait_tile = [&](int need, int issued) __attribute__((always_inline)) {
+      const int k = issued - need;  // tiles that may stay in flight
+      if (k >= 5) vm_wait_barrier<5 * LOADS8>();
+      else if (k == 4) vm_wait_barrier<4 * LOADS8>();
+      else if (k == 3) vm_wait_barrier<3 * LOADS8>();
+      else if (k == 2) vm_wait_barrier<2 * LOADS8>();
+      else if (k == 1) vm_wait_barrier<LOADS8>();
+      else vm_wait_barrier<0>();
+    };
+
+    f32x16 O[CB];
+    // m_ref: the reference maximum (true score units, base 2); rs_max: the largest per-tile sum of
+    // this lane's probabilities, which bounds how far scores went past m_ref
+    float m_ref = -__builtin_inff(), rs_max = 0.f, l_lane = 0.f;
+    bool have_ref = false;
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) O[cb] = f32x16{};
+      l_lane = 0.f;
+      bool over = false;
+      if (pass > 0) prime(0);
+
+      // Softmax of one tile; register r of S holds token 8(r/4) + 4g + r%4 of the tile. With
+      // c_r = scale_token * 2^-e_h, the score is S_r c_r; the probability against the reference
+      // is e_r = 2^(S_r c_r - m_ref) and P carries e_r c_r (= p * scale_token * 2^-e_h: the output
+      // accumulates 2^-e_h O, and the normaliser l 2^-e_h undoes it). Steps 0-15 handle one
+      // register each; 16 and 17 publish P. Overflow past m_ref + HEAD shows in the tile's sum.
+      // The token scales of register group q (tokens 8q + 4g ..+3) are read from the tile's scale
+      // slot one group ahead, into cg[q & 1] (group 0 during the scores).
+      f32x16 S;
+      f32x4 cg[2];
+      const float* sct = (const float*)(lds + ROWSB);  // scale slot of the tile being softmaxed
+      float rs = 0.f;
+      int valid = TT;
+      uint8_t* pw = lds_p;
+      auto load_group = [&](int q) __attribute__((always_inline)) {
+        cg[q & 1] = *(const f32x4*)(sct + 8 * q + 4 * g);
+      };
+      auto mask_tail = [&]() __attribute__((always_inline)) {
+        if (valid < TT) {
+          const int vg = valid - 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[r] = (8 * (r >> 2) + (r & 3)) < vg ? S[r] : -__builtin_inff();
+        }
+      };
+      // the segment's first tile fixes m_ref (pass 0): the head's maximum over both halves
+      auto set_ref = [&]() __attribute__((always_inline)) {
+        if (!have_ref) {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r] * sct[8 * (r >> 2) + 4 * g + (r & 3)] * fh);
+          m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          have_ref = true;
+        }
+      };
+      auto fill = [&](int ks, bool first) __attribute__((always_inline)) {
+        if (ks < 16) {
+          const int r = ks;
+          if ((r & 3) == 0 && r < 12) load_group((r >> 2) + 1);
+          if (!first) asm volatile("" : "+v"(S[r]));
+          const float c = cg[(r >> 2) & 1][r & 3] * fh;
+          const float e = __builtin_amdgcn_exp2f(fmaf(S[r], c, -m_ref));
+          rs = r == 0 ? e : rs + e;
+          S[r] = e * c;
+        } else if (ks == 16) {
+          l_lane += rs;
+          rs_max = fmaxf(rs_max, rs);
+          over |= rs > 0x1p64f;
+          *(bf16x8*)(pw + head * 64 + ((g ^ ((head >> 2) & 3)) << 4)) =
+              bf16x8{(__bf16)S[0], (__bf16)S[1], (__bf16)S[2], (__bf16)S[3],
+                     (__bf16)S[4], (__bf16)S[5], (__bf16)S[6], (__bf16)S[7]};
+        } else if (ks == 17) {
+          *(bf16x8*)(pw + head * 64 + (((2 + g) ^ ((head >> 2) & 3)) << 4)) =
+              bf16x8{(__bf16)S[8], (__bf16)S[9], (__bf16)S[10], (__bf16)S[11],
+                     (__bf16)S[12], (__bf16)S[13], (__bf16)S[14], (__bf16)S[15]};
+        }
+      };
+      constexpr int FILL8 = 18;
+
+      // V^T fragments of one tile: transposing 8-bit reads, widened to bf16
+      auto vbase = [&](const uint8_t* tile, uint32_t (&vb)[2][2]) __attribute__((always_inline)) {
+        const uint32_t tb = (uint32_t)(uintptr_t)(MLA_LDS void*)tile + 128u * w;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            vb[kk][par] = tb + vq[kk][par];
+            asm volatile("" : "+v"(vb[kk][par]));
+          }
+      };
+      auto ldv = [&](const uint32_t (&vb)[2][2], int kk, int cb) __attribute__((always_inline)) -> u32x2 {
+        const uint32_t ia = vb[kk][cb & 1] + 64u * (cb >> 1);
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(uintptr_t)ia));
+      };
+      // P fragment (B operand) of heads 32hb.. for k step kk
+      auto ldp = [&](const uint8_t* pr, int kk, int hb) __attribute__((always_inline)) -> bf16x8 {
+        const int hr = 32 * hb + l32;
+        return *(const bf16x8*)(pr + hr * 64 + (((2 * kk + g) ^ ((hr >> 2) & 3)) << 4));
+      };
+      // PV of tile `tile` (P from `pr`); av: the kk = 0 fragments, already widened; p0: the first
+      // P fragment. between(j) runs after MFMA j (0..31). The first MFMA that reads a freshly
+      // widened fragment starts with the 2 wait states a VALU write -> MFMA read needs.
+      auto pv = [&](const uint8_t* tile, const uint8_t* pr, bf16x8 (&av)[4], const bf16x8& p0, auto&& between)
+                    __attribute__((always_inline)) {
+        uint32_t vb[2][2];
+        vbase(tile, vb);
+        u32x2 rv[4];
+        bf16x8 pbc = p0, pbn;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            const bool last_group = kk == 1 && hb == 3;
+            if (!last_group) pbn = ldp(pr, hb == 3 ? kk + 1 : kk, hb == 3 ? 0 : hb + 1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              if (last_group && cb == 3) {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              } else if (hb == 0) {
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              } else {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(O[4 * cb + hb]) : "v"(av[cb]), "v"(pbc));
+              }
+              between(16 * kk + 4 * hb + cb);
+              if (kk == 0 && hb == 1) rv[cb] = ldv(vb, 1, cb);
+              if (kk == 0 && hb == 3) av[cb] = widen8(rv[cb]);
+            }
+            pbc = pbn;
+          }
+        }
+      };
+      // Scores of tile tn (`copies` runs after MFMA j as well). Spread over its MFMAs, what the
+      // next steps need first is fetched well ahead of use: the kk = 0 V fragments of tile tv
+      // (read, then widened one per MFMA), the first P fragment of PV (from pr), and the
+      // coefficients c_r of tile tn.
+      auto scores = [&](const uint8_t* tn, const uint8_t* tv, const uint8_t* pr, bf16x8 (&av)[4], bf16x8& p0,
+                        auto&& copies) __attribute__((always_inline)) {
+        sct = (const float*)(tn + ROWSB);
+        uint32_t vb[2][2];
+        vbase(tv, vb);
+        u32x2 rv[4];
+        // after score MFMA j: V reads at JV, JV + 1; P fragment at JP; widening at JW..JW+3;
+        // the first scale group at JS
+        constexpr int JV = 5, JP = 12, JW = 9, JS = 14;
+        S = tile_scores8(tn, kq, qh, ql, [&](int j) __attribute__((always_inline)) {
+          copies(j);
+          if (j == JV) { rv[0] = ldv(vb, 0, 0); rv[1] = ldv(vb, 0, 1); }
+          if (j == JV + 1) { rv[2] = ldv(vb, 0, 2); rv[3] = ldv(vb, 0, 3); }
+          if (j == JP) p0 = ldp(pr, 0, 0);
+          if (j >= JW && j < JW + 4) {
+            av[j - JW] = widen8(rv[j - JW]);
+            asm volatile("" : "+v"(av[j - JW]));
+          }
+          if (j == JS) load_group(0);
+        });
+      };
+
+      auto tile_buf = [&](int it) -> const uint8_t* { return lds + (it % NBUF) * TILEB; };
+      bf16x8 av[4], p0;
+      wait_tile(0, (AHEAD < ntiles - 1 ? AHEAD : ntiles - 1));
+      scores(lds, lds, lds_p, av, p0, [](int) {});
+      valid = valid_of(0);
+      mask_tail();
+      if (pass == 0) set_ref();
+      pw = lds_p;
+#pragma unroll
+      for (int ks = 0; ks < FILL8; ++ks) fill(ks, true);
+      for (int it = 0; it < ntiles; ++it) {
+        // P(it) visible, tile it + 1 resident, every wave past PV(it - 1)
+        {
+          const int issued = it + AHEAD < ntiles - 1 ? it + AHEAD : ntiles - 1;
+          wait_tile(it + 1 < ntiles ? it + 1 : issued, issued);
+        }
+        const uint8_t* pr = lds_p + (it & 1) * PB;
+        const uint8_t* tv = tile_buf(it);
+        if (it + 1 < ntiles) {
+          const uint8_t* tn = tile_buf(it + 1);
+          if (it + AHEAD + 1 < ntiles) {
+            const CopyPlan cp = plan_tile(it + AHEAD + 1);
+            if (cp.last < TT - 1) {
+              scores(tn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
+                if (j % 3 == 1 && j / 3 < LOADS8) copy(cp, j / 3, true);
+              });
+            } else {
+              scores(tn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
+                if (j % 3 == 1 && j / 3 < LOADS8) copy(cp, j / 3, false);
+              });
+            }
+          } else {
+            scores(tn, tv, pr, av, p0, [](int) {});
+          }
+        } else {
+          uint32_t vb[2][2];
+          vbase(tv, vb);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) av[cb] = widen8(ldv(vb, 0, cb));
+          p0 = ldp(pr, 0, 0);
+        }
+        valid = it + 1 < ntiles ? valid_of(it + 1) : 0;
+        mask_tail();
+        pw = lds_p + ((it + 1) & 1) * PB;
+        pv(tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
+          if (j < FILL8) fill(j, false);
+        });
+      }
+      __syncthreads();
+      if (tid == 0) *redo_flag = 0;
+      __syncthreads();
+      if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) *redo_flag = 1;
+      __syncthreads();
+      const int redo = *redo_flag;
+      __syncthreads();
+      if (!redo) break;
+      // a reference at most log2(16) above the segment's true maximum (rs_max >= 1: the first
+      // tile holds a probability of 1 for each head)
+      m_ref += __log2f(fmaxf(rs_max, __shfl_xor(rs_max, 32, 64)));
+    }
+
+    // ---- normalised partial (float16 rows scaled by 2^-e, 2^e to the scale array) and lse
+    const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
+    if (g == 0) lds_l[head] = l_run * fh;  // O holds 2^-e_h times the weighted sum
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      float m = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(O[4 * cb + hb][r]));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0) lds_m[w][32 * hb + l32] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int hr = 32 * hb + l32;
+      const float inv_l = 1.f / lds_l[hr];
+      const float mx2 = fmaxf(fmaxf(lds_m[0][hr], lds_m[1][hr]), fmaxf(lds_m[2][hr], lds_m[3][hr])) * inv_l;
+      int e = 0;
+      if (mx2 > 0.f) (void)frexpf(mx2, &e);
+      const float f = ldexpf(inv_l, -e);
+      uint8_t* dst = otr + hr * OTR;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& o = O[4 * cb + hb];
+          const u32x2 v = {pack_f16x2(o[4 * r4 + 0] * f, o[4 * r4 + 1] * f),
+                           pack_f16x2(o[4 * r4 + 2] * f, o[4 * r4 + 3] * f)};
+          *(u32x2*)(dst + 64 * cb + 16 * r4 + 8 * g) = v;
+        }
+      if (w == 0 && g == 0) sc_part[slot * NH + hr] = ldexpf(1.f, e);
+    }
+    {
+      uint16_t* dst = o_part + slot * NH * DC + 128 * w;
+      const int rsub = lane >> 4, ch = lane & 15;
+#pragma unroll 8
+      for (int j = 0; j < NH / 4; ++j) {
+        const int r = 4 * j + rsub;
+        const u32x4 v = *(const u32x4*)(otr + r * OTR + 16 * ch);
+        *(u32x4*)(dst + (int64_t)r * DC + 8 * ch) = v;
+      }
+    }
+    if (g == 0) lse_part[slot * NH + head] = (m_ref + __log2f(l_run)) * 0.69314718055994530942f;
+    __syncthreads();
 
     start = seg_end;
     if (start < end) {
@@ -1530,13 +1782,20 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   if (mfma) {
     const bool paged = c.page_size > 0;
 #define MLA_FP8(PG) \
-    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
+    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, q8, fhv, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
 #define MLA_V3(PG) \
     hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
-    if (c.dtype == MLA_BF16) { if (paged) MLA_V3(true); else MLA_V3(false); }
-    else { if (paged) MLA_FP8(true); else MLA_FP8(false); }
+    if (c.dtype == MLA_BF16) {
+      if (paged) MLA_V3(true); else MLA_V3(false);
+    } else {
+      uint8_t* q8 = (uint8_t*)(base + L.off_q8);
+      float* fhv = (float*)(base + L.off_fh);
+      const int nheads = B * d.n_h;
+      hipLaunchKernelGGL(k_q8, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, q8, fhv);
+      if (paged) MLA_FP8(true); else MLA_FP8(false);
+    }
 #undef MLA_FP8
 #undef MLA_V3
   } else {
