@@ -175,15 +175,17 @@ __device__ __forceinline__ int swz(int t, int c) { return c ^ swz_key(t); }
 // 16-byte global -> LDS copy per lane (LDS destination: wave-uniform `lds_addr` + 16 * lane).
 // Written as asm so the compiler does not add its conservative "wait for every LDS DMA" before
 // each LDS read: the kernel tracks these loads itself (vm_wait_barrier). The instruction has no
-// VGPR result; only M0 (not used by any other instruction of these kernels) is changed.
+// VGPR result; only M0 (not used by any other instruction of these kernels) is changed. Cached
+// rows are read once: the copies are non-temporal (nt), so the stream does not evict what the
+// workgroups share through L2 (the query).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :: "v"(src), "s"(lds_addr) : "memory", "m0");
 }
 
 // Same copy with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 
@@ -757,11 +759,11 @@ __device__ __forceinline__ int key8(int t) { return (t >> 2) & 3; }
 
 // 4-byte global -> LDS copy per lane (LDS destination: wave-uniform `lds_addr` + 4 * lane).
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
                :: "v"(src), "s"(lds_addr) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 nt"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 

@@ -111,6 +111,12 @@ __device__ __forceinline__ void g2l16(const void* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+// The same copy, non-temporal: for weights, read once per product, so that their stream does not
+// evict the activations every workgroup re-reads from L2.
+__device__ __forceinline__ void g2l16_nt(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
 // At most N copies of this wave still in flight, this wave's LDS reads done, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_copies_barrier() {
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
     uint8_t* buf = lds + (j % NS) * C::SB;
     if (i < C::DW) {
       const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
-      g2l16(Wb + (int64_t)kst * 2, ofs[i], wl + i * 4096);
+      g2l16_nt(Wb + (int64_t)kst * 2, ofs[i], wl + i * 4096);
     } else {
       const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
       g2l16(Xb + (int64_t)kst * ESX, ofs[i], xl + (i - C::DW) * 4096);
@@ -419,7 +425,7 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int f = k * 256 + tid, e = f >> 4, cc = (f & 15) * 8;
-      wv[k] = *(const u32x4*)(W_uk + ((int64_t)i * DH + e) * d_c + c0 + cc);
+      wv[k] = __builtin_nontemporal_load((const u32x4*)(W_uk + ((int64_t)i * DH + e) * d_c + c0 + cc));
     }
 #pragma unroll
     for (int k = 0; k < 4 * NB; ++k) {
