@@ -27,8 +27,8 @@ DecodeLayout decode_layout(const mla_dims& d, int B, int G) {
   L.off_sc = al256(L.off_lse + (size_t)L.n_pieces * d.n_h * 4);
   L.off_o = al256(L.off_sc + (size_t)L.n_pieces * d.n_h * 4);
   L.bytes = L.off_o + (size_t)L.n_pieces * d.n_h * d.d_c * 4;  // sized for float32 partials
-  // MFMA shape: the query in the fp8 kernel's form (two e4m3 parts per element, 1152 bytes per
-  // head) and its per-head power-of-two factor
+  // MFMA shape: the query in the MFMA kernels' operand form (1152 bytes per head: bf16, or two
+  // e4m3 parts per element) and the fp8 form's per-head power-of-two factor
   L.off_q8 = L.off_fh = 0;
   if (d.n_h == 128 && d.d_c == 512 && d.d_r == 64) {
     L.off_q8 = al256(L.bytes);
@@ -277,6 +277,73 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
 }
 
 // ================================================================================================
+// The query of every (sequence, head) in the MFMA kernels' operand form, once per call instead
+// of once per workgroup. Layout: [B][wave block w = head / 32][36 loads][64 lanes][16 bytes], so
+// that load j of lane (g = lane / 32, head 32w + lane % 32) is one coalesced 1 KB wave load.
+//   bf16 kernel: load ks holds bf16(q * qscale) for dims 16ks + 8g .. +7 (the B fragment of k-step ks).
+//   fp8 kernel: x = q * qscale * 2^e_h with the head's largest |x| in [128, 256), split into e4m3
+//     parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi)); loads 4kb, 4kb+1 hold hi and 4kb+2,
+//     4kb+3 lo of dims 64kb + 32g .. +31 (the B fragments of k block kb); 2^-e_h goes to fh.
+// One wave per (sequence, head), four elements per lane and step.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, const float* __restrict__ q_pe,
+                                               float qscale, int nheads, uint8_t* __restrict__ qop,
+                                               float* __restrict__ fh) {
+  using namespace v2;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= nheads) return;
+  const float* ql = q_lat + (int64_t)wv * DC;
+  const float* qp = q_pe + (int64_t)wv * DR;
+  const int bw = wv >> 5, l32 = wv & 31;  // (sequence, wave block) and the head's lane column
+  uint8_t* const blk = qop + (int64_t)bw * 36 * 1024;
+  constexpr int QUADS = RW / 4;  // 144
+  f32x4 v[3];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int k = 4 * (lane + 64 * i);
+    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (k < 4 * QUADS) v[i] = k < DC ? *(const f32x4*)(ql + k) : *(const f32x4*)(qp + (k - DC));
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
+  }
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int k = 4 * (lane + 64 * i);
+      if (k >= 4 * QUADS) break;
+      const int ks = k >> 4, g = (k >> 3) & 1, pos = k & 7;
+      *(u32x2*)(blk + ((ks * 64 + g * 32 + l32) << 4) + 2 * pos) =
+          u32x2{pack_bf16x2(v[i][0] * qscale, v[i][1] * qscale), pack_bf16x2(v[i][2] * qscale, v[i][3] * qscale)};
+    }
+  } else {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx *= qscale;
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+    const float qs = ldexpf(qscale, 8 - e);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int k = 4 * (lane + 64 * i);
+      if (k >= 4 * QUADS) break;
+      const f32x4 x = v[i] * qs;
+      int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+      int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], 0, false);
+      lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], lw, true);
+      const int kb = k >> 6, g = (k >> 5) & 1, off = k & 31;
+      const int j = 4 * kb + (off >> 4);  // hi load; lo is j + 2
+      uint8_t* dst = blk + ((j * 64 + g * 32 + l32) << 4) + (off & 15);
+      *(int*)dst = hw;
+      *(int*)(dst + 2 * 1024) = lw;
+    }
+    if (lane == 0) fh[wv] = ldexpf(1.f, e - 8);
+  }
+}
+
+// ================================================================================================
 // MFMA kernel for bf16 caches at the DeepSeek-V2 shape: 36 MFMA 32x32x16 per tile for the
 // scores (K rows via ds_read_b128), V^T via ds_read_b64_tr_b16. Tiles go straight from HBM into
 // LDS (global->LDS copies), and the memory traffic is spread over the math:
@@ -321,11 +388,10 @@ __device__ __forceinline__ f32x16 tile_scores_copy(const uint8_t* tile, const ui
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ q_lat,
-                                                      const float* __restrict__ q_pe, CacheArgs cache,
+__global__ __launch_bounds__(256, 1) void k_decode_v3(const uint8_t* __restrict__ qop, CacheArgs cache,
                                                       const int32_t* __restrict__ seq_lens, int B, int G,
                                                       int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
-                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ lse_part,
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
   using namespace v2;
@@ -461,25 +527,15 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const float* __restrict__ 
 #pragma unroll 1
     for (int it = 0; it < EARLY && it < ntiles; ++it) issue_all(it);
 
-    // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in)
+    // ---- absorbed query of this wave's 32 heads, as bf16 B-operand fragments (scale folded in;
+    // k_qprep's layout: one coalesced 1 KB load per k-step)
     bf16x8 qf[KSTEPS];
     {
-      const float* ql = q_lat + ((int64_t)b * NH + head) * DC;
-      const float* qp = q_pe + ((int64_t)b * NH + head) * DR;
+      const bf16x8* src = (const bf16x8*)(qop + ((int64_t)b * 4 + w) * 36 * 1024) + lane;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int f0 = 16 * ks + 8 * g;
-        const float* src = f0 < DC ? ql + f0 : qp + (f0 - DC);
-        const f32x4 a = *(const f32x4*)src, c = *(const f32x4*)(src + 4);
-        bf16x8 v;
-        v[0] = (__bf16)(a[0] * qscale); v[1] = (__bf16)(a[1] * qscale);
-        v[2] = (__bf16)(a[2] * qscale); v[3] = (__bf16)(a[3] * qscale);
-        v[4] = (__bf16)(c[0] * qscale); v[5] = (__bf16)(c[1] * qscale);
-        v[6] = (__bf16)(c[2] * qscale); v[7] = (__bf16)(c[3] * qscale);
-        qf[ks] = v;
-      }
-      // every fragment converted before the remaining copies are issued (keeps the waits for the
-      // query loads in front of those copies)
+      for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[64 * ks];
+      // every fragment in registers before the remaining copies are issued (keeps the waits for
+      // the query loads in front of those copies)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
     }
@@ -816,60 +872,12 @@ __device__ __forceinline__ bf16x8 widen8(u32x2 r) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// The query of every (sequence, head) in the fp8 kernel's form, once per call instead of once per
-// workgroup: x = q * sm_scale * log2(e) * 2^e_h with the head's largest |x| in [128, 256), split
-// into e4m3 parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi), both exact-range). Layout per head:
-// [k block (9)][g (2)][hi 32 bytes | lo 32 bytes], i.e. the B-operand bytes of lane half g; the
-// head's 2^-e_h goes to fh. One wave per head, four f32 elements per lane and step.
-__global__ __launch_bounds__(256) void k_q8(const float* __restrict__ q_lat, const float* __restrict__ q_pe,
-                                            float qscale, int nheads, uint8_t* __restrict__ q8,
-                                            float* __restrict__ fh) {
-  using namespace v2;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wv >= nheads) return;
-  const float* ql = q_lat + (int64_t)wv * DC;
-  const float* qp = q_pe + (int64_t)wv * DR;
-  constexpr int QUADS = RW / 4;  // 144
-  f32x4 v[3];
-  float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int k = 4 * (lane + 64 * i);
-    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (k < 4 * QUADS) v[i] = k < DC ? *(const f32x4*)(ql + k) : *(const f32x4*)(qp + (k - DC));
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  mx *= qscale;
-  int e = 0;
-  if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
-  const float qs = ldexpf(qscale, 8 - e);
-  uint8_t* dst0 = q8 + (int64_t)wv * 1152;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int k = 4 * (lane + 64 * i);
-    if (k >= 4 * QUADS) break;
-    const f32x4 x = v[i] * qs;
-    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
-    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], 0, false);
-    lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], lw, true);
-    uint8_t* dst = dst0 + ((k >> 6) * 2 + ((k >> 5) & 1)) * 64 + (k & 31);
-    *(int*)dst = hw;
-    *(int*)(dst + 32) = lw;
-  }
-  if (lane == 0) fh[wv] = ldexpf(1.f, e - 8);
-}
-
 template <bool PAGED>
-__global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict__ q8,
+__global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict__ qop,
                                                       const float* __restrict__ fh_in, CacheArgs cache,
                                                       const int32_t* __restrict__ seq_lens, int B, int G,
                                                       int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
-                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ lse_part,
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
   using namespace v2;
@@ -1013,15 +1021,16 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
 #pragma unroll 1
     for (int it = 0; it < EARLY && it < ntiles; ++it) issue_all(it);
 
-    // ---- absorbed query of this wave's 32 heads as two e4m3 parts (k_q8's layout: the B-operand
-    // bytes of lane half g, k = 32g..32g+31 of each 64-wide block)
+    // ---- absorbed query of this wave's 32 heads as two e4m3 parts (k_qprep's layout: the
+    // B-operand bytes of lane half g, k = 32g..32g+31 of each 64-wide block)
     i32x8 qh[KB], ql[KB];
     float fh;  // 2^-e_h
     {
-      const u32x4* src = (const u32x4*)(q8 + ((int64_t)b * NH + head) * 1152 + 64 * g);
+      const u32x4* src = (const u32x4*)(qop + ((int64_t)b * 4 + w) * 36 * 1024) + lane;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 x0 = src[8 * kb], x1 = src[8 * kb + 1], y0 = src[8 * kb + 2], y1 = src[8 * kb + 3];
+        const u32x4 x0 = src[64 * (4 * kb)], x1 = src[64 * (4 * kb + 1)];
+        const u32x4 y0 = src[64 * (4 * kb + 2)], y1 = src[64 * (4 * kb + 3)];
         qh[kb] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         ql[kb] = i32x8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
       }
@@ -1784,18 +1793,19 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   if (mfma) {
     const bool paged = c.page_size > 0;
 #define MLA_FP8(PG) \
-    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, q8, fhv, c, seq_lens, B, G, cu, fmt, qscale, \
+    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, qop, fhv, c, seq_lens, B, G, cu, fmt, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
 #define MLA_V3(PG) \
-    hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, q_lat, q_pe, c, seq_lens, B, G, cu, fmt, qscale, \
+    hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, qop, c, seq_lens, B, G, cu, fmt, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
+    uint8_t* qop = (uint8_t*)(base + L.off_q8);
+    float* fhv = (float*)(base + L.off_fh);
+    const int nheads = B * d.n_h;
     if (c.dtype == MLA_BF16) {
+      hipLaunchKernelGGL(k_qprep<false>, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, qop, fhv);
       if (paged) MLA_V3(true); else MLA_V3(false);
     } else {
-      uint8_t* q8 = (uint8_t*)(base + L.off_q8);
-      float* fhv = (float*)(base + L.off_fh);
-      const int nheads = B * d.n_h;
-      hipLaunchKernelGGL(k_q8, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, q8, fhv);
+      hipLaunchKernelGGL(k_qprep<true>, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, qop, fhv);
       if (paged) MLA_FP8(true); else MLA_FP8(false);
     }
 #undef MLA_FP8

@@ -27,7 +27,7 @@ struct DecodeLayout {
   size_t off_lse;     // float [n_pieces, n_h]
   size_t off_sc;      // float [n_pieces, n_h]: row scales of float16 partials
   size_t off_o;       // float or float16 [n_pieces, n_h, d_c]
-  size_t off_q8;      // MFMA shape only: e4m3 query parts [B, n_h, 1152 bytes] (fp8 caches)
+  size_t off_q8;      // MFMA shape only: the query in operand form [B, n_h, 1152 bytes]
   size_t off_fh;      // MFMA shape only: float [B, n_h], 2^-e of each head's query scaling
   size_t bytes;
 };
