@@ -282,64 +282,87 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
 // that load j of lane (g = lane / 32, head 32w + lane % 32) is one coalesced 1 KB wave load.
 //   bf16 kernel: load ks holds bf16(q * qscale) for dims 16ks + 8g .. +7 (the B fragment of k-step ks).
 //   fp8 kernel: x = q * qscale * 2^e_h with the head's largest |x| in [128, 256), split into e4m3
-//     parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi)); loads 4kb, 4kb+1 hold hi and 4kb+2,
-//     4kb+3 lo of dims 64kb + 32g .. +31 (the B fragments of k block kb); 2^-e_h goes to fh.
-// One wave per (sequence, head), four elements per lane and step.
+//     parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi)); loads 4kb + p (p = 0, 1) hold hi and
+//     4kb + 2 + p lo of dims 64kb + 32g + 16p .. +15 (the B fragments of k block kb); 2^-e_h goes
+//     to fh.
+// One workgroup per (sequence, wave block): its 36 KB of output are written in order, 16 bytes per
+// thread and store.
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, const float* __restrict__ q_pe,
-                                               float qscale, int nheads, uint8_t* __restrict__ qop,
-                                               float* __restrict__ fh) {
+                                               float qscale, uint8_t* __restrict__ qop, float* __restrict__ fh) {
   using namespace v2;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wv >= nheads) return;
-  const float* ql = q_lat + (int64_t)wv * DC;
-  const float* qp = q_pe + (int64_t)wv * DR;
-  const int bw = wv >> 5, l32 = wv & 31;  // (sequence, wave block) and the head's lane column
+  const int bw = blockIdx.x, tid = threadIdx.x;  // bw = sequence * 4 + wave block
+  const int64_t head0 = (int64_t)bw * 32;        // first (sequence, head) row of the block
   uint8_t* const blk = qop + (int64_t)bw * 36 * 1024;
-  constexpr int QUADS = RW / 4;  // 144
-  f32x4 v[3];
-  float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int k = 4 * (lane + 64 * i);
-    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (k < 4 * QUADS) v[i] = k < DC ? *(const f32x4*)(ql + k) : *(const f32x4*)(qp + (k - DC));
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
-  }
+  // 8 consecutive elements d0.. of head row hr (d0 % 8 == 0, never straddling q_lat / q_pe)
+  auto load8 = [&](int64_t hr, int d0, f32x4& a, f32x4& c) __attribute__((always_inline)) {
+    const float* src = d0 < DC ? q_lat + hr * DC + d0 : q_pe + hr * DR + (d0 - DC);
+    a = *(const f32x4*)src;
+    c = *(const f32x4*)(src + 4);
+  };
   if constexpr (!FP8) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int k = 4 * (lane + 64 * i);
-      if (k >= 4 * QUADS) break;
-      const int ks = k >> 4, g = (k >> 3) & 1, pos = k & 7;
-      *(u32x2*)(blk + ((ks * 64 + g * 32 + l32) << 4) + 2 * pos) =
-          u32x2{pack_bf16x2(v[i][0] * qscale, v[i][1] * qscale), pack_bf16x2(v[i][2] * qscale, v[i][3] * qscale)};
+    for (int i = 0; i < 9; ++i) {
+      const int u = i * 256 + tid, ks = u >> 6, ln = u & 63;  // unit = (k-step, lane)
+      f32x4 a, c;
+      load8(head0 + (ln & 31), 16 * ks + 8 * (ln >> 5), a, c);
+      a *= qscale;
+      c *= qscale;
+      *(u32x4*)(blk + (u << 4)) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                       pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
     }
   } else {
+    __shared__ float qsh[32];
+    {
+      // head l = tid / 8, eight threads per head, 72 elements each
+      const int l = tid >> 3, part = tid & 7;
+      float mx = 0.f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    mx *= qscale;
-    int e = 0;
-    if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
-    const float qs = ldexpf(qscale, 8 - e);
+      for (int q = 0; q < 9; ++q) {
+        f32x4 a, c;
+        load8(head0 + l, 72 * part + 8 * q, a, c);
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
+                             fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])))));
+      }
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int k = 4 * (lane + 64 * i);
-      if (k >= 4 * QUADS) break;
-      const f32x4 x = v[i] * qs;
-      int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
-      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-      int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], 0, false);
-      lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], lw, true);
-      const int kb = k >> 6, g = (k >> 5) & 1, off = k & 31;
-      const int j = 4 * kb + (off >> 4);  // hi load; lo is j + 2
-      uint8_t* dst = blk + ((j * 64 + g * 32 + l32) << 4) + (off & 15);
-      *(int*)dst = hw;
-      *(int*)(dst + 2 * 1024) = lw;
+      for (int o = 4; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      mx *= qscale;
+      int e = 0;
+      if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+      if (part == 0) {
+        qsh[l] = ldexpf(qscale, 8 - e);
+        fh[head0 + l] = ldexpf(1.f, e - 8);
+      }
     }
-    if (lane == 0) fh[wv] = ldexpf(1.f, e - 8);
+    __syncthreads();
+    // unit pair (kb, p, lane): 16 elements, whose hi bytes go to load 4kb + p and lo to 4kb + 2 + p
+    for (int u = tid; u < 18 * 64; u += 256) {
+      const int kp = u >> 6, ln = u & 63, kb = kp >> 1, p = kp & 1;
+      const int l = ln & 31;
+      const float qs = qsh[l];
+      const int d0 = 64 * kb + 32 * (ln >> 5) + 16 * p;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 a, c;
+        load8(head0 + l, d0 + 8 * h, a, c);
+        const f32x4 xs[2] = {a * qs, c * qs};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 x = xs[q];
+          int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+          int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], 0, false);
+          lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], lw, true);
+          hi[2 * h + q] = (uint32_t)hw;
+          lo[2 * h + q] = (uint32_t)lw;
+        }
+      }
+      *(u32x4*)(blk + (((4 * kb + p) * 64 + ln) << 4)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *(u32x4*)(blk + (((4 * kb + 2 + p) * 64 + ln) << 4)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
   }
 }
 
@@ -1800,12 +1823,11 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
     uint8_t* qop = (uint8_t*)(base + L.off_q8);
     float* fhv = (float*)(base + L.off_fh);
-    const int nheads = B * d.n_h;
     if (c.dtype == MLA_BF16) {
-      hipLaunchKernelGGL(k_qprep<false>, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, qop, fhv);
+      hipLaunchKernelGGL(k_qprep<false>, dim3(B * 4), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
       if (paged) MLA_V3(true); else MLA_V3(false);
     } else {
-      hipLaunchKernelGGL(k_qprep<true>, dim3((nheads + 3) / 4), dim3(256), 0, st, q_lat, q_pe, qscale, nheads, qop, fhv);
+      hipLaunchKernelGGL(k_qprep<true>, dim3(B * 4), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
       if (paged) MLA_FP8(true); else MLA_FP8(false);
     }
 #undef MLA_FP8
