@@ -23,10 +23,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-# HBM bytes per decode_attn launch from rocprofv3 FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0), both scaled by
-# a plain copy of known size; recorded in profiles/decode_attn_config2_hbm_counters.md for the
-# decode kernel as it stands. Workloads without a recorded measurement report null.
-DECODE_TRAFFIC_BYTES = {"2": 158755 * 1024 * 2 + 39169 * 1024}
+# HBM bytes per launch of the decode kernel (k_decode_v3 / k_decode_fp8) from rocprofv3 FETCH_SIZE
+# (KiB, x2.0) + WRITE_SIZE (KiB, x1.0), both scaled by a plain copy of known size; recorded in
+# profiles/decode_attn_config2_hbm_counters.md and profiles/decode_attn_config4_hbm_counters.md for
+# the kernels as they stand. Workloads without a recorded measurement report null.
+DECODE_TRAFFIC_BYTES = {
+    "2": 153660 * 1024 * 2 + 38145 * 1024,
+    "4": 297086 * 1024 * 2 + 38144 * 1024,
+    "4f8": 151018 * 1024 * 2 + 37120 * 1024,
+}
 
 
 def parse():
