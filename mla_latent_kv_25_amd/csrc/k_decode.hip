@@ -285,14 +285,16 @@ __device__ __forceinline__ f32x16 tile_scores(const uint8_t* tile, const uint32_
 //     parts x = hi + lo (hi = RNE(x), lo = RNE(x - hi)); loads 4kb + p (p = 0, 1) hold hi and
 //     4kb + 2 + p lo of dims 64kb + 32g + 16p .. +15 (the B fragments of k block kb); 2^-e_h goes
 //     to fh.
-// One workgroup per (sequence, wave block): its 36 KB of output are written in order, 16 bytes per
-// thread and store.
+// One workgroup per (sequence, 8 heads): 128-byte runs of its rows of the layout, 16 bytes per
+// thread and store (16 workgroups per sequence, so that small batches still spread over the chip).
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, const float* __restrict__ q_pe,
                                                float qscale, uint8_t* __restrict__ qop, float* __restrict__ fh) {
   using namespace v2;
-  const int bw = blockIdx.x, tid = threadIdx.x;  // bw = sequence * 4 + wave block
-  const int64_t head0 = (int64_t)bw * 32;        // first (sequence, head) row of the block
+  constexpr int HB = 8;                              // heads per workgroup
+  const int tid = threadIdx.x;
+  const int64_t head0 = (int64_t)blockIdx.x * HB;    // first (sequence, head) row
+  const int bw = (int)(head0 >> 5), l0 = (int)(head0 & 31);
   uint8_t* const blk = qop + (int64_t)bw * 36 * 1024;
   // 8 consecutive elements d0.. of head row hr (d0 % 8 == 0, never straddling q_lat / q_pe)
   auto load8 = [&](int64_t hr, int d0, f32x4& a, f32x4& c) __attribute__((always_inline)) {
@@ -301,31 +303,29 @@ __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, 
     c = *(const f32x4*)(src + 4);
   };
   if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      const int u = i * 256 + tid, ks = u >> 6, ln = u & 63;  // unit = (k-step, lane)
+    for (int u = tid; u < 36 * 2 * HB; u += 256) {    // unit = (k-step, g, head)
+      const int ks = u / (2 * HB), g = (u / HB) & 1, l = u % HB;
       f32x4 a, c;
-      load8(head0 + (ln & 31), 16 * ks + 8 * (ln >> 5), a, c);
+      load8(head0 + l, 16 * ks + 8 * g, a, c);
       a *= qscale;
       c *= qscale;
-      *(u32x4*)(blk + (u << 4)) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                       pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+      *(u32x4*)(blk + ((ks * 64 + g * 32 + l0 + l) << 4)) =
+          u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
     }
   } else {
-    __shared__ float qsh[32];
+    __shared__ float qsh[HB];
     {
-      // head l = tid / 8, eight threads per head, 72 elements each
-      const int l = tid >> 3, part = tid & 7;
+      // head l = tid / 32, 32 threads per head over its 72 groups of 8 elements
+      const int l = tid >> 5, part = tid & 31;
       float mx = 0.f;
-#pragma unroll
-      for (int q = 0; q < 9; ++q) {
+      for (int q = part; q < RW / 8; q += 32) {
         f32x4 a, c;
-        load8(head0 + l, 72 * part + 8 * q, a, c);
+        load8(head0 + l, 8 * q, a, c);
         mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
                              fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])))));
       }
 #pragma unroll
-      for (int o = 4; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
       mx *= qscale;
       int e = 0;
       if (mx > 0.f) (void)frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
@@ -335,12 +335,11 @@ __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, 
       }
     }
     __syncthreads();
-    // unit pair (kb, p, lane): 16 elements, whose hi bytes go to load 4kb + p and lo to 4kb + 2 + p
-    for (int u = tid; u < 18 * 64; u += 256) {
-      const int kp = u >> 6, ln = u & 63, kb = kp >> 1, p = kp & 1;
-      const int l = ln & 31;
+    // unit pair (kb, p, g, head): 16 elements, whose hi bytes go to load 4kb + p and lo to 4kb + 2 + p
+    for (int u = tid; u < 18 * 2 * HB; u += 256) {
+      const int kp = u / (2 * HB), g = (u / HB) & 1, l = u % HB, kb = kp >> 1, p = kp & 1;
       const float qs = qsh[l];
-      const int d0 = 64 * kb + 32 * (ln >> 5) + 16 * p;
+      const int d0 = 64 * kb + 32 * g + 16 * p;
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -360,6 +359,7 @@ __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, 
           lo[2 * h + q] = (uint32_t)lw;
         }
       }
+      const int ln = g * 32 + l0 + l;
       *(u32x4*)(blk + (((4 * kb + p) * 64 + ln) << 4)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
       *(u32x4*)(blk + (((4 * kb + 2 + p) * 64 + ln) << 4)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
@@ -1824,10 +1824,10 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
     uint8_t* qop = (uint8_t*)(base + L.off_q8);
     float* fhv = (float*)(base + L.off_fh);
     if (c.dtype == MLA_BF16) {
-      hipLaunchKernelGGL(k_qprep<false>, dim3(B * 4), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
+      hipLaunchKernelGGL(k_qprep<false>, dim3(B * 16), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
       if (paged) MLA_V3(true); else MLA_V3(false);
     } else {
-      hipLaunchKernelGGL(k_qprep<true>, dim3(B * 4), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
+      hipLaunchKernelGGL(k_qprep<true>, dim3(B * 16), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
       if (paged) MLA_FP8(true); else MLA_FP8(false);
     }
 #undef MLA_FP8
