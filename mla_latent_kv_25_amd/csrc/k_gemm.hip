@@ -166,6 +166,23 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   }
 }
 
+// Eight float32 values (v0, then v1) as bf16 hi + lo parts (x = hi + lo to ~16 significand bits).
+// Pairs are rounded to bf16 in one conversion; a bf16 widens back to float by placing its bits in
+// the high half, so lo = x - hi is exact before its own rounding.
+__device__ __forceinline__ void split_hi_lo(const f32x4& v0, const f32x4& v1, bf16x8& bh, bf16x8& bl) {
+  uint32_t hv[4], lv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
+    const float x1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
+    const uint32_t h = pack_bf16x2(x0, x1);
+    hv[e] = h;
+    lv[e] = pack_bf16x2(x0 - __builtin_bit_cast(float, h << 16), x1 - __builtin_bit_cast(float, h & 0xffff0000u));
+  }
+  bh = __builtin_bit_cast(bf16x8, u32x4{hv[0], hv[1], hv[2], hv[3]});
+  bl = __builtin_bit_cast(bf16x8, u32x4{lv[0], lv[1], lv[2], lv[3]});
+}
+
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -308,13 +325,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
       }
       if constexpr (XF32) {
         if (q % (2 * MB) == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const __bf16 h0 = (__bf16)cur.x0[jb][e], h1 = (__bf16)cur.x1[jb][e];
-            bh[e] = h0; bh[4 + e] = h1;
-            bl[e] = (__bf16)(cur.x0[jb][e] - (float)h0);
-            bl[4 + e] = (__bf16)(cur.x1[jb][e] - (float)h1);
-          }
+          split_hi_lo(cur.x0[jb], cur.x1[jb], bh, bl);
         }
         mfma_acc(acc[mb][jb], cur.a[mb], half ? bl : bh);
       } else {
@@ -466,13 +477,7 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
       const float* xr = xs + (32 * j + l32) * XP + 16 * ks + 8 * g;
       const f32x4 v0 = *(const f32x4*)xr, v1 = *(const f32x4*)(xr + 4);
       bf16x8 bh, bl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        __bf16 h0 = (__bf16)v0[e], h1 = (__bf16)v1[e];
-        bh[e] = h0; bh[4 + e] = h1;
-        bl[e] = (__bf16)(v0[e] - (float)h0);
-        bl[4 + e] = (__bf16)(v1[e] - (float)h1);
-      }
+      split_hi_lo(v0, v1, bh, bl);
       acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[j], 0, 0, 0);
       acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[j], 0, 0, 0);
     }
