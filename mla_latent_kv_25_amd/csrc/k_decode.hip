@@ -1083,9 +1083,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
     };
 
     f32x16 O[CB];
-    // m_ref: the reference maximum (true score units, base 2); rs_max: the largest per-tile sum of
-    // this lane's probabilities, which bounds how far scores went past m_ref
-    float m_ref = -__builtin_inff(), rs_max = 0.f, l_lane = 0.f;
+    // m_ref: the reference maximum (true score units, base 2); x_max: the largest exponent
+    // s - m_ref this lane met in the pass (the segment's maximum is m_ref + x_max)
+    float m_ref = -__builtin_inff(), x_max = -__builtin_inff(), l_lane = 0.f;
     bool have_ref = false;
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
       // c_r = scale_token * 2^-e_h, the score is S_r c_r; the probability against the reference
       // is e_r = 2^(S_r c_r - m_ref) and P carries e_r c_r (= p * scale_token * 2^-e_h: the output
       // accumulates 2^-e_h O, and the normaliser l 2^-e_h undoes it). Steps 0-15 handle one
-      // register each; 16 and 17 publish P. Overflow past m_ref + HEAD shows in the tile's sum.
+      // register each; 16 and 17 publish P.
       // The token scales of register group q (tokens 8q + 4g ..+3) are read from the tile's scale
       // slot one group ahead, into cg[q & 1] (group 0 during the scores).
       f32x16 S;
@@ -1134,13 +1134,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
           if ((r & 3) == 0 && r < 12) load_group((r >> 2) + 1);
           if (!first) asm volatile("" : "+v"(S[r]));
           const float c = cg[(r >> 2) & 1][r & 3] * fh;
-          const float e = __builtin_amdgcn_exp2f(fmaf(S[r], c, -m_ref));
+          const float x = fmaf(S[r], c, -m_ref);
+          x_max = fmaxf(x_max, x);
+          const float e = __builtin_amdgcn_exp2f(x);
           rs = r == 0 ? e : rs + e;
           S[r] = e * c;
         } else if (ks == 16) {
           l_lane += rs;
-          rs_max = fmaxf(rs_max, rs);
-          over |= rs > 0x1p64f;
           *(bf16x8*)(pw + head * 64 + ((g ^ ((head >> 2) & 3)) << 4)) =
               bf16x8{(__bf16)S[0], (__bf16)S[1], (__bf16)S[2], (__bf16)S[3],
                      (__bf16)S[4], (__bf16)S[5], (__bf16)S[6], (__bf16)S[7]};
@@ -1281,6 +1281,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
           if (j < FILL8) fill(j, false);
         });
       }
+      over = x_max > HEAD;
       __syncthreads();
       if (tid == 0) *redo_flag = 0;
       __syncthreads();
@@ -1289,9 +1290,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
       const int redo = *redo_flag;
       __syncthreads();
       if (!redo) break;
-      // a reference at most log2(16) above the segment's true maximum (rs_max >= 1: the first
-      // tile holds a probability of 1 for each head)
-      m_ref += __log2f(fmaxf(rs_max, __shfl_xor(rs_max, 32, 64)));
+      // the segment's exact maximum per head (x_max >= 0: the first tile holds the reference)
+      m_ref += fmaxf(x_max, __shfl_xor(x_max, 32, 64));
+      x_max = -__builtin_inff();
     }
 
     // ---- normalised partial (float16 rows scaled by 2^-e, 2^e to the scale array) and lse

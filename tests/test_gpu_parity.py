@@ -224,3 +224,41 @@ def test_appended_row_storage():
                 dv = np.abs(e4m3_decode(g) - e4m3_decode(codes[0]))
                 assert np.mean(g != codes[0]) < 0.02
                 assert np.all(dv <= np.abs(e4m3_decode(codes[0])) * 2.0 ** -3 + 2.0 ** -9)
+
+
+@pytest.mark.parametrize("key", ["0", "1", "2", "4f8"])
+def test_late_score_spike(key):
+    """A cached row far along a range with a score far above everything before it: the attention
+    kernels take the first tile's maximum as their softmax reference, and a score more than 2^64
+    above it sends the range through a second pass with a higher reference. One row per sequence
+    is scaled by 64 (exact in every storage type, and the fp8 scale follows it), so that for the
+    heads whose score at that row is positive the scaled score lies far above the reference; with
+    4 ranges over T = [1000, 300], both rows sit in later tiles of their ranges."""
+    case = _case(key, 2, [1000, 300], stress=True)
+    src = case.row_source()
+    assert case.cfg.layout == "contiguous"
+    for b, pos in ((0, 900), (1, 250)):
+        src[b, pos] = src[b, pos] * 64
+    print(f"case cfg={key} B=2 T=[1000, 300] spike rows (0, 900), (1, 250) x64 splits=4", flush=True)
+    step, _ = run_gpu(case, 4)
+    ref = run_oracle(case)
+    u_ref = np.stack([ref[b]["u"] for b in range(2)])
+    # the scaled rows make u up to ~50x larger than in the standard workloads (|u| < 1): the
+    # rel-L2 bar holds as it is, the max-abs bar is taken relative to the largest |u| when that
+    # exceeds 1
+    u_gpu = step.u.double().cpu().numpy()
+    rl, ma = rel_l2(u_gpu, u_ref), float(np.max(np.abs(u_gpu - u_ref)))
+    scale = max(1.0, float(np.max(np.abs(u_ref))))
+    tr, ta = TOL[case.cfg.cdtype]
+    print(f"spike cfg{key} u rel-L2 {rl:.3e} max-abs {ma:.3e} (|ref|max {scale:.3e})", flush=True)
+    assert rl <= tr and ma <= ta * scale, (rl, ma, scale)
+    lse_ref = np.stack([ref[b]["lse"] for b in range(2)])
+    # the spike must dominate some heads by far more than 2^64, or the second pass is not reached
+    assert float(np.max(lse_ref)) > 100.0, float(np.max(lse_ref))
+    # the scaled rows' scores are 64x larger, and so is the absolute error that the rounding of the
+    # query to the MFMA operand type puts on them (2^-9 relative per element at bf16: ~0.5 on a score
+    # of ~50 built from 576 products): the bar is the usual one plus 1.5 % of |lse|
+    err = np.abs(step.lse.double().cpu().numpy() - lse_ref)
+    abs_tol, rel_tol = (1e-4, 1e-6) if case.cfg.cdtype == "f32" else (2e-2, 1.5e-2)
+    print(f"  lse max-abs {float(err.max()):.3e} (largest lse {float(np.max(lse_ref)):.1f})", flush=True)
+    assert np.all(err <= abs_tol + rel_tol * np.abs(lse_ref)), float(np.max(err - rel_tol * np.abs(lse_ref)))
