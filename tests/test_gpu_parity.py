@@ -262,3 +262,17 @@ def test_late_score_spike(key):
     abs_tol, rel_tol = (1e-4, 1e-6) if case.cfg.cdtype == "f32" else (2e-2, 1.5e-2)
     print(f"  lse max-abs {float(err.max()):.3e} (largest lse {float(np.max(lse_ref)):.1f})", flush=True)
     assert np.all(err <= abs_tol + rel_tol * np.abs(lse_ref)), float(np.max(err - rel_tol * np.abs(lse_ref)))
+
+
+@pytest.mark.parametrize("key,ps", [("2", 32), ("2", 256), ("4f8", 32), ("4f8", 128), ("1", 16), ("0", 8)])
+def test_page_sizes(key, ps):
+    """Paged caches with other page sizes than the configs' 64: the MFMA kernels take any power of
+    two >= 32 (a 32-token tile spans at most two pages), the generic kernel any size. Ragged
+    lengths put range starts at every offset inside a page."""
+    cfg = get_config(key, stress=True).with_(page_size=ps)
+    case = make_case(cfg, device="cuda", B=3, T=[300, 70, 5], layout="paged")
+    print(f"case cfg={key} page_size={ps} B=3 T=[300, 70, 5] splits=7", flush=True)
+    step, _ = run_gpu(case, 7)
+    ref = run_oracle(case)
+    u_ref = np.stack([ref[b]["u"] for b in range(3)])
+    check_u(step.u.double().cpu().numpy(), u_ref, case.cfg.cdtype, f"paged ps={ps} cfg{key}")
