@@ -92,16 +92,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 
 // ------------------------------------------------------------------ typed element access
 template <int DT> struct Elem;
+// ld: load and widen; cvt: widen stored bits (kept raw while a load is in flight, so that the
+// conversion does not force a wait at the load)
 template <> struct Elem<MLA_F32> {
   typedef float T;
+  static __device__ __forceinline__ float cvt(T x) { return x; }
   static __device__ __forceinline__ float ld(const T* p, int64_t i) { return p[i]; }
 };
 template <> struct Elem<MLA_F16> {
   typedef uint16_t T;
+  static __device__ __forceinline__ float cvt(T x) { return f16_bits_to_f32(x); }
   static __device__ __forceinline__ float ld(const T* p, int64_t i) { return f16_bits_to_f32(p[i]); }
 };
 template <> struct Elem<MLA_BF16> {
   typedef uint16_t T;
+  static __device__ __forceinline__ float cvt(T x) { return bf16_bits_to_f32(x); }
   static __device__ __forceinline__ float ld(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
 };
 

@@ -500,7 +500,9 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
 // ================================================================================================
 // float32 VALU GEMM for float32 / float16 / bf16 weights of any shape:
 //   Y[n][m] = sum_k A(m, k) X[n][k],  A(m, k) = TRANS ? W[k*lda + m] : W[m*lda + k].
-// Tile 64 (m) x 16 (n) per 256 threads, k in steps of 32 through LDS.
+// Tile 64 (m) x 16 (n) per 256 threads, k in steps of 32 through LDS. The shapes it serves are
+// small (tens of workgroups), so each step's compute is far shorter than a load round trip: the
+// elements of the next PD steps are kept in flight in registers (one round trip per 256 k).
 // Barrier for LDS hand-offs only (waits for this wave's LDS operations, not its global loads).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -517,48 +519,61 @@ __global__ __launch_bounds__(256) void k_gemm_valu(int M, int N, int K, const vo
   const typename Elem<XDT>::T* X = (const typename Elem<XDT>::T*)Xv + (int64_t)z * zX;
   const int mi = tid & 63, nq = tid >> 6;  // thread: row mi, columns nq*4 .. nq*4+3
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  // the next k-chunk's elements are fetched into registers while the current one is used from
-  // LDS; barriers wait for LDS only, so those loads stay in flight
-  float wv[8], xv[2];
-  auto fetch = [&](int k0) __attribute__((always_inline)) {
+  // the elements of k-chunks k0 .. k0 + 32 PD - 32 are fetched into registers (slot p holds
+  // chunk k0 + 32p) while earlier chunks are used from LDS; barriers wait for LDS only, so those
+  // loads stay in flight. Loads use clamped (always valid) indices and keep the stored bits:
+  // a conditional load, or a conversion at the load, makes the compiler wait for it at once.
+  constexpr int PD = 8;
+  typename Elem<ADT>::T wr[PD][8];
+  typename Elem<XDT>::T xr[PD][2];
+  auto w_el = [&](int q, int& mm, int& kk) __attribute__((always_inline)) {
+    const int e = tid + 256 * q;
+    if (TRANS) { mm = e & 63; kk = e >> 6; } else { kk = e & 31; mm = e >> 5; }
+  };
+  auto fetch = [&](int p, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
       int mm, kk;
-      if (TRANS) { mm = e & 63; kk = e >> 6; } else { kk = e & 31; mm = e >> 5; }
-      const int m = m0 + mm, k = k0 + kk;
-      wv[q] = (m < M && k < K) ? Elem<ADT>::ld(W, TRANS ? (int64_t)k * lda + m : (int64_t)m * lda + k) : 0.f;
+      w_el(q, mm, kk);
+      const int m = min(m0 + mm, M - 1), k = min(k0 + kk, K - 1);
+      wr[p][q] = W[TRANS ? (int64_t)k * lda + m : (int64_t)m * lda + k];
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int e = tid + 256 * q;
-      const int nn = e >> 5, kk = e & 31;
-      const int n = n0 + nn, k = k0 + kk;
-      xv[q] = (n < N && k < K) ? Elem<XDT>::ld(X, (int64_t)n * ldx + k) : 0.f;
+      const int n = min(n0 + (e >> 5), N - 1), k = min(k0 + (e & 31), K - 1);
+      xr[p][q] = X[(int64_t)n * ldx + k];
     }
   };
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += 32) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
-      if (TRANS) Ws[e & 63][e >> 6] = wv[q];
-      else Ws[e >> 5][e & 31] = wv[q];
-    }
+  for (int p = 0; p < PD; ++p)
+    if (32 * p < K) fetch(p, 32 * p);
+  for (int kb = 0; kb < K; kb += 32 * PD) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + 256 * q;
-      Xs[e >> 5][e & 31] = xv[q];
-    }
-    lds_sync();
-    if (k0 + 32 < K) fetch(k0 + 32);
+    for (int p = 0; p < PD; ++p) {
+      const int k0 = kb + 32 * p;
+      if (k0 >= K) break;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        int mm, kk;
+        w_el(q, mm, kk);
+        Ws[mm][kk] = (m0 + mm < M && k0 + kk < K) ? Elem<ADT>::cvt(wr[p][q]) : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = tid + 256 * q;
+        Xs[e >> 5][e & 31] = (n0 + (e >> 5) < N && k0 + (e & 31) < K) ? Elem<XDT>::cvt(xr[p][q]) : 0.f;
+      }
+      lds_sync();
+      if (k0 + 32 * PD < K) fetch(p, k0 + 32 * PD);
 #pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float a = Ws[mi][kk];
+      for (int kk = 0; kk < 32; ++kk) {
+        const float a = Ws[mi][kk];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += a * Xs[nq * 4 + q][kk];
+        for (int q = 0; q < 4; ++q) acc[q] += a * Xs[nq * 4 + q][kk];
+      }
+      lds_sync();
     }
-    lds_sync();
   }
   const int m = m0 + mi;
   if (m >= M) return;
