@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="2", help="workload key (2, 3, 4, 4f8)")
-    ap.add_argument("--splits", type=int, default=0, help="decode ranges (0 = one per CU)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode ranges (0 = the library's default: one per CU at the V2 shape, two otherwise)")
     ap.add_argument("--rotate", type=int, default=2, help="cache copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -318,7 +319,7 @@ def main():
         "config": {"workload": f"config {cfg.key}: {cfg.title}", "batch": B, "seq_len": int(seq_lens.max()),
                    "sum_context_tokens": sigma_T, "cache_dtype": cfg.cdtype, "layout": cfg.layout,
                    "n_h": dims.n_h, "d_c": dims.d_c, "d_r": dims.d_r, "d": dims.d,
-                   "decode_splits": args.splits or "one per CU", "cache_copies_cycled": len(caches),
+                   "decode_splits": args.splits or ("one per CU" if dims.n_h == 128 else "two per CU"), "cache_copies_cycled": len(caches),
                    "hip_graph": bool(graphs),
                    "absorption": "pre-combined" if args.precombined else "two-step"},
         "latent_cache_gbps": cache_bytes / (t_dec + t_comb) / 1e9,

@@ -157,7 +157,8 @@ MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_
  *     s_ij = (q_lat_i . c_j + q_pe_i . k^R_j) * sm_scale
  * and the result is the softmax-weighted latent sum plus its log-sum-exp.
  * The batch's tokens (sum of seq_lens) are cut into `num_splits` contiguous ranges of equal
- * length (0 = one per compute unit; at most 1024); each range is one workgroup, and a sequence
+ * length (0 = the library's choice: one per compute unit at n_h = 128, d_c = 512, d_r = 64, two
+ * per compute unit otherwise; at most 1024); each range is one workgroup, and a sequence
  * is split where ranges cut it. Each (range, sequence) piece writes a partial result into the
  * workspace: its normalised latent sum and log-sum-exp per head; mla_combine merges them. At most
  * num_splits + B - 1 pieces exist. The partial latent sums are float32, except on the MFMA path

@@ -112,9 +112,12 @@ int device_cu_count() {
 }
 }  // namespace mla
 
-static int resolve_splits(int32_t num_splits) {
+// Default range count: one per CU at the DeepSeek-V2 shape (the MFMA kernels hold a CU each);
+// two per CU otherwise, so that the latency-bound generic kernel has two workgroups per CU.
+static int resolve_splits(const mla_dims* d, int32_t num_splits) {
   if (num_splits > 0) return num_splits;
-  const int n = mla::device_cu_count();
+  const bool v2 = d->n_h == 128 && d->d_c == 512 && d->d_r == 64;
+  const int n = mla::device_cu_count() * (v2 ? 1 : 2);
   return n < 1024 ? n : 1024;
 }
 
@@ -179,7 +182,7 @@ mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, fl
 
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t num_splits) {
   if (!dims || B <= 0 || num_splits < 0) return 0;
-  return mla::decode_layout(*dims, B, resolve_splits(num_splits)).bytes;
+  return mla::decode_layout(*dims, B, resolve_splits(dims, num_splits)).bytes;
 }
 
 mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, const float* q_pe,
@@ -199,7 +202,7 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const float* q_lat, 
   if (!mla::decode_supported(*dims, c.dtype, c.page_size))
     return fail(MLA_E_UNSUPPORTED, "%s: no decode kernel for n_h=%d d_c=%d d_r=%d with cache dtype %d", fn,
                 dims->n_h, dims->d_c, dims->d_r, c.dtype);
-  const int G = resolve_splits(num_splits);
+  const int G = resolve_splits(dims, num_splits);
   const size_t need = mla::decode_layout(*dims, B, G).bytes;
   if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   return hip_status(mla::launch_decode(*dims, B, q_lat, q_pe, c, seq_lens, G, resolve_scale(dims), workspace, stream),
@@ -216,7 +219,7 @@ mla_status mla_combine(const mla_dims* dims, int32_t B, int32_t num_splits, cons
   if (B == 0) return ok();
   if (!seq_lens || !o_lat) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
   if (misaligned(o_lat, workspace) || misaligned4(seq_lens, lse)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
-  const int G = resolve_splits(num_splits);
+  const int G = resolve_splits(dims, num_splits);
   const size_t need = mla::decode_layout(*dims, B, G).bytes;
   if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   return hip_status(mla::launch_combine(*dims, B, G, workspace, o_lat, lse, stream), fn);
