@@ -506,16 +506,32 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
 // Barrier for LDS hand-offs only (waits for this wave's LDS operations, not its global loads).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Up to 3 products sharing X, K and lda launched as one grid (segment s owns the 64-row tiles
+// [t0[s], t0[s+1]) of blockIdx.x): the running model's first projections are too small to fill
+// the chip one at a time.
+struct VSeg {
+  int n;
+  int t0[4];
+  const void* W[3];
+  float* Y[3];
+  int64_t ldy[3];
+  int M[3];
+};
+
 template <int ADT, int XDT, bool TRANS>
-__global__ __launch_bounds__(256) void k_gemm_valu(int M, int N, int K, const void* __restrict__ Wv,
-                                                   int64_t lda, int64_t zW, const void* __restrict__ Xv,
-                                                   int64_t ldx, int64_t zX, float* __restrict__ Y,
-                                                   int64_t ldy, int64_t zY) {
+__global__ __launch_bounds__(256) void k_gemm_valu(VSeg sg, int N, int K, int64_t lda, int64_t zW,
+                                                   const void* __restrict__ Xv, int64_t ldx, int64_t zX,
+                                                   int64_t zY) {
   __shared__ float Ws[64][33];
   __shared__ float Xs[16][33];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 16, z = blockIdx.z;
-  const typename Elem<ADT>::T* W = (const typename Elem<ADT>::T*)Wv + (int64_t)z * zW;
+  const int mt = blockIdx.x;
+  const int s = sg.n > 2 && mt >= sg.t0[2] ? 2 : (sg.n > 1 && mt >= sg.t0[1] ? 1 : 0);
+  const int M = sg.M[s];
+  const int64_t ldy = sg.ldy[s];
+  float* __restrict__ Y = sg.Y[s];
+  const int m0 = (mt - sg.t0[s]) * 64, n0 = blockIdx.y * 16, z = blockIdx.z;
+  const typename Elem<ADT>::T* W = (const typename Elem<ADT>::T*)sg.W[s] + (int64_t)z * zW;
   const typename Elem<XDT>::T* X = (const typename Elem<XDT>::T*)Xv + (int64_t)z * zX;
   const int mi = tid & 63, nq = tid >> 6;  // thread: row mi, columns nq*4 .. nq*4+3
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -585,12 +601,47 @@ __global__ __launch_bounds__(256) void k_gemm_valu(int M, int N, int K, const vo
 }
 
 // ------------------------------------------------------------------ dispatch helpers
+static VSeg vseg1(int M, const void* W, float* Y, int64_t ldy) {
+  VSeg sg{};
+  sg.n = 1;
+  sg.t0[0] = 0;
+  sg.t0[1] = (M + 63) / 64;
+  sg.W[0] = W;
+  sg.Y[0] = Y;
+  sg.ldy[0] = ldy;
+  sg.M[0] = M;
+  return sg;
+}
+
+template <int ADT, int XDT, bool TRANS>
+static void valu_seg(hipStream_t st, const VSeg& sg, int N, int K, int64_t lda, int64_t zW, const void* X,
+                     int64_t ldx, int64_t zX, int64_t zY, int Z) {
+  dim3 grid(sg.t0[sg.n], (N + 15) / 16, Z);
+  hipLaunchKernelGGL((k_gemm_valu<ADT, XDT, TRANS>), grid, dim3(256), 0, st, sg, N, K, lda, zW, X, ldx, zX, zY);
+}
 template <int ADT, int XDT, bool TRANS>
 static void valu(hipStream_t st, int M, int N, int K, const void* W, int64_t lda, int64_t zW, const void* X,
                  int64_t ldx, int64_t zX, float* Y, int64_t ldy, int64_t zY, int Z) {
-  dim3 grid((M + 63) / 64, (N + 15) / 16, Z);
-  hipLaunchKernelGGL((k_gemm_valu<ADT, XDT, TRANS>), grid, dim3(256), 0, st, M, N, K, W, lda, zW, X, ldx, zX, Y,
-                     ldy, zY);
+  valu_seg<ADT, XDT, TRANS>(st, vseg1(M, W, Y, ldy), N, K, lda, zW, X, ldx, zX, zY, Z);
+}
+// Three products Y_s[n][m] = sum_k W_s[m][k] X[n][k] (W_s row-major with lda = K; X in the weight
+// dtype) in one launch.
+static void valu_stacked(int wdt, hipStream_t st, int N, int K, const void* X, int64_t ldx, const void* W0,
+                         int M0, float* Y0, int64_t ldy0, const void* W1, int M1, float* Y1, int64_t ldy1,
+                         const void* W2, int M2, float* Y2, int64_t ldy2) {
+  VSeg sg{};
+  sg.n = 3;
+  sg.t0[0] = 0;
+  sg.t0[1] = (M0 + 63) / 64;
+  sg.t0[2] = sg.t0[1] + (M1 + 63) / 64;
+  sg.t0[3] = sg.t0[2] + (M2 + 63) / 64;
+  sg.W[0] = W0; sg.W[1] = W1; sg.W[2] = W2;
+  sg.Y[0] = Y0; sg.Y[1] = Y1; sg.Y[2] = Y2;
+  sg.ldy[0] = ldy0; sg.ldy[1] = ldy1; sg.ldy[2] = ldy2;
+  sg.M[0] = M0; sg.M[1] = M1; sg.M[2] = M2;
+  if (wdt == MLA_F32) valu_seg<MLA_F32, MLA_F32, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
+  else if (wdt == MLA_F16) valu_seg<MLA_F16, MLA_F16, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
+  else valu_seg<MLA_BF16, MLA_BF16, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
 }
 
 // Y[n][m] = sum_k A(m,k) X[n][k] with runtime weight dtype; X is float32 or the weight dtype.
@@ -693,10 +744,9 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     else hipLaunchKernelGGL(k_absorb_uk<4>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
     return hipGetLastError();
   }
-  // VALU path (any dims, float32/float16/bf16 weights)
-  valu_any(wdt, true, false, st, d.d_cq, B, d.d, W_dq, d.d, 0, h, d.d, 0, cq, d.d_cq, 0, 1);
-  valu_any(wdt, true, false, st, d.d_c, B, d.d, W_dkv, d.d, 0, h, d.d, 0, kv_new, rw, 0, 1);
-  valu_any(wdt, true, false, st, d.d_r, B, d.d, W_kr, d.d, 0, h, d.d, 0, kv_new + d.d_c, rw, 0, 1);
+  // VALU path (any dims, float32/float16/bf16 weights); W^DQ, W^DKV and W^KR share h: one launch
+  valu_stacked(wdt, st, B, d.d, h, d.d, W_dq, d.d_cq, cq, d.d_cq, W_dkv, d.d_c, kv_new, rw, W_kr, d.d_r,
+               kv_new + d.d_c, rw);
   valu_any(wdt, false, false, st, nhdh, B, d.d_cq, W_uq, d.d_cq, 0, cq, d.d_cq, 0, qc, nhdh, 0, 1);
   valu_any(wdt, false, false, st, d.n_h * d.d_r, B, d.d_cq, W_qr, d.d_cq, 0, cq, d.d_cq, 0, q_pe,
            (int64_t)d.n_h * d.d_r, 0, 1);
@@ -849,9 +899,8 @@ hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h,
     mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
     return hipGetLastError();
   }
-  valu_any(wdt, true, false, st, d.d_cq, B, d.d, W_dq, d.d, 0, h, d.d, 0, cq, d.d_cq, 0, 1);
-  valu_any(wdt, true, false, st, d.d_c, B, d.d, W_dkv, d.d, 0, h, d.d, 0, kv_new, rw, 0, 1);
-  valu_any(wdt, true, false, st, d.d_r, B, d.d, W_kr, d.d, 0, h, d.d, 0, kv_new + d.d_c, rw, 0, 1);
+  valu_stacked(wdt, st, B, d.d, h, d.d, W_dq, d.d_cq, cq, d.d_cq, W_dkv, d.d_c, kv_new, rw, W_kr, d.d_r,
+               kv_new + d.d_c, rw);
   valu_any(wdt, false, false, st, nhdc, B, d.d_cq, Wq_pre, d.d_cq, 0, cq, d.d_cq, 0, q_lat, nhdc, 0, 1);
   valu_any(wdt, false, false, st, d.n_h * d.d_r, B, d.d_cq, W_qr, d.d_cq, 0, cq, d.d_cq, 0, q_pe,
            (int64_t)d.n_h * d.d_r, 0, 1);
