@@ -665,6 +665,27 @@ static void valu_any(int wdt, bool x_is_w, bool trans, hipStream_t st, int M, in
 #undef MLA_VALU_CASE
 }
 
+// Y[n][m] = sum_k W[m][k] X[n][k] (W row-major, lda = ldx = K, X float32) with K cut into S
+// slices: the slices run as S batched problems into part[S][N][M] (float32; at least S*N*M floats),
+// then k_splitk_reduce adds them in slice order into Y (deterministic). For products whose few
+// 64-row tiles would otherwise each run the whole K serially. Falls back to one launch when K does
+// not split into slices of at least 32.
+static void valu_splitk(int wdt, hipStream_t st, int M, int N, int K, const void* W, const float* X, float* Y,
+                        int64_t ldy, int S, float* part) {
+  if (S < 2 || K % S != 0 || K / S < 32 || M % 4 != 0 || part == nullptr) {
+    valu_any(wdt, false, false, st, M, N, K, W, K, 0, X, K, 0, Y, ldy, 0, 1);
+    return;
+  }
+  const int Ks = K / S;
+  valu_any(wdt, false, false, st, M, N, Ks, W, K, Ks, X, K, Ks, part, M, (int64_t)N * M, S);
+  Seg sg{};
+  sg.Y[0] = Y; sg.ldy[0] = ldy;
+  sg.m0[0] = 0; sg.m0[1] = M; sg.nseg = 1;
+  const int64_t n4 = (int64_t)N * (M / 4);
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256), 1), dim3(256), 0, st, sg, N, M, S,
+                     (const float*)part, (int64_t)0);
+}
+
 static bool mfma_dims_ok(const mla_dims& d) {
   return d.d % 256 == 0 && d.d_cq % 256 == 0 && d.d_cq % 64 == 0 && d.d_c % 128 == 0 && d.d_r % 64 == 0 &&
          d.d_h == absq::DH && (d.n_h * d.d_h) % 256 == 0;
@@ -779,7 +800,9 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
   }
   valu_any(wdt, false, false, st, d.d_h, B, d.d_c, W_uv, d.d_c, (int64_t)d.d_h * d.d_c, o_lat,
            (int64_t)d.n_h * d.d_c, d.d_c, o, nhdh, d.d_h, d.n_h);
-  valu_any(wdt, false, false, st, d.d, B, nhdh, W_o, nhdh, 0, o, nhdh, 0, u, d.d, 0, 1);
+  // W^O: the layout's partial area holds sk5 * B * d floats
+  const int sk5 = o_splits(d, B).sk5;
+  valu_splitk(wdt, st, d.d, B, nhdh, W_o, o, u, d.d, sk5, sk5 > 1 ? part : nullptr);
   return hipGetLastError();
 }
 
@@ -918,7 +941,9 @@ hipError_t launch_absorb_out_pre(const mla_dims& d, int B, int wdt, const float*
                     o_wide(B) ? 8 : 4);
     return hipGetLastError();
   }
-  valu_any(wdt, false, false, st, d.d, B, nhdc, Wo_pre, nhdc, 0, o_lat, nhdc, 0, u, d.d, 0, 1);
+  // the layout holds sk * B * d partial floats
+  const int sk = o_pre_splits(d, B).sk5;
+  valu_splitk(wdt, st, d.d, B, nhdc, Wo_pre, o_lat, u, d.d, sk, sk > 1 ? (float*)ws : nullptr);
   return hipGetLastError();
 }
 
