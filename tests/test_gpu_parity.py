@@ -140,6 +140,33 @@ def test_split_count_invariance():
         assert float((l - outs[0][2]).abs().max()) < 1e-3
 
 
+@pytest.mark.parametrize("key", ["0", "1", "2", "4f8"])
+def test_zero_length_sequences(key):
+    """decode_attn + combine with some sequences at length 0 (first, middle and last), called on
+    the queries and cache of a normal step: those sequences get o_lat = 0 and lse = -inf, and the
+    others match the normal step up to the range split (the batch's total changes)."""
+    T = [1, 300, 1, 77, 5, 1]
+    empty = [0, 2, 5]
+    case = _case(key, len(T), T, layout="paged" if key in ("2", "4f8") else None, stress=True)
+    print(f"case cfg={key} T={T} zeroed={empty}", flush=True)
+    step, cache = run_gpu(case, 7)
+    lens = case.seq_lens.clone()
+    lens[empty] = 0
+    o_lat = torch.full_like(step.o_lat, 7.0)
+    lse = torch.full_like(step.lse, 7.0)
+    mla.decode_attn(step.dims, step.q_lat, step.q_pe, cache, lens, 7, step.ws_d)
+    mla.combine(step.dims, 7, lens, step.ws_d, o_lat, lse)
+    torch.cuda.synchronize()
+    for b in range(len(T)):
+        if b in empty:
+            assert torch.all(o_lat[b] == 0) and torch.all(torch.isneginf(lse[b])), b
+        else:
+            e = rel_l2(o_lat[b].double().cpu().numpy(), step.o_lat[b].double().cpu().numpy())
+            le = float((lse[b] - step.lse[b]).abs().max())
+            print(f"  b{b}: o_lat rel-L2 {e:.2e}, lse max-abs {le:.2e}", flush=True)
+            assert e < (1e-5 if key == "0" else 2e-3) and le < (1e-5 if key == "0" else 1e-3)
+
+
 def test_paged_equals_contiguous():
     for key in ("2", "4f8"):
         pc = _case(key, 3, [300, 64, 129], layout="paged", stress=True)
