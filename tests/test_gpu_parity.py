@@ -36,6 +36,9 @@ SMALL_CASES = [
     ("4f8", 2, [3000, 129], None, False, 8),
     ("4f8", 2, [2000, 33], None, True, 3),
     ("4f8", 3, [900, 64, 2], "paged", True, 5),
+    # more ranges than tokens: most ranges are empty, the rest hold one or two tokens
+    ("2", 2, [3, 40], None, True, 64),
+    ("4f8", 2, [5, 20], "paged", True, 48),
 ]
 
 
