@@ -189,16 +189,16 @@ def prefill_bench(args):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "
+                                   "for how the path shards across GPUs"}))
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
     if args.prefill:
         prefill_bench(args)
         return
-    if args.gpus != 1:
-        print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "
-                                   "for how the path shards across GPUs"}))
-        sys.exit(2)
     import numpy as np
     import torch
 
