@@ -145,7 +145,9 @@ MLA_API mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype,
  *   seq_lens: device int32 [B]; pos_b = seq_lens[b] - 1.
  *   q_pe [B, n_h, d_r] and the k^R part of kv_new [B, d_c + d_r] are rotated IN PLACE.
  *   cache: if non-NULL, row [c^KV | k^R] of each sequence is written to slot pos_b, rounded to
- *   the cache dtype (RNE; fp8: per-token scale amax/448 and saturating RNE codes). */
+ *   the cache dtype (RNE; fp8: per-token scale amax/448 and saturating RNE codes).
+ *   A sequence with seq_lens[b] == 0 (outside the contract) is left alone: its q_pe and kv_new
+ *   rows are not rotated and nothing is written to the cache. */
 MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, float* q_pe,
                     float* kv_new, const mla_cache* cache, hipStream_t stream);
 

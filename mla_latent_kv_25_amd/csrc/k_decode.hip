@@ -379,10 +379,8 @@ __global__ __launch_bounds__(256) void k_qprep(const float* __restrict__ q_lat, 
 // two halves of a head are joined once per segment.
 namespace v3 {
 constexpr int NBUF = 4;
+constexpr int EARLY = 1;  // tiles whose copies are issued before the query loads
 }
-#ifndef V3_EARLY_TILES
-#define V3_EARLY_TILES 1  // tiles whose copies are issued before the query loads
-#endif
 
 // Scores of one tile (as tile_scores) with between(ks) run after MFMA ks; the calls sit between
 // the volatile MFMA statements in program order (used to issue tile copies under the math).
@@ -546,7 +544,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const uint8_t* __restrict_
     // The first tiles go out ahead of the query loads (the query waits then also cover them);
     // the rest of the prime follows once the query is in registers, so that it does not queue
     // in front of the query.
-    constexpr int EARLY = V3_EARLY_TILES;
+    constexpr int EARLY = v3::EARLY;
 #pragma unroll 1
     for (int it = 0; it < EARLY && it < ntiles; ++it) issue_all(it);
 

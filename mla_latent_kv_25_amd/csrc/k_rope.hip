@@ -77,6 +77,9 @@ __global__ __launch_bounds__(256) void k_rope_append(int n_h, int d_c, int d_r, 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int pos = seq_lens[b] - 1;
+  // a zero-length sequence (outside the contract) has no current token: nothing is rotated and no
+  // row is stored (pos = -1 would address the row before the sequence's first one)
+  if (pos < 0) return;
   for (int m = tid; m < half; m += blockDim.x) {
     double ang = (double)pos * freq(m, d_r);
     double s, c;

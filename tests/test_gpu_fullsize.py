@@ -1,10 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times (one range per
 compute unit), on sampled outputs the oracle can compute one by one.
 
-Every config runs its whole decode step on the GPU through the C ABI. The oracle is then run on a
-few sampled sequences, with explicit K/V reconstruction: the first, the last and one in between,
-or the shortest and longest of a ragged batch. For the long contexts only a few sampled heads
-are checked (o_lat, lse), because u needs every head.
+Every config runs its whole decode step on the GPU through the C ABI. The oracle is then run, with
+explicit K/V reconstruction and every head, on sampled sequences: the first, the last and one in
+between of config 2; the shortest, the longest and ten more seeded picks of the ragged config 3;
+two whole 131,072-token sequences of config 4 (bf16 and fp8 caches). Each sampled sequence is
+compared on u (the step's output) and on o_lat and lse of all its heads.
 """
 import numpy as np
 import pytest
@@ -61,25 +62,38 @@ def test_fullsize_config1():
         check_u(step.u[b].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg1 b={b}")
 
 
+def config3_sample(lens, n_extra=10, seed=7):
+    """Sequences of config 3 checked against the oracle: the shortest, the longest and n_extra more
+    drawn without replacement from the rest with a fixed seed."""
+    lens = np.asarray(lens)
+    b_short, b_long = int(np.argmin(lens)), int(np.argmax(lens))
+    rest = [b for b in range(len(lens)) if b not in (b_short, b_long)]
+    rng = np.random.default_rng(seed)
+    extra = sorted(int(b) for b in rng.choice(rest, size=min(n_extra, len(rest)), replace=False))
+    return [b_short, b_long] + extra
+
+
 def test_fullsize_config3():
-    """B=128 ragged T in [1024, 32768], 64-token pages: shortest and longest sequence."""
+    """B=128 ragged T in [1024, 32768], 64-token pages: u, o_lat and lse of 12 sampled sequences
+    (the shortest, the longest and ten seeded picks), every head."""
     case = make_case(get_config("3"), device="cuda")
     step, _ = run_gpu(case, 0)
     lens = case.seq_lens.cpu().numpy()
-    b_short, b_long = int(np.argmin(lens)), int(np.argmax(lens))
-    ref = _oracle(case, b_short)
-    check_u(step.u[b_short].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg3 b={b_short}")
-    heads = [0, 57, 127]
-    ref = _oracle(case, b_long, heads=heads, want_u=False)
-    _check_heads(step, case, b_long, ref, heads, "cfg3")
+    sample = config3_sample(lens)
+    print(f"cfg3 sample {sample} (T = {[int(lens[b]) for b in sample]})", flush=True)
+    for b in sample:
+        ref = _oracle(case, b)
+        check_u(step.u[b].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg3 b={b}")
+        _check_heads(step, case, b, ref, list(range(case.dims.n_h)), "cfg3")
 
 
 @pytest.mark.parametrize("key", ["4", "4f8"])
 def test_fullsize_config4(key):
-    """B=4, T=131072 (bf16 and fp8 e4m3 caches): sampled heads of two sequences."""
+    """B=4, T=131072 (bf16 and fp8 e4m3 caches), split over 64 ranges per sequence: u, o_lat and
+    lse of every head of the first and the last sequence."""
     case = make_case(get_config(key), device="cuda")
     step, _ = run_gpu(case, 0)
-    heads = [0, 101]
     for b in (0, case.B - 1):
-        ref = _oracle(case, b, heads=heads, want_u=False)
-        _check_heads(step, case, b, ref, heads, f"cfg{key}")
+        ref = _oracle(case, b)
+        check_u(step.u[b].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg{key} b={b}")
+        _check_heads(step, case, b, ref, list(range(case.dims.n_h)), f"cfg{key}")

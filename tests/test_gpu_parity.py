@@ -170,6 +170,44 @@ def test_zero_length_sequences(key):
             assert e < (1e-5 if key == "0" else 2e-3) and le < (1e-5 if key == "0" else 1e-3)
 
 
+@pytest.mark.parametrize("key,layout", [("2", "contiguous"), ("2", "paged"), ("4f8", "contiguous"), ("0", "contiguous")])
+def test_rope_zero_length_writes_nothing(key, layout):
+    """mla_rope with sequences of length 0 (outside the contract; the first and the last of the
+    batch): their q_pe and kv_new rows stay as they were and nothing is stored for them. In a
+    contiguous cache, position -1 of sequence 0 would be the row before the buffer, and in a paged
+    cache slot -1 of its first page. The only cache rows that change are the rows the other
+    sequences append at their positions."""
+    T = [5, 300, 9]
+    empty = [0, 2]
+    case = _case(key, 3, T, layout=layout)
+    print(f"case cfg={key} layout={layout} T={T} zeroed={empty}", flush=True)
+    cache = build_cache(case)
+    step = mla.DecodeStep(case.dims, 3, 4)
+    mla.absorb_q(step.dims, case.h, case.weights, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.clone()
+    lens[empty] = 0
+    rows0, qpe0, kv0 = cache.rows.clone(), step.q_pe.clone(), step.kv_new.clone()
+    sc0 = cache.scales.clone() if cache.scales is not None else None
+    mla.rope(step.dims, lens, step.q_pe, step.kv_new, cache)
+    torch.cuda.synchronize()
+    for b in empty:
+        assert torch.equal(step.q_pe[b], qpe0[b]) and torch.equal(step.kv_new[b], kv0[b]), b
+    assert not torch.equal(step.q_pe[1], qpe0[1])  # the non-empty sequence was rotated
+    row = case.dims.row
+    changed = (cache.rows != rows0).reshape(-1, row).any(dim=1)
+    if sc0 is not None:
+        changed |= (cache.scales != sc0).reshape(-1)
+    pos = T[1] - 1
+    if layout == "contiguous":
+        allowed = 1 * case.t_cap + pos
+    else:
+        ps = case.cfg.page_size
+        allowed = int(case.block_table[1, pos // ps]) * ps + pos % ps
+    idx = torch.nonzero(changed).flatten().tolist()
+    assert set(idx) <= {allowed}, idx
+
+
 def test_paged_equals_contiguous():
     for key in ("2", "4f8"):
         pc = _case(key, 3, [300, 64, 129], layout="paged", stress=True)
@@ -256,42 +294,76 @@ def test_appended_row_storage():
                 assert np.all(dv <= np.abs(e4m3_decode(codes[0])) * 2.0 ** -3 + 2.0 ** -9)
 
 
-@pytest.mark.parametrize("key", ["0", "1", "2", "4f8"])
-def test_late_score_spike(key):
+def spike_budget(case, ref, mult):
+    """Error budget of the late-spike case (reading R10 of the design notes), from the oracle's own
+    query and stored rows. The MFMA kernels hold the query as bf16 (or as two e4m3 parts with the
+    same 8 significant bits) and the probabilities as bf16: each is rounded with a relative error of
+    at most 2^-8, so
+      score s_ij:  |ds_ij| <= 2^-8 * scale * sum_k |q_ik c_jk|, and lse_i moves by at most max_j |ds_ij|;
+      u:           one dominating row carries its rounded weight into every output, |du| <= 2^-8 |u|,
+                   plus 2^-11 for the float16 partial rows.
+    The bars are the benchmark spec's absolute ones plus twice these terms (2^-7), and they grow with the
+    spike: 8x more from x8 to x64."""
+    import numpy as np
+    from oracle import OracleDims, absorbed_query, score_scale
+    dims = OracleDims.of(case.dims)
+    W = weights64(case)
+    scale = float(score_scale(dims))
+    lse_bar, u_bar = [], []
+    for b in range(case.B):
+        T = int(case.seq_lens[b])
+        q_lat, q_pe, _ = absorbed_query(W, case.h[b].double().cpu().numpy(), T - 1, dims)
+        q = np.abs(np.concatenate([q_lat, q_pe], axis=1))                       # [n_h, 576]
+        from gpu_helpers import oracle_prefix
+        rows = np.abs(np.vstack([oracle_prefix(case, b), ref[b]["read_new"][None, :]]))  # [T, 576]
+        lse_bar.append(2e-2 + 2.0 ** -7 * scale * (rows @ q.T).max(axis=0))   # per head
+        u_bar.append(2e-2 + 2.0 ** -7 * float(np.max(np.abs(ref[b]["u"]))))
+    return np.stack(lse_bar), np.array(u_bar)
+
+
+@pytest.mark.parametrize("key,mult", [("0", 64), ("1", 64), ("2", 8), ("2", 64), ("4f8", 8), ("4f8", 64)])
+def test_late_score_spike(key, mult):
     """A cached row far along a range with a score far above everything before it: the attention
     kernels take the first tile's maximum as their softmax reference, and a score more than 2^64
     above it sends the range through a second pass with a higher reference. One row per sequence
-    is scaled by 64 (exact in every storage type, and the fp8 scale follows it), so that for the
-    heads whose score at that row is positive the scaled score lies far above the reference; with
-    4 ranges over T = [1000, 300], both rows sit in later tiles of their ranges."""
+    is scaled by `mult` (exact in every storage type, and the fp8 scale follows it); with 4 ranges
+    over T = [1000, 300], both rows sit in later tiles of their ranges. At x64 the spike dominates
+    some heads by far more than 2^64 (second pass), at x8 it does not; u is up to ~50x larger than in
+    the standard workloads. The MFMA kernels (configs 2, 4f8) are held to the error budget of
+    spike_budget, the float32 generic kernel (configs 0, 1) to the plain bars."""
+    import numpy as np
     case = _case(key, 2, [1000, 300], stress=True)
     src = case.row_source()
     assert case.cfg.layout == "contiguous"
     for b, pos in ((0, 900), (1, 250)):
-        src[b, pos] = src[b, pos] * 64
-    print(f"case cfg={key} B=2 T=[1000, 300] spike rows (0, 900), (1, 250) x64 splits=4", flush=True)
+        src[b, pos] = src[b, pos] * mult
+    print(f"case cfg={key} B=2 T=[1000, 300] spike rows (0, 900), (1, 250) x{mult} splits=4", flush=True)
     step, _ = run_gpu(case, 4)
     ref = run_oracle(case)
     u_ref = np.stack([ref[b]["u"] for b in range(2)])
-    # the scaled rows make u up to ~50x larger than in the standard workloads (|u| < 1): the
-    # rel-L2 bar holds as it is, the max-abs bar is taken relative to the largest |u| when that
-    # exceeds 1
-    u_gpu = step.u.double().cpu().numpy()
-    rl, ma = rel_l2(u_gpu, u_ref), float(np.max(np.abs(u_gpu - u_ref)))
-    scale = max(1.0, float(np.max(np.abs(u_ref))))
-    tr, ta = TOL[case.cfg.cdtype]
-    print(f"spike cfg{key} u rel-L2 {rl:.3e} max-abs {ma:.3e} (|ref|max {scale:.3e})", flush=True)
-    assert rl <= tr and ma <= ta * scale, (rl, ma, scale)
     lse_ref = np.stack([ref[b]["lse"] for b in range(2)])
-    # the spike must dominate some heads by far more than 2^64, or the second pass is not reached
-    assert float(np.max(lse_ref)) > 100.0, float(np.max(lse_ref))
-    # the scaled rows' scores are 64x larger, and so is the absolute error that the rounding of the
-    # query to the MFMA operand type puts on them (2^-9 relative per element at bf16: ~0.5 on a score
-    # of ~50 built from 576 products): the bar is the usual one plus 1.5 % of |lse|
-    err = np.abs(step.lse.double().cpu().numpy() - lse_ref)
-    abs_tol, rel_tol = (1e-4, 1e-6) if case.cfg.cdtype == "f32" else (2e-2, 1.5e-2)
-    print(f"  lse max-abs {float(err.max()):.3e} (largest lse {float(np.max(lse_ref)):.1f})", flush=True)
-    assert np.all(err <= abs_tol + rel_tol * np.abs(lse_ref)), float(np.max(err - rel_tol * np.abs(lse_ref)))
+    u_gpu = step.u.double().cpu().numpy()
+    lse_err = np.abs(step.lse.double().cpu().numpy() - lse_ref)
+    rl = rel_l2(u_gpu, u_ref)
+    u_err = np.max(np.abs(u_gpu - u_ref), axis=1)
+    tr, ta = TOL[case.cfg.cdtype]
+    print(f"spike cfg{key} x{mult}: u rel-L2 {rl:.3e}, max-abs per seq {u_err}, |u|max {np.max(np.abs(u_ref)):.3e}; "
+          f"lse max-abs {lse_err.max():.3e} (largest lse {lse_ref.max():.1f})", flush=True)
+    assert rl <= tr, rl
+    if mult == 64:  # the second pass is reached
+        assert float(np.max(lse_ref)) > 100.0, float(np.max(lse_ref))
+    if case.cfg.cdtype in ("f32", "f16"):
+        # float32 arithmetic on the stored values throughout: the absolute bars plus a float32
+        # budget of 2^-16 relative (unit roundoff 2^-24 grown by sums of up to a few thousand terms)
+        assert np.all(u_err <= ta + 2.0 ** -16 * np.max(np.abs(u_ref), axis=1)), u_err
+        lse_tol = (1e-4 if case.cfg.cdtype == "f32" else 2e-2) + 2.0 ** -16 * np.abs(lse_ref)
+        assert np.all(lse_err <= lse_tol), float(np.max(lse_err - lse_tol))
+        return
+    lse_bar, u_bar = spike_budget(case, ref, mult)
+    print(f"  budget: u max-abs <= {u_bar}, lse max-abs <= {lse_bar.min():.3e} .. {lse_bar.max():.3e}; "
+          f"worst lse use {float(np.max(lse_err / lse_bar)):.2f} of its bar", flush=True)
+    assert np.all(u_err <= u_bar), (u_err, u_bar)
+    assert np.all(lse_err <= lse_bar), float(np.max(lse_err - lse_bar))
 
 
 @pytest.mark.parametrize("key,ps", [("2", 32), ("2", 256), ("4f8", 32), ("4f8", 128), ("1", 16), ("0", 8)])
