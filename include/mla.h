@@ -201,6 +201,21 @@ MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
                           float* u, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_absorb_out_noalloc — mla_absorb_out for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same inputs,
+ * output, kernels and result as mla_absorb_out, but no workspace argument: the W^UV output and
+ * the K-split partial sums live in a library-owned static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES bytes per GPU (each GPU the library runs on holds it until the process
+ * ends). The call allocates and frees nothing.
+ *   Rejects (MLA_E_WORKSPACE, nothing launched) a B whose mla_absorb_out_workspace_bytes(dims, B)
+ *   exceeds MLA_NOALLOC_SCRATCH_BYTES (at the DeepSeek-V2 shape: any B above 315).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on the same GPU (other
+ *   streams, other threads) race and must be ordered by the caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+MLA_API mla_status mla_absorb_out_noalloc(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
+                                  const void* W_uv, const void* W_o, float* u, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_prefill_tables — chunked prefill through the decode calls.
  * "DeepSeek-V2 from Scratch" section 6 gives attention for token t over positions 0..t. A chunk
  * of C new tokens per sequence (positions p0[b] .. p0[b] + C - 1) is run as a batch of B * C

@@ -68,6 +68,7 @@ def lib():
         "mla_combine": (I32, [D, I32, I32, P, P, SZ, P, P, ST]),
         "mla_absorb_out_workspace_bytes": (SZ, [D, I32]),
         "mla_absorb_out": (I32, [D, I32, I32, P, P, P, P, SZ, P, ST]),
+        "mla_absorb_out_noalloc": (I32, [D, I32, I32, P, P, P, P, ST]),
         "mla_prefill_tables": (I32, [C, I32, I32, P, P, P, ST]),
         "mla_precombine": (I32, [D, I32, P, P, P, P, P, P, ST]),
         "mla_absorb_q_pre": (I32, [D, I32, I32, P, P, P, P, P, P, P, SZ, P, P, P, ST]),
@@ -88,6 +89,7 @@ def lib():
 
 EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_decode_workspace_bytes",
            "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
+           "mla_absorb_out_noalloc",
            "mla_prefill_tables", "mla_precombine", "mla_absorb_q_pre", "mla_absorb_out_pre_workspace_bytes",
            "mla_absorb_out_pre", "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
 
@@ -206,6 +208,14 @@ def absorb_out(dims: Dims, o_lat, W_uv, W_o, workspace, u):
                                 _ptr(W_uv, name="W_uv"), _ptr(W_o, W_uv.dtype, "W_o"),
                                 _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
                                 _ptr(u, torch.float32, "u"), _stream()))
+
+
+def absorb_out_noalloc(dims: Dims, o_lat, W_uv, W_o, u):
+    """absorb_out with the library's static scratch in place of a workspace (no allocation)."""
+    wdt = DTYPE_CODE[W_uv.dtype]
+    _check(lib().mla_absorb_out_noalloc(ctypes.byref(dims), o_lat.shape[0], wdt, _ptr(o_lat, torch.float32, "o_lat"),
+                                        _ptr(W_uv, name="W_uv"), _ptr(W_o, W_uv.dtype, "W_o"),
+                                        _ptr(u, torch.float32, "u"), _stream()))
 
 
 def precombine(dims: Dims, W, Wq_pre=None, Wo_pre=None):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mla.h"
 #include "launch.hpp"
@@ -111,6 +112,37 @@ int device_cu_count() {
   return n;
 }
 }  // namespace mla
+
+// ------------------------------------------------------------------------------------------------
+// Scratch of mla_absorb_out_noalloc: a file-scope device array (each GPU the library runs on holds
+// its own copy, at its own address, until the process ends). In host code `scratch` is only a
+// stand-in symbol, never a device address: its address on the current device is looked up once per
+// device with hipGetSymbolAddress and only that pointer is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first call on that device).
+mla_status scratch_on_current_device(void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_E_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_E_UNSUPPORTED, "%s: device ordinal %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_E_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+}  // namespace
 
 // Default range count: one per CU at the DeepSeek-V2 shape (the MFMA kernels hold a CU each);
 // two per CU otherwise, so that the latency-bound generic kernel has two workgroups per CU.
@@ -243,6 +275,26 @@ mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const
   if (!workspace || ws_bytes < mla_absorb_out_workspace_bytes(dims, B))
     return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_out_workspace_bytes(dims, B));
   return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
+}
+
+mla_status mla_absorb_out_noalloc(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
+                                  const void* W_uv, const void* W_o, float* u, hipStream_t stream) {
+  const char* fn = "mla_absorb_out_noalloc";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (B == 0) return ok();
+  if (!o_lat || !W_uv || !W_o || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(o_lat, W_uv, W_o, u)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = mla_absorb_out_workspace_bytes(dims, B);
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_E_WORKSPACE, "%s: B=%d needs %zu bytes of scratch, more than the %zu the library holds", fn, B,
+                need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws, fn);
+  if (s) return s;
+  return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, ws, u, stream), fn);
 }
 
 mla_status mla_precombine(const mla_dims* dims, int32_t wdtype, const void* W_uq, const void* W_uk,

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -132,6 +132,21 @@ def test_absorb_out_and_store_validation(L):
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 65, FAKE, 65, None) == 1  # > t_cap
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 1, FAKE, 10, FAKE, 5, None) == 1   # stride
     assert L.mla_cache_store(ctypes.byref(d), ctypes.byref(c), 0, None, 0, None, 0, None) == 0
+
+
+def test_absorb_out_noalloc_validation(L):
+    """The no-allocation variant rejects bad arguments, and any batch whose workspace would not fit
+    the library's static scratch, before touching the device."""
+    d = _dims()
+    assert L.mla_absorb_out_noalloc(ctypes.byref(d), 2, 0, None, FAKE, FAKE, FAKE, None) == 1
+    assert L.mla_absorb_out_noalloc(ctypes.byref(d), 2, 7, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.mla_absorb_out_noalloc(ctypes.byref(d), 0, 0, None, None, None, None, None) == 0
+    v2 = _dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
+    limit = 32 << 20
+    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 315) <= limit
+    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 316) > limit
+    assert L.mla_absorb_out_noalloc(ctypes.byref(v2), 316, 2, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert b"scratch" in L.mla_last_error()
 
 
 def test_precombined_validation(L):
