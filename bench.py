@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the decode_attn sub-records of the other DeepSeek-V2 workloads (configs 3, 4, 4f8)")
     ap.add_argument("--prefill", type=int, default=0, metavar="C",
                     help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
                          "(a separate JSON line; the default run is the decode step)")
@@ -110,7 +112,68 @@ def cpu_baseline(case, budget_s):
     T = int(case.seq_lens[0])
     return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {case.B} sequences (T={T} each, full decode step incl. all heads), "
-                      f"{dt:.1f} s, numpy float64 explicit K/V reconstruction"}
+                      f"{dt:.1f} s, numpy float64 explicit K/V reconstruction",
+            "cpu_model": _cpu_model(), "blas": _blas_name()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_name():
+    try:
+        import numpy as np
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:  # numpy without the build-info dictionary
+        return None
+
+
+def decode_subrecord(mla, key, splits):
+    """decode_attn (and combine) of another DeepSeek-V2 workload, event-timed on its launch stream:
+    the latent-cache bytes over the decode_attn call as a fraction of the HBM peak."""
+    import numpy as np
+    import torch
+    from synth import get_config, make_case
+    cfg = get_config(key)
+    case = make_case(cfg, device="cuda")
+    caches = [build_cache(mla, case) for _ in range(1 if key == "3" else 2)]
+    step = mla.DecodeStep(cfg.dims, case.B, splits)
+    d = step.dims
+    mla.absorb_q(d, case.h, case.weights, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+    for c in caches:  # append the current rows (rotating copies, so q_pe itself is rotated once)
+        mla.rope(d, case.seq_lens, step.q_pe.clone(), step.kv_new.clone(), c)
+    mla.rope(d, case.seq_lens, step.q_pe, step.kv_new, None)
+    sigma_T = int(case.seq_lens.sum())
+    row_bytes = cfg.dims.row * (1 if cfg.cdtype == "fp8_e4m3" else 2) + (4 if cfg.cdtype == "fp8_e4m3" else 0)
+    n = 10
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n + 3)]
+    for i, e in enumerate(evs):
+        c = caches[i % len(caches)]
+        e[0].record()
+        mla.decode_attn(d, step.q_lat, step.q_pe, c, case.seq_lens, splits, step.ws_d)
+        e[1].record()
+        mla.combine(d, splits, case.seq_lens, step.ws_d, step.o_lat, step.lse)
+        e[2].record()
+    torch.cuda.synchronize()
+    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[3:]])) * 1e-3
+    t_comb = float(np.mean([e[1].elapsed_time(e[2]) for e in evs[3:]])) * 1e-3
+    cache_bytes = sigma_T * row_bytes
+    out = {"workload": f"config {cfg.key}: {cfg.title}", "sum_context_tokens": sigma_T,
+           "decode_attn_us": t_dec * 1e6, "combine_us": t_comb * 1e6,
+           "achieved_gbps": cache_bytes / t_dec / 1e9, "frac": cache_bytes / t_dec / 1e9 / HBM_PEAK_GBPS,
+           "traffic": DECODE_TRAFFIC_BYTES.get(key), "bytes_per_launch": cache_bytes,
+           "per_unit": f"{row_bytes} B per cached token x {sigma_T} tokens"}
+    del caches, case, step
+    torch.cuda.empty_cache()
+    return out
 
 
 def prefill_bench(args):
@@ -337,6 +400,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if cfg.key == "2" and not args.no_other_workloads and not args.precombined:
+        del caches
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {k: decode_subrecord(mla, k, args.splits) for k in ("3", "4", "4f8")}
     print(json.dumps(out), flush=True)
 
 
