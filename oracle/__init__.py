@@ -6,6 +6,7 @@ The GPU library never imports, links or calls it, and it shares no code with the
 from .encodings import (  # noqa: F401
     bf16_encode, bf16_decode, fp16_encode, fp16_decode, e4m3_encode, e4m3_decode,
     quantize_row_e4m3, quantize_rows_e4m3, store_rows, load_rows,
+    e2m3_encode, e2m3_decode, pack_e2m3, unpack_e2m3, quantize_rows_e2m3,
 )
 from .mla import (  # noqa: F401
     OracleDims, softmax, rope, rope_frequencies, score_scale, decode_step_explicit, decode_step_absorbed, decode_batch, prefill_chunk,

@@ -35,7 +35,7 @@ RUNNING_DIMS = Dims(d=512, n_h=8, d_h=64, d_c=128, d_cq=96, d_r=32)
 V2_DIMS = Dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
 
 # storage type names used across the repository
-STORAGE = ("f32", "f16", "bf16", "fp8_e4m3")
+STORAGE = ("f32", "f16", "bf16", "fp8_e4m3", "fp6_e2m3")
 
 
 @dataclass(frozen=True)
@@ -77,6 +77,9 @@ CONFIGS = {
                 4, ("fixed", 131072), sigma_h=1.0, sigma_w=0.006, seed=1004),
     "4f8": Config("4f8", "DeepSeek-V2 shape long context, B=4, T=131072, fp8 e4m3 cache + per-token scale",
                   V2_DIMS, "bf16", "fp8_e4m3", 4, ("fixed", 131072), sigma_h=1.0, sigma_w=0.006, seed=1005),
+    # the ~6-bit cache: e2m3 codes packed 6 bits each (432 bytes per row) + one float32 scale per token
+    "4f6": Config("4f6", "DeepSeek-V2 shape long context, B=4, T=131072, fp6 e2m3 cache (6 bits + per-token scale)",
+                  V2_DIMS, "bf16", "fp6_e2m3", 4, ("fixed", 131072), sigma_h=1.0, sigma_w=0.006, seed=1006),
 }
 
 # kappa for the score-stress variants: W^UQ and W^QR are scaled by kappa so that the scaled scores
@@ -86,7 +89,7 @@ CONFIGS = {
 #   std(c^KV) = std(k^R) = s_w s_h sqrt(d);  std(k^C) = s_w std(c^KV) sqrt(d_c)
 #   std(score) = sqrt(d_h std(q^C)^2 std(k^C)^2 + d_r std(q^R)^2 std(k^R)^2) / sqrt(d_h + d_r)
 # which is 0.0255 kappa at the V2 shape and 9.7e-6 kappa for the running model.
-STRESS_KAPPA = {"0": 2.2e5, "1": 2.2e5, "2": 80.0, "3": 80.0, "4": 80.0, "4f8": 80.0}
+STRESS_KAPPA = {"0": 2.2e5, "1": 2.2e5, "2": 80.0, "3": 80.0, "4": 80.0, "4f8": 80.0, "4f6": 80.0}
 
 
 def get_config(key: str, stress: bool = False, **overrides) -> Config:

@@ -43,8 +43,8 @@ class Case:
     seq_lens: torch.Tensor               # [B] int32, includes the current token
     t_cap: int                           # contiguous capacity (max T_b)
     # cache payload. For f32/f16/bf16: `rows` holds the stored rows (contiguous [B, t_cap, row] or
-    # paged pool [P, page, row]). For fp8: `rows32` holds float32 source rows in the same layout
-    # and each side quantises them with its own encoder.
+    # paged pool [P, page, row]). For fp8 / fp6: `rows32` holds float32 source rows in the same
+    # layout and each side quantises them with its own encoder.
     rows: Optional[torch.Tensor] = None
     rows32: Optional[torch.Tensor] = None
     block_table: Optional[torch.Tensor] = None   # [B, max_pages] int32, -1 = unused
@@ -116,7 +116,7 @@ def make_case(cfg: Config, device="cpu", B: Optional[int] = None, T=None, seed: 
 
     case = Case(cfg=cfg, weights=weights, h=h, seq_lens=seq_lens.to(device), t_cap=t_cap)
     row = dims.row
-    src_dt = torch.float32 if cfg.cdtype in ("f32", "fp8_e4m3") else TORCH_DTYPE[cfg.cdtype]
+    src_dt = torch.float32 if cfg.cdtype in ("f32", "fp8_e4m3", "fp6_e2m3") else TORCH_DTYPE[cfg.cdtype]
 
     # prefix rows are drawn on the target device (the large configs hold billions of values)
     gd = torch.Generator(device=device)
@@ -151,7 +151,7 @@ def make_case(cfg: Config, device="cpu", B: Optional[int] = None, T=None, seed: 
             buf[idx] = padded.view(npg, ps, row)
         case.block_table = bt.to(device)
         case.num_pages = P
-    if cfg.cdtype == "fp8_e4m3":
+    if cfg.cdtype in ("fp8_e4m3", "fp6_e2m3"):
         case.rows32 = buf
     else:
         case.rows = buf

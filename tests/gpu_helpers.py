@@ -11,6 +11,7 @@ TOL = {  # (rel-L2, max-abs) on u
     "f16": (5e-3, 2e-2),
     "bf16": (5e-3, 2e-2),
     "fp8_e4m3": (5e-3, 2e-2),
+    "fp6_e2m3": (5e-3, 2e-2),
 }
 
 
@@ -21,10 +22,10 @@ def build_cache(case):
         cache = mla.LatentCache.contiguous(case.B, case.t_cap, dims.row, cfg.cdtype)
     else:
         cache = mla.LatentCache.paged(case.num_pages, cfg.page_size, dims.row, cfg.cdtype, case.block_table)
-    if cfg.cdtype != "fp8_e4m3":
+    if cfg.cdtype not in ("fp8_e4m3", "fp6_e2m3"):
         cache.rows.copy_(case.rows)
         return cache
-    # fp8: the library's encoder writes codes + scales from the float32 source rows
+    # fp8 / fp6: the library's encoder writes codes + scales from the float32 source rows
     d = mla.Dims.of(dims)
     n_rows = (case.seq_lens - 1).to(torch.int32).contiguous()
     if cfg.layout == "contiguous":
@@ -52,6 +53,10 @@ def oracle_prefix(case, b):
         codes, scales = quantize_rows_e4m3(pre.float().cpu().numpy())
         from oracle import e4m3_decode
         return e4m3_decode(codes) * scales.astype(np.float64)[:, None]
+    if case.cfg.cdtype == "fp6_e2m3":
+        from oracle import e2m3_decode, quantize_rows_e2m3
+        codes, scales = quantize_rows_e2m3(pre.float().cpu().numpy())
+        return e2m3_decode(codes) * scales.astype(np.float64)[:, None]
     return pre.double().cpu().numpy()
 
 

@@ -94,3 +94,104 @@ def test_fp16_matches_torch():
     ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(fp16_encode(x), ref)
     assert np.array_equal(fp16_decode(ref), torch.from_numpy(ref.view(np.int16)).view(torch.float16).double().numpy())
+
+
+# ---------------------------------------------------------------- fp6 e2m3 (no torch type: the
+# format's definition and brute force are the references)
+def _e2m3_table():
+    """Every code's value written out from the definition: sign, exponent e (bias 1), mantissa m:
+    e = 0 -> m/8 (subnormal), else (1 + m/8) * 2^(e-1)."""
+    vals = {}
+    for c in range(64):
+        s, e, m = c >> 5, (c >> 3) & 3, c & 7
+        mag = m / 8.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 1)
+        vals[c] = -mag if s else mag
+    return vals
+
+
+def test_e2m3_decode_all_codes():
+    from oracle import e2m3_decode
+    tab = _e2m3_table()
+    codes = np.arange(64, dtype=np.uint8)
+    assert np.array_equal(e2m3_decode(codes), np.array([tab[c] for c in range(64)]))
+    mags = sorted({abs(v) for v in tab.values()})
+    assert len(mags) == 32 and mags[1] == 0.125 and mags[8] == 1.0 and mags[-1] == 7.5
+    assert np.signbit(e2m3_decode(np.array([0x20], dtype=np.uint8)))[0]    # -0 keeps its sign
+    # codes are monotonic in magnitude: neighbouring codes are neighbouring values
+    assert np.all(np.diff(e2m3_decode(np.arange(32, dtype=np.uint8))) > 0)
+
+
+def test_e2m3_encode_round_trip():
+    from oracle import e2m3_decode, e2m3_encode
+    codes = np.arange(64, dtype=np.uint8)
+    assert np.array_equal(e2m3_encode(e2m3_decode(codes).astype(np.float32)), codes)
+
+
+def _e2m3_brute(x):
+    """Nearest e2m3 value by exhaustive search over the 32 magnitudes, ties to the even code,
+    saturating at 7.5 (the reference the arithmetic encoder is pinned to)."""
+    mags = np.array([abs(v) for c, v in sorted(_e2m3_table().items()) if c < 32])
+    out = np.empty(len(x), dtype=np.uint8)
+    for i, v in enumerate(np.asarray(x, dtype=np.float64)):
+        a = min(abs(v), 7.5)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        out[i] = c | (0x20 if np.signbit(v) else 0)
+    return out
+
+
+def test_e2m3_encode_matches_brute_force():
+    from oracle import e2m3_encode
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        (rng.standard_normal(60000) * np.exp(rng.uniform(-6, 2.5, 60000))).astype(np.float32),
+        rng.uniform(-9, 9, 20000).astype(np.float32),
+    ])
+    assert np.array_equal(e2m3_encode(x), _e2m3_brute(x))
+
+
+def test_e2m3_ties_and_saturation():
+    from oracle import e2m3_decode, e2m3_encode
+    pos = e2m3_decode(np.arange(32, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (pos[:-1] + pos[1:]) / 2)     # exact in float32
+    got = e2m3_encode(mids).astype(np.int64)
+    lo = np.arange(31)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))           # the even neighbour
+    big = np.array([7.5, 7.74, 7.75, 8.0, 1e30, -7.76, -1e30, np.inf, -np.inf], dtype=np.float32)
+    assert list(e2m3_encode(big)) == [0x1F, 0x1F, 0x1F, 0x1F, 0x1F, 0x3F, 0x3F, 0x1F, 0x3F]
+    assert e2m3_encode(np.array([np.nan], dtype=np.float32))[0] == 0
+
+
+def test_e2m3_packing_bit_positions():
+    from oracle import pack_e2m3, unpack_e2m3
+    # code j sits at bits 6j .. 6j + 5 of a little-endian stream
+    for j in range(8):
+        c = np.zeros(8, dtype=np.uint8)
+        c[j] = 0x3F
+        p = pack_e2m3(c).astype(np.int64)
+        stream = sum(int(b) << (8 * i) for i, b in enumerate(p))
+        assert stream == 0x3F << (6 * j), j
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 64, (7, 576), dtype=np.uint8)
+    p = pack_e2m3(codes)
+    assert p.shape == (7, 432)
+    assert np.array_equal(unpack_e2m3(p, 576), codes)
+
+
+def test_quantize_rows_e2m3_scale_and_error_bound():
+    from oracle import e2m3_decode, quantize_rows_e2m3
+    rng = np.random.default_rng(13)
+    rows = (rng.standard_normal((64, 576)) * 0.4).astype(np.float32)
+    rows[5] = 0.0
+    codes, scales = quantize_rows_e2m3(rows)
+    assert scales[5] == 1.0 and np.all(codes[5] == 0)
+    amax = np.abs(rows).max(1)
+    nz = amax > 0
+    assert np.array_equal(scales[nz], (amax[nz] / np.float32(7.5)).astype(np.float32))
+    deq = e2m3_decode(codes) * scales[:, None].astype(np.float64)
+    # at most half a spacing: 2^-4 relative for normals, 2^-4 * scale absolute below 1 * scale
+    bound = np.maximum(np.abs(rows) * 2.0 ** -4, 2.0 ** -4 * scales[:, None]) * (1 + 1e-6)
+    assert np.all(np.abs(deq - rows) <= bound)
+    assert np.all(np.abs(e2m3_decode(codes)).max(1)[nz] == 7.5)

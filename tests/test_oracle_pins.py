@@ -29,6 +29,7 @@ def _rand_weights(dims, rng, sw=0.3, kappa=1.0):
 
 
 SMALL = OracleDims(d=24, n_h=3, d_h=4, d_c=6, d_cq=5, d_r=4)
+SMALL6 = OracleDims(d=24, n_h=3, d_h=4, d_c=8, d_cq=5, d_r=4)   # rows of whole 6-bit groups (12 codes)
 
 
 # ---------------------------------------------------------------- printed values on the pages
@@ -158,6 +159,7 @@ def test_absorption_identity_both_ways():
     (SMALL, 1, "f32"), (SMALL, 9, "f32"), (SMALL, 9, "bf16"), (SMALL, 9, "fp8_e4m3"),
     (OracleDims.of(RUNNING_DIMS), 33, "f16"), (OracleDims.of(RUNNING_DIMS), 64, "f32"),
     (OracleDims.of(V2_DIMS), 5, "bf16"), (OracleDims.of(V2_DIMS), 3, "fp8_e4m3"),
+    (SMALL6, 9, "fp6_e2m3"), (OracleDims.of(V2_DIMS), 4, "fp6_e2m3"),
 ])
 def test_explicit_equals_absorbed(dims, T, cdtype):
     """An independent formulation (scores against the latent with W^UK absorbed into the query,
