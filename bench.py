@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="2", help="workload key (2, 3, 4, 4f8)")
+    ap.add_argument("--config", default="2", help="workload key (0, 1, 2, 3, 4, 4f8, 4f6)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode ranges (0 = the library's default: one per CU at the V2 shape, two otherwise)")
     ap.add_argument("--rotate", type=int, default=2, help="cache copies cycled through")
@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the decode_attn sub-records of the other DeepSeek-V2 workloads (configs 3, 4, 4f8)")
+                    help="skip the decode_attn sub-records of the other DeepSeek-V2 workloads (configs 3, 4, 4f8, 4f6)")
     ap.add_argument("--prefill", type=int, default=0, metavar="C",
                     help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
                          "(a separate JSON line; the default run is the decode step)")
@@ -79,7 +79,7 @@ def build_cache(mla, case):
         cache = mla.LatentCache.contiguous(case.B, case.t_cap, dims.row, cfg.cdtype)
     else:
         cache = mla.LatentCache.paged(case.num_pages, cfg.page_size, dims.row, cfg.cdtype, case.block_table)
-    if cfg.cdtype != "fp8_e4m3":
+    if cfg.cdtype not in ("fp8_e4m3", "fp6_e2m3"):
         cache.rows.copy_(case.rows)
     else:
         n_rows = (case.seq_lens - 1).to(torch.int32).contiguous()
@@ -102,6 +102,10 @@ def cpu_baseline(case, budget_s):
             from oracle import e4m3_decode, quantize_rows_e4m3
             codes, sc = quantize_rows_e4m3(pre.float().cpu().numpy())
             pre64 = e4m3_decode(codes) * sc.astype(np.float64)[:, None]
+        elif case.cfg.cdtype == "fp6_e2m3":
+            from oracle import e2m3_decode, quantize_rows_e2m3
+            codes, sc = quantize_rows_e2m3(pre.float().cpu().numpy())
+            pre64 = e2m3_decode(codes) * sc.astype(np.float64)[:, None]
         else:
             pre64 = pre.double().cpu().numpy()
         decode_step_explicit(W, case.h[b].double().cpu().numpy(), pre64, od, case.cfg.cdtype)
@@ -152,7 +156,7 @@ def decode_subrecord(mla, key, splits):
         mla.rope(d, case.seq_lens, step.q_pe.clone(), step.kv_new.clone(), c)
     mla.rope(d, case.seq_lens, step.q_pe, step.kv_new, None)
     sigma_T = int(case.seq_lens.sum())
-    row_bytes = cfg.dims.row * (1 if cfg.cdtype == "fp8_e4m3" else 2) + (4 if cfg.cdtype == "fp8_e4m3" else 0)
+    row_bytes = mla.row_bytes(cfg.cdtype, cfg.dims.row) + (4 if cfg.cdtype in ("fp8_e4m3", "fp6_e2m3") else 0)
     n = 10
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n + 3)]
     for i, e in enumerate(evs):
@@ -283,7 +287,7 @@ def main():
     W, h, seq_lens = case.weights, case.h, case.seq_lens
     d = step.dims
     sigma_T = int(seq_lens.sum())
-    row_bytes = dims.row * (1 if cfg.cdtype == "fp8_e4m3" else 2) + (4 if cfg.cdtype == "fp8_e4m3" else 0)
+    row_bytes = mla.row_bytes(cfg.cdtype, dims.row) + (4 if cfg.cdtype in ("fp8_e4m3", "fp6_e2m3") else 0)
     cache_bytes = sigma_T * row_bytes
     flops_attn = sigma_T * 2 * dims.n_h * (dims.row + dims.d_c)
     wsz = {k: v.numel() * v.element_size() for k, v in case.weights.items()}
@@ -403,7 +407,7 @@ def main():
     if cfg.key == "2" and not args.no_other_workloads and not args.precombined:
         del caches
         torch.cuda.empty_cache()
-        out["other_workloads"] = {k: decode_subrecord(mla, k, args.splits) for k in ("3", "4", "4f8")}
+        out["other_workloads"] = {k: decode_subrecord(mla, k, args.splits) for k in ("3", "4", "4f8", "4f6")}
     print(json.dumps(out), flush=True)
 
 

@@ -62,8 +62,11 @@ typedef enum {
   MLA_F32 = 0,       /* IEEE binary32 */
   MLA_F16 = 1,       /* IEEE binary16 */
   MLA_BF16 = 2,      /* bfloat16 */
-  MLA_FP8_E4M3 = 3   /* OCP e4m3 (max 448, no inf) codes + one float32 scale per cached token;
+  MLA_FP8_E4M3 = 3,  /* OCP e4m3 (max 448, no inf) codes + one float32 scale per cached token;
                         cache storage only */
+  MLA_FP6_E2M3 = 4   /* OCP FP6 E2M3 codes (max 7.5, no inf / NaN) packed 6 bits each, as a
+                        little-endian bit stream per row (code j at bits 6j..6j+5), + one float32
+                        scale per cached token; cache storage only */
 } mla_dtype;
 
 typedef enum {
@@ -107,7 +110,10 @@ typedef struct {
  *      block_table is device int32 [B, max_pages]; unused entries may hold -1.
  *  dtype MLA_FP8_E4M3: rows holds uint8 codes and scales holds one float32 per row with the
  *      same indexing (scales[(b * t_cap + j)] or scales[page * page_size + slot]); value =
- *      code * scale. scales must be NULL for the other dtypes.
+ *      code * scale. The scale is amax / 448 of the row (1 for an all-zero row).
+ *  dtype MLA_FP6_E2M3: rows are (d_c + d_r) * 6 / 8 bytes (the packed codes; 432 bytes at
+ *      d_c + d_r = 576) with the same row indexing; scales as for fp8, amax / 7.5 of the row.
+ *  scales must be NULL for the other dtypes.
  * The struct itself is read on the host during the call; it need not outlive the call. */
 typedef struct {
   void* rows;
@@ -145,7 +151,8 @@ MLA_API mla_status mla_absorb_q(const mla_dims* dims, int32_t B, int32_t wdtype,
  *   seq_lens: device int32 [B]; pos_b = seq_lens[b] - 1.
  *   q_pe [B, n_h, d_r] and the k^R part of kv_new [B, d_c + d_r] are rotated IN PLACE.
  *   cache: if non-NULL, row [c^KV | k^R] of each sequence is written to slot pos_b, rounded to
- *   the cache dtype (RNE; fp8: per-token scale amax/448 and saturating RNE codes).
+ *   the cache dtype (RNE; fp8 / fp6: per-token scale amax/448 or amax/7.5 and saturating RNE
+ *   codes).
  *   A sequence with seq_lens[b] == 0 (outside the contract) is left alone: its q_pe and kv_new
  *   rows are not rotated and nothing is written to the cache. */
 MLA_API mla_status mla_rope(const mla_dims* dims, int32_t B, const int32_t* seq_lens, float* q_pe,

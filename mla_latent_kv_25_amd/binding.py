@@ -17,7 +17,11 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
-STORAGE_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "fp8_e4m3": FP8_E4M3}
+FP6_E2M3 = 4
+STORAGE_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "fp8_e4m3": FP8_E4M3, "fp6_e2m3": FP6_E2M3}
+# bytes of one cached row of `row` elements in each storage type
+def row_bytes(dtype: str, row: int) -> int:
+    return {"f32": 4 * row, "f16": 2 * row, "bf16": 2 * row, "fp8_e4m3": row, "fp6_e2m3": row * 6 // 8}[dtype]
 
 
 class MLAError(RuntimeError):
@@ -120,7 +124,8 @@ def _stream():
 @dataclass
 class LatentCache:
     """Device buffers of one layer's latent cache (see mla_cache in include/mla.h)."""
-    rows: torch.Tensor                       # [B, t_cap, row] or [P, page, row]; uint8 codes for fp8
+    rows: torch.Tensor                       # [B, t_cap, row] or [P, page, row]; uint8 codes for fp8,
+                                             # [.., row * 6 / 8] packed bytes for fp6
     dtype: str                               # "f32" | "f16" | "bf16" | "fp8_e4m3"
     t_cap: int
     scales: Optional[torch.Tensor] = None    # fp8: float32 per row
@@ -129,8 +134,8 @@ class LatentCache:
 
     @classmethod
     def contiguous(cls, B, t_cap, row, dtype, device="cuda"):
-        if dtype == "fp8_e4m3":
-            return cls(torch.zeros((B, t_cap, row), dtype=torch.uint8, device=device), dtype, t_cap,
+        if dtype in ("fp8_e4m3", "fp6_e2m3"):
+            return cls(torch.zeros((B, t_cap, row_bytes(dtype, row)), dtype=torch.uint8, device=device), dtype, t_cap,
                        scales=torch.ones((B, t_cap), dtype=torch.float32, device=device))
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
         return cls(torch.zeros((B, t_cap, row), dtype=tdt, device=device), dtype, t_cap)
@@ -138,8 +143,8 @@ class LatentCache:
     @classmethod
     def paged(cls, num_pages, page_size, row, dtype, block_table, device="cuda"):
         max_pages = int(block_table.shape[1])
-        if dtype == "fp8_e4m3":
-            return cls(torch.zeros((num_pages, page_size, row), dtype=torch.uint8, device=device), dtype,
+        if dtype in ("fp8_e4m3", "fp6_e2m3"):
+            return cls(torch.zeros((num_pages, page_size, row_bytes(dtype, row)), dtype=torch.uint8, device=device), dtype,
                        max_pages * page_size, scales=torch.ones((num_pages, page_size), dtype=torch.float32,
                                                                device=device),
                        block_table=block_table, page_size=page_size)

@@ -35,7 +35,9 @@ mla_status hip_status(hipError_t e, const char* what) {
 }
 
 bool valid_wdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16; }
-bool valid_cdtype(int32_t t) { return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+bool valid_cdtype(int32_t t) {
+  return t == MLA_F32 || t == MLA_F16 || t == MLA_BF16 || t == MLA_FP8_E4M3 || t == MLA_FP6_E2M3;
+}
 
 // Kernels use 16-byte vector accesses on tensors and workspaces (16-byte alignment required);
 // int32 / float arrays read element by element (lengths, block tables, scales) need 4 bytes.
@@ -70,8 +72,8 @@ mla_status check_cache(const mla_cache* c, const char* fn, mla::CacheArgs* out) 
   if (!valid_cdtype(c->dtype)) return fail(MLA_E_ARG, "%s: bad cache dtype %d", fn, c->dtype);
   if (misaligned(c->rows) || misaligned4(c->scales, c->block_table))
     return fail(MLA_E_ARG, "%s: cache pointers must be 16-byte aligned", fn);
-  if ((c->dtype == MLA_FP8_E4M3) != (c->scales != nullptr))
-    return fail(MLA_E_ARG, "%s: scales must be given exactly for the fp8 cache", fn);
+  if ((c->dtype == MLA_FP8_E4M3 || c->dtype == MLA_FP6_E2M3) != (c->scales != nullptr))
+    return fail(MLA_E_ARG, "%s: scales must be given exactly for the fp8 and fp6 caches", fn);
   if (c->page_size < 0) return fail(MLA_E_ARG, "%s: page_size < 0", fn);
   if (c->page_size == 0) {
     if (c->t_cap < 1) return fail(MLA_E_ARG, "%s: contiguous cache needs t_cap >= 1", fn);

@@ -90,6 +90,36 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// OCP FP6 E2M3 (sign, 2 exponent bits with bias 1, 3 mantissa bits, subnormals m/8, largest
+// 7.5, no infinity or NaN): code (low 6 bits) -> value, exact in float32.
+__device__ __forceinline__ float e2m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 3u, m = c & 7u;
+  const float v = e == 0 ? (float)m * 0.125f : __builtin_bit_cast(float, ((e + 126u) << 23) | (m << 20));
+  return (c & 0x20u) ? -v : v;
+}
+
+// float32 -> e2m3 code: round to nearest even on the exact binary value, saturate at +-7.5; NaN
+// (which the format cannot hold) -> +0.
+__device__ __forceinline__ uint32_t f32_to_e2m3(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 26) & 0x20u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0u;                          // NaN
+  if (a >= 0x40f00000u) return sign | 0x1fu;              // >= 7.5 (incl. inf): saturate
+  const int e = (int)(a >> 23) - 127;                      // a in [2^e, 2^(e+1)), e <= 2
+  if (e < 0) {
+    // below 1: the grid is k/8, k in [0, 8]; exact scaling by 8, then integer RNE
+    const float q = __builtin_rintf(__builtin_bit_cast(float, a) * 8.0f);
+    return sign | (uint32_t)q;                             // q == 8 is code 8 = 1.0
+  }
+  const uint32_t mant = a & 0x7fffffu;
+  const uint32_t keep = mant >> 20, rest = mant & 0xfffffu, half = 0x80000u;
+  uint32_t code = ((uint32_t)(e + 1) << 3) | keep;
+  if (rest > half || (rest == half && (keep & 1u))) code += 1;  // may carry into the exponent
+  if (code > 0x1fu) code = 0x1fu;
+  return sign | code;
+}
+
 // ------------------------------------------------------------------ typed element access
 template <int DT> struct Elem;
 // ld: load and widen; cvt: widen stored bits (kept raw while a load is in flight, so that the

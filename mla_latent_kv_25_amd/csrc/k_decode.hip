@@ -828,6 +828,24 @@ constexpr int PB = v2::NH * v2::TT * 2;    // bytes of P of one tile
 constexpr int LDS_BYTES = NBUF * TILEB + 2 * PB;
 }  // namespace f8
 
+// The same kernel over fp6 e2m3 caches: rows of 576 codes packed 6 bits each (432 bytes) are
+// copied into a ring of packed slots, and each tile is converted once, exactly, into the e4m3 tile
+// layout above (every e2m3 value is an e4m3 value) in one of two e4m3 buffers; the scores, softmax
+// and PV then run as for an fp8 cache. A packed slot holds the 32 rows, 512 bytes that absorb the
+// copy lanes past the last row, and the two token-scale slots.
+namespace f6 {
+constexpr int RB = 432;                    // bytes of one packed row
+constexpr int CH = RB / 16;                // 16-byte chunks per row (27)
+constexpr int ROWSB = v2::TT * RB;         // 13824 (864 chunks: 13.5 copies of 1 KB)
+constexpr int SCO = ROWSB + 512;           // token-scale slots
+constexpr int SLOTB = SCO + 512;           // 14848
+constexpr int NBUF = 7;
+constexpr int LOADS = 4;                   // copy instructions per wave per tile
+constexpr int EB = v2::TT * f8::RB;        // one e4m3 tile (18432)
+constexpr int LDS_BYTES = NBUF * SLOTB + 2 * EB + 2 * f8::PB;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+}  // namespace f6
+
 // 16-byte chunk c of fp8 tile row t sits at chunk position (c & ~3) | ((c & 3) ^ key8(t)) (rows of
 // 36 chunks, so the XOR stays inside the aligned group of 4). With rows 576 bytes apart, row t
 // starts at bank group 4t mod 16; the key separates rows t, t+4, t+8, t+12, so the 16 rows of a
@@ -893,7 +911,10 @@ __device__ __forceinline__ bf16x8 widen8(u32x2 r) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <bool PAGED>
+// LDS-only barrier: waits for this wave's LDS operations (not for its in-flight global->LDS copies)
+__device__ __forceinline__ void lds_sync_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool PAGED, bool FP6>
 __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict__ qop,
                                                       const float* __restrict__ fh_in, CacheArgs cache,
                                                       const int32_t* __restrict__ seq_lens, int B, int G,
@@ -902,19 +923,24 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
                                                       float* __restrict__ sc_part,
                                                       uint16_t* __restrict__ o_part) {
   using namespace v2;
-  using f8::RB;
-  using f8::TILEB;
-  using f8::ROWSB;
+  using f8::RB;        // e4m3 row bytes in LDS
   using f8::KB;
-  constexpr int NBUF = f8::NBUF, AHEAD = f8::AHEAD, LOADS8 = f8::LOADS, PB = f8::PB;
+  // HRB: bytes of one cached row in HBM (and in the copy slots); SLOTB: one copy slot; SCO: offset
+  // of its token-scale slots
+  constexpr int HRB = FP6 ? f6::RB : f8::RB, HCH = FP6 ? f6::CH : f8::CH;
+  constexpr int SLOTB = FP6 ? f6::SLOTB : f8::TILEB, SCO = FP6 ? f6::SCO : f8::ROWSB;
+  constexpr int NBUF = FP6 ? f6::NBUF : f8::NBUF, AHEAD = NBUF - 2, LOADS8 = FP6 ? f6::LOADS : f8::LOADS;
+  constexpr int PB = f8::PB;
+  constexpr int LDS_BYTES = FP6 ? f6::LDS_BYTES : f8::LDS_BYTES;
   constexpr float HEAD = 64.f;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[f8::LDS_BYTES];
-  uint8_t* const lds_p = lds + NBUF * TILEB;  // P of two consecutive tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  uint8_t* const ebase = lds + NBUF * SLOTB;              // fp6: the two converted e4m3 tiles
+  uint8_t* const lds_p = ebase + (FP6 ? 2 * f6::EB : 0);  // P of two consecutive tiles
   int* const redo_flag = (int*)lds;
   float* const lds_l = (float*)(lds + 16);
   float (*const lds_m)[NH] = (float (*)[NH])(lds + 16 + NH * 4);
   constexpr int OTR = 272;
-  static_assert(4096 + 4 * NH * OTR <= f8::LDS_BYTES, "partial staging exceeds the tile ring");
+  static_assert(4096 + 4 * NH * OTR <= LDS_BYTES, "partial staging exceeds the tile ring");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int g = lane >> 5, l32 = lane & 31;
@@ -955,14 +981,27 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
   // copy the 32 token scales (each into its own slot, so that every wave issues 5 copies per
   // tile). Row chunk R, lane L fills LDS chunk 64R + L = row t, position pos: source chunk
   // (pos & ~3) | ((pos & 3) ^ key8(t)) of row t. Offsets are < 2^16: two per register.
+  // fp6: the packed rows are copied as they are (LDS chunk 64R + L from source chunk 64R + L):
+  // wave w moves R = w + 4i (i < 3) and, for w < 2, R = 12 + w; waves 2 and 3 copy the scales, so
+  // every wave issues 4 copies. The 32 lanes of R = 13 past the 864 chunks of the rows re-read the
+  // last chunk into the slot's 512-byte pad.
   uint32_t doff2[3] = {0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < LOADS8; ++i) {
-    const int R = i < 4 ? w + 4 * i : 16 + w;
-    if (R < 18) {
-      const int f = 64 * R + lane, t = f / f8::CH, pos = f - t * f8::CH;
-      const uint32_t o = (uint32_t)(t * RB + (((pos & ~3) | ((pos & 3) ^ key8(t))) << 4));
-      doff2[i >> 1] |= o << (16 * (i & 1));
+    if constexpr (FP6) {
+      const int R = i < 3 ? w + 4 * i : 12 + w;
+      if (R < 14) {
+        const int f = 64 * R + lane;
+        const uint32_t o = (uint32_t)((f < 864 ? f : 863) << 4);
+        doff2[i >> 1] |= o << (16 * (i & 1));
+      }
+    } else {
+      const int R = i < 4 ? w + 4 * i : 16 + w;
+      if (R < 18) {
+        const int f = 64 * R + lane, t = f / f8::CH, pos = f - t * f8::CH;
+        const uint32_t o = (uint32_t)(t * RB + (((pos & ~3) | ((pos & 3) ^ key8(t))) << 4));
+        doff2[i >> 1] |= o << (16 * (i & 1));
+      }
     }
   }
 
@@ -996,9 +1035,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
       cp.tt0 = tt0;
       cp.last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
       cp.dst = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * TILEB));
+          (uint32_t)(uintptr_t)(MLA_LDS void*)(lds + (it % NBUF) * SLOTB));
       if constexpr (!PAGED) {
-        cp.b0 = rows_b + (rows.base_row + tt0) * RB;
+        cp.b0 = rows_b + (rows.base_row + tt0) * HRB;
         cp.b1 = cp.b0;
         cp.sc0 = cache.scales + rows.base_row + tt0;
         cp.split = 0xffffffffu;
@@ -1006,29 +1045,31 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
         rows.tile(tt0, tt0 + cp.last);
         const int ps = 1 << rows.ps_shift;
         const int s_in = (int)(tt0 & (ps - 1));
-        cp.split = (uint32_t)(ps - s_in) * RB;
-        cp.b0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * RB;
-        cp.b1 = rows_b + (int64_t)rows.pg1 * ps * RB - (int64_t)cp.split;
+        cp.split = (uint32_t)(ps - s_in) * HRB;
+        cp.b0 = rows_b + ((int64_t)rows.pg0 * ps + s_in) * HRB;
+        cp.b1 = rows_b + (int64_t)rows.pg1 * ps * HRB - (int64_t)cp.split;
         cp.sc0 = cache.scales;
       }
       return cp;
     };
-    // copy i of this wave for the planned tile; `partial` as in the bf16 kernel
+    // copy i of this wave for the planned tile; `partial` as in the bf16 kernel (a chunk of a row
+    // past the segment's last row re-reads the same chunk of the last row)
+    constexpr int NROWCP = FP6 ? 3 : 4;  // row copies every wave issues; waves 0 and 1 add one more
     auto copy = [&](const CopyPlan& cp, int i, bool partial) __attribute__((always_inline)) {
-      if (i < 4 || wu < 2) {
+      if (i < NROWCP || wu < 2) {
         uint32_t d2 = doff2[i >> 1];
         asm volatile("" : "+v"(d2));
         uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
         if (partial && cp.last < TT - 1) {
-          const int t = (int)(off / RB);
-          if (t > cp.last) off -= (uint32_t)(t - cp.last) * RB;
+          const int t = (int)(off / HRB);
+          if (t > cp.last) off -= (uint32_t)(t - cp.last) * HRB;
         }
-        const uint32_t dst = cp.dst + 1024u * (uint32_t)(i < 4 ? wu + 4 * i : 16 + wu);
+        const uint32_t dst = cp.dst + 1024u * (uint32_t)(i < NROWCP ? wu + 4 * i : 4 * NROWCP + wu);
         if constexpr (!PAGED) dma16_s(cp.b0, off, dst);
         else dma16((off < cp.split ? cp.b0 : cp.b1) + off, dst);
       } else {
         const int tk = l32 < cp.last ? l32 : cp.last;
-        const uint32_t dst = cp.dst + (uint32_t)ROWSB + 256u * (uint32_t)(wu - 2);
+        const uint32_t dst = cp.dst + (uint32_t)SCO + 256u * (uint32_t)(wu - 2);
         if constexpr (!PAGED) dma4_s(cp.sc0, 4u * (uint32_t)tk, dst);
         else dma4(cp.sc0 + rows.row(cp.tt0 + tk), dst);
       }
@@ -1102,7 +1143,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
       // slot one group ahead, into cg[q & 1] (group 0 during the scores).
       f32x16 S;
       f32x4 cg[2];
-      const float* sct = (const float*)(lds + ROWSB);  // scale slot of the tile being softmaxed
+      const float* sct = (const float*)(lds + SCO);  // scale slot of the tile being softmaxed
       float rs = 0.f;
       int valid = TT;
       uint8_t* pw = lds_p;
@@ -1209,9 +1250,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
       // next steps need first is fetched well ahead of use: the kk = 0 V fragments of tile tv
       // (read, then widened one per MFMA), the first P fragment of PV (from pr), and the
       // coefficients c_r of tile tn.
-      auto scores = [&](const uint8_t* tn, const uint8_t* tv, const uint8_t* pr, bf16x8 (&av)[4], bf16x8& p0,
-                        auto&& copies) __attribute__((always_inline)) {
-        sct = (const float*)(tn + ROWSB);
+      auto scores = [&](const uint8_t* tn, const uint8_t* sn, const uint8_t* tv, const uint8_t* pr, bf16x8 (&av)[4],
+                        bf16x8& p0, auto&& copies) __attribute__((always_inline)) {
+        sct = (const float*)sn;
         uint32_t vb[2][2];
         vbase(tv, vb);
         u32x2 rv[4];
@@ -1231,10 +1272,50 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
         });
       };
 
-      auto tile_buf = [&](int it) -> const uint8_t* { return lds + (it % NBUF) * TILEB; };
+      // e4m3 rows of tile j (fp8: its copy slot; fp6: converted buffer j & 1) and its token scales
+      auto tile_buf = [&](int it) -> const uint8_t* {
+        if constexpr (FP6) return ebase + (it & 1) * f6::EB;
+        else return lds + (it % NBUF) * SLOTB;
+      };
+      auto scale_buf = [&](int it) -> const uint8_t* { return lds + (it % NBUF) * SLOTB + SCO; };
+      // fp6: the packed rows of tile j -> the e4m3 layout of buffer j & 1 (exact: every e2m3 value
+      // is an e4m3 value); group = 32 codes of one row (24 packed bytes -> two 16-byte chunks).
+      // Every wave must be past the last reads of that buffer (PV of tile j - 2) and every copy of
+      // tile j must have landed: the callers run it right after the barrier that ensures both.
+      auto convert = [&](int j) __attribute__((always_inline)) {
+        if constexpr (FP6) {
+          typedef int i32x6 __attribute__((ext_vector_type(6)));
+          typedef float f32x32 __attribute__((ext_vector_type(32)));
+          const uint8_t* ps = lds + (j % NBUF) * SLOTB;
+          uint8_t* eb = ebase + (j & 1) * f6::EB;
+          for (int gi = tid; gi < TT * 18; gi += 256) {
+            const int t = gi / 18, kb = gi - 18 * t;
+            const uint8_t* src = ps + t * f6::RB + kb * 24;
+            const u32x2 a0 = *(const u32x2*)src, a1 = *(const u32x2*)(src + 8), a2 = *(const u32x2*)(src + 16);
+            const i32x6 x = {(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y};
+            const f32x32 f = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(x, 1.0f);
+            uint32_t wd[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              int hw = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * q], f[4 * q + 1], 0, false);
+              hw = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * q + 2], f[4 * q + 3], hw, true);
+              wd[q] = (uint32_t)hw;
+            }
+            const int kx = key8(t);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int cc = 2 * kb + h;
+              *(u32x4*)(eb + t * RB + (((cc & ~3) | ((cc & 3) ^ kx)) << 4)) =
+                  u32x4{wd[4 * h], wd[4 * h + 1], wd[4 * h + 2], wd[4 * h + 3]};
+            }
+          }
+          lds_sync_barrier();
+        }
+      };
       bf16x8 av[4], p0;
       wait_tile(0, (AHEAD < ntiles - 1 ? AHEAD : ntiles - 1));
-      scores(lds, lds, lds_p, av, p0, [](int) {});
+      convert(0);
+      scores(tile_buf(0), scale_buf(0), tile_buf(0), lds_p, av, p0, [](int) {});
       valid = valid_of(0);
       mask_tail();
       if (pass == 0) set_ref();
@@ -1250,20 +1331,22 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
         const uint8_t* pr = lds_p + (it & 1) * PB;
         const uint8_t* tv = tile_buf(it);
         if (it + 1 < ntiles) {
+          convert(it + 1);
           const uint8_t* tn = tile_buf(it + 1);
+          const uint8_t* sn = scale_buf(it + 1);
           if (it + AHEAD + 1 < ntiles) {
             const CopyPlan cp = plan_tile(it + AHEAD + 1);
             if (cp.last < TT - 1) {
-              scores(tn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
+              scores(tn, sn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
                 if (j % 3 == 1 && j / 3 < LOADS8) copy(cp, j / 3, true);
               });
             } else {
-              scores(tn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
+              scores(tn, sn, tv, pr, av, p0, [&](int j) __attribute__((always_inline)) {
                 if (j % 3 == 1 && j / 3 < LOADS8) copy(cp, j / 3, false);
               });
             }
           } else {
-            scores(tn, tv, pr, av, p0, [](int) {});
+            scores(tn, sn, tv, pr, av, p0, [](int) {});
           }
         } else {
           uint32_t vb[2][2];
@@ -1367,10 +1450,18 @@ constexpr int OPT = 16;  // outputs per thread
 
 // Raw stored bits of one element, and their value (fp8: times the row's scale). Loads keep the raw
 // bits so that no conversion waits on a load before the next ones are issued.
+// fp6 rows are rw * 6 / 8 bytes: code e sits at bits 6e .. 6e + 5 of the row's little-endian
+// stream, i.e. in byte 6e / 8 and (for a shift above 2) the next byte, which is then inside the row.
 template <int CDT>
 __device__ __forceinline__ uint32_t cache_bits(const CacheArgs& c, int64_t ridx, int rw, int e) {
   if constexpr (CDT == MLA_F32) return ((const uint32_t*)c.rows)[ridx * rw + e];
   else if constexpr (CDT == MLA_F16 || CDT == MLA_BF16) return ((const uint16_t*)c.rows)[ridx * rw + e];
+  else if constexpr (CDT == MLA_FP6_E2M3) {
+    const uint8_t* row = (const uint8_t*)c.rows + ridx * (rw / 4 * 3);
+    const int bit = 6 * e, byte = bit >> 3, sh = bit & 7;
+    const int nxt = sh > 2 ? byte + 1 : byte;
+    return (((uint32_t)row[byte] | ((uint32_t)row[nxt] << 8)) >> sh) & 63u;
+  }
   else return ((const uint8_t*)c.rows)[ridx * rw + e];
 }
 template <int CDT>
@@ -1378,16 +1469,10 @@ __device__ __forceinline__ float bits_value(uint32_t x, float sc) {
   if constexpr (CDT == MLA_F32) return __builtin_bit_cast(float, x);
   else if constexpr (CDT == MLA_F16) return f16_bits_to_f32((uint16_t)x);
   else if constexpr (CDT == MLA_BF16) return bf16_bits_to_f32((uint16_t)x);
+  else if constexpr (CDT == MLA_FP6_E2M3) return e2m3_to_f32(x) * sc;
   else return e4m3_to_f32(x) * sc;
 }
 
-template <int CDT>
-__device__ __forceinline__ float cache_elem(const CacheArgs& c, int64_t ridx, int rw, int e) {
-  if constexpr (CDT == MLA_F32) return ((const float*)c.rows)[ridx * rw + e];
-  else if constexpr (CDT == MLA_F16) return f16_bits_to_f32(((const uint16_t*)c.rows)[ridx * rw + e]);
-  else if constexpr (CDT == MLA_BF16) return bf16_bits_to_f32(((const uint16_t*)c.rows)[ridx * rw + e]);
-  else return e4m3_to_f32(((const uint8_t*)c.rows)[ridx * rw + e]) * c.scales[ridx];
-}
 
 template <int CDT, int EPL, bool PAGED>
 __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_r,
@@ -1458,7 +1543,7 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
       // every load is issued (indices past the row clamp to its last element), none behind a branch
 #pragma unroll
       for (int m = 0; m < RPW; ++m) {
-        if constexpr (CDT == MLA_FP8_E4M3) vsc[m] = cache.scales[ridx[m]];
+        if constexpr (CDT == MLA_FP8_E4M3 || CDT == MLA_FP6_E2M3) vsc[m] = cache.scales[ridx[m]];
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = lane + 64 * j;
@@ -1475,7 +1560,9 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = lane + 64 * j;
-          if (e < rw) ts[(w + 4 * m) * rwp + e] = bits_value<CDT>(v[m][j], CDT == MLA_FP8_E4M3 ? vsc[m] : 1.f);
+          if (e < rw)
+            ts[(w + 4 * m) * rwp + e] =
+                bits_value<CDT>(v[m][j], (CDT == MLA_FP8_E4M3 || CDT == MLA_FP6_E2M3) ? vsc[m] : 1.f);
         }
       lds_barrier();
       if (tb + TT < t1) fetch(tb + TT);  // in flight while this tile is processed
@@ -1795,7 +1882,7 @@ static bool is_v2(const mla_dims& d) { return d.n_h == v2::NH && d.d_c == v2::DC
 static bool v2_page_ok(int ps) { return ps == 0 || (ps >= 32 && (ps & (ps - 1)) == 0); }
 
 bool decode_supported(const mla_dims& d, int cdt, int page_size) {
-  if (is_v2(d) && (cdt == MLA_BF16 || cdt == MLA_FP8_E4M3)) return v2_page_ok(page_size);
+  if (is_v2(d) && (cdt == MLA_BF16 || cdt == MLA_FP8_E4M3 || cdt == MLA_FP6_E2M3)) return v2_page_ok(page_size);
   const int rw = d.d_c + d.d_r;
   return d.n_h * rw <= 16384 && rw <= 512 && d.n_h <= 64 && d.n_h * d.d_c <= 256 * gen::OPT;
 }
@@ -1810,12 +1897,12 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
   int32_t* fmt = (int32_t*)(base + L.off_fmt);
   float* lse_part = (float*)(base + L.off_lse);
   float* o_part = (float*)(base + L.off_o);
-  const bool mfma = is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3);
+  const bool mfma = is_v2(d) && (c.dtype == MLA_BF16 || c.dtype == MLA_FP8_E4M3 || c.dtype == MLA_FP6_E2M3);
   const float qscale = sm_scale * 1.44269504088896340736f;  // log2(e)
   if (mfma) {
     const bool paged = c.page_size > 0;
-#define MLA_FP8(PG) \
-    hipLaunchKernelGGL((k_decode_fp8<PG>), dim3(G), dim3(256), 0, st, qop, fhv, c, seq_lens, B, G, cu, fmt, \
+#define MLA_FP8(PG, F6) \
+    hipLaunchKernelGGL((k_decode_fp8<PG, F6>), dim3(G), dim3(256), 0, st, qop, fhv, c, seq_lens, B, G, cu, fmt, \
                        lse_part, (float*)(base + L.off_sc), (uint16_t*)o_part)
 #define MLA_V3(PG) \
     hipLaunchKernelGGL((k_decode_v3<PG>), dim3(G), dim3(256), 0, st, qop, c, seq_lens, B, G, cu, fmt, \
@@ -1827,7 +1914,11 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
       if (paged) MLA_V3(true); else MLA_V3(false);
     } else {
       hipLaunchKernelGGL(k_qprep<true>, dim3(B * 16), dim3(256), 0, st, q_lat, q_pe, qscale, qop, fhv);
-      if (paged) MLA_FP8(true); else MLA_FP8(false);
+      if (c.dtype == MLA_FP6_E2M3) {
+        if (paged) MLA_FP8(true, true); else MLA_FP8(false, true);
+      } else {
+        if (paged) MLA_FP8(true, false); else MLA_FP8(false, false);
+      }
     }
 #undef MLA_FP8
 #undef MLA_V3
@@ -1846,6 +1937,7 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
       case MLA_F32: MLA_GEN_DT(MLA_F32); break;
       case MLA_F16: MLA_GEN_DT(MLA_F16); break;
       case MLA_BF16: MLA_GEN_DT(MLA_BF16); break;
+      case MLA_FP6_E2M3: MLA_GEN_DT(MLA_FP6_E2M3); break;
       default: MLA_GEN_DT(MLA_FP8_E4M3); break;
     }
 #undef MLA_GEN_DT

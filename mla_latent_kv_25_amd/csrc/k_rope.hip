@@ -19,12 +19,24 @@ __device__ __forceinline__ int64_t cache_row_index(const CacheArgs& c, int b, in
   return (int64_t)page * c.page_size + (j % c.page_size);
 }
 
+// Four e2m3 codes of consecutive elements -> the 3 bytes of their 24 bits in the row's little-endian
+// 6-bit stream (code j at bits 6j .. 6j + 5; rows hold a multiple of 4 codes).
+__device__ __forceinline__ void store_e2m3x4(uint8_t* row, int g, const float* v, float scale) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bits |= f32_to_e2m3(v[k] / scale) << (6 * k);
+  row[3 * g] = (uint8_t)bits;
+  row[3 * g + 1] = (uint8_t)(bits >> 8);
+  row[3 * g + 2] = (uint8_t)(bits >> 16);
+}
+
 // Store one row held by a 256-thread block in `vals` (LDS, float32, `rw` values).
 // fp8: scale = amax / 448 (1 for an all-zero row), code = e4m3(x / scale).
+// fp6: scale = amax / 7.5 (1 for an all-zero row), code = e2m3(x / scale), packed 6 bits each.
 __device__ void store_row_block(const CacheArgs& c, int64_t ridx, const float* vals, int rw,
                                 float* red) {
   const int tid = threadIdx.x;
-  if (c.dtype == MLA_FP8_E4M3) {
+  if (c.dtype == MLA_FP8_E4M3 || c.dtype == MLA_FP6_E2M3) {
     float a = 0.f;
     for (int e = tid; e < rw; e += blockDim.x) a = fmaxf(a, fabsf(vals[e]));
     a = wave_max(a);
@@ -32,6 +44,13 @@ __device__ void store_row_block(const CacheArgs& c, int64_t ridx, const float* v
     __syncthreads();
     float amax = 0.f;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
+    if (c.dtype == MLA_FP6_E2M3) {
+      const float scale = amax == 0.f ? 1.f : amax / 7.5f;
+      uint8_t* dst = (uint8_t*)c.rows + ridx * (rw / 4 * 3);
+      for (int g = tid; g < rw / 4; g += blockDim.x) store_e2m3x4(dst, g, vals + 4 * g, scale);
+      if (tid == 0) c.scales[ridx] = scale;
+      return;
+    }
     float scale = amax == 0.f ? 1.f : amax / 448.0f;
     uint8_t* dst = (uint8_t*)c.rows + ridx * rw;
     for (int e = tid; e < rw; e += blockDim.x) dst[e] = (uint8_t)f32_to_e4m3(vals[e] / scale);
@@ -126,6 +145,16 @@ __global__ __launch_bounds__(256) void k_cache_store(int rw, CacheArgs cache,
   if (j >= n_rows[b]) return;
   const float* s = src + ((int64_t)b * src_stride + j) * rw;
   const int64_t ridx = cache_row_index(cache, b, j);
+  if (cache.dtype == MLA_FP6_E2M3) {
+    float a = 0.f;
+    for (int e = lane; e < rw; e += 64) a = fmaxf(a, fabsf(s[e]));
+    a = wave_max(a);
+    const float scale = a == 0.f ? 1.f : a / 7.5f;
+    uint8_t* dst = (uint8_t*)cache.rows + ridx * (rw / 4 * 3);
+    for (int g = lane; g < rw / 4; g += 64) store_e2m3x4(dst, g, s + 4 * g, scale);
+    if (lane == 0) cache.scales[ridx] = scale;
+    return;
+  }
   if (cache.dtype == MLA_FP8_E4M3) {
     float a = 0.f;
     for (int e = lane; e < rw; e += 64) a = fmaxf(a, fabsf(s[e]));

@@ -4,7 +4,7 @@ compute unit), on sampled outputs the oracle can compute one by one.
 Every config runs its whole decode step on the GPU through the C ABI. The oracle is then run, with
 explicit K/V reconstruction and every head, on sampled sequences: the first, the last and one in
 between of config 2; the shortest, the longest and ten more seeded picks of the ragged config 3;
-two whole 131,072-token sequences of config 4 (bf16 and fp8 caches). Each sampled sequence is
+two whole 131,072-token sequences of config 4 (bf16, fp8 and fp6 caches). Each sampled sequence is
 compared on u (the step's output) and on o_lat and lse of all its heads.
 """
 import numpy as np
@@ -87,10 +87,10 @@ def test_fullsize_config3():
         _check_heads(step, case, b, ref, list(range(case.dims.n_h)), "cfg3")
 
 
-@pytest.mark.parametrize("key", ["4", "4f8"])
+@pytest.mark.parametrize("key", ["4", "4f8", "4f6"])
 def test_fullsize_config4(key):
-    """B=4, T=131072 (bf16 and fp8 e4m3 caches), split over 64 ranges per sequence: u, o_lat and
-    lse of every head of the first and the last sequence."""
+    """B=4, T=131072 (bf16, fp8 e4m3 and fp6 e2m3 caches), split over 64 ranges per sequence: u,
+    o_lat and lse of every head of the first and the last sequence."""
     case = make_case(get_config(key), device="cuda")
     step, _ = run_gpu(case, 0)
     for b in (0, case.B - 1):

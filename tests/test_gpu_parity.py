@@ -39,6 +39,11 @@ SMALL_CASES = [
     # more ranges than tokens: most ranges are empty, the rest hold one or two tokens
     ("2", 2, [3, 40], None, True, 64),
     ("4f8", 2, [5, 20], "paged", True, 48),
+    # fp6 e2m3 cache (packed rows converted to the fp8 tile layout in LDS)
+    ("4f6", 2, [3000, 129], None, False, 8),
+    ("4f6", 2, [2000, 33], None, True, 3),
+    ("4f6", 3, [900, 64, 2], "paged", True, 5),
+    ("4f6", 2, [5, 20], "paged", True, 48),
 ]
 
 
@@ -67,7 +72,7 @@ def test_small_parity(key, B, T, layout, stress, splits):
     assert o_err <= tol_o and lse_err <= (1e-4 if case.cfg.cdtype == "f32" else 2e-2)
 
 
-@pytest.mark.parametrize("key", ["0", "1", "2", "4f8"])
+@pytest.mark.parametrize("key", ["0", "1", "2", "4f8", "4f6"])
 def test_tiny_contexts(key):
     """Contexts of 1-4 tokens (T = 1 is the closed form: one weight of 1)."""
     case = _case(key, 4, [1, 2, 3, 4], stress=True)
@@ -143,14 +148,14 @@ def test_split_count_invariance():
         assert float((l - outs[0][2]).abs().max()) < 1e-3
 
 
-@pytest.mark.parametrize("key", ["0", "1", "2", "4f8"])
+@pytest.mark.parametrize("key", ["0", "1", "2", "4f8", "4f6"])
 def test_zero_length_sequences(key):
     """decode_attn + combine with some sequences at length 0 (first, middle and last), called on
     the queries and cache of a normal step: those sequences get o_lat = 0 and lse = -inf, and the
     others match the normal step up to the range split (the batch's total changes)."""
     T = [1, 300, 1, 77, 5, 1]
     empty = [0, 2, 5]
-    case = _case(key, len(T), T, layout="paged" if key in ("2", "4f8") else None, stress=True)
+    case = _case(key, len(T), T, layout="paged" if key in ("2", "4f8", "4f6") else None, stress=True)
     print(f"case cfg={key} T={T} zeroed={empty}", flush=True)
     step, cache = run_gpu(case, 7)
     lens = case.seq_lens.clone()
@@ -170,7 +175,8 @@ def test_zero_length_sequences(key):
             assert e < (1e-5 if key == "0" else 2e-3) and le < (1e-5 if key == "0" else 1e-3)
 
 
-@pytest.mark.parametrize("key,layout", [("2", "contiguous"), ("2", "paged"), ("4f8", "contiguous"), ("0", "contiguous")])
+@pytest.mark.parametrize("key,layout", [("2", "contiguous"), ("2", "paged"), ("4f8", "contiguous"), ("4f6", "paged"),
+                                        ("0", "contiguous")])
 def test_rope_zero_length_writes_nothing(key, layout):
     """mla_rope with sequences of length 0 (outside the contract; the first and the last of the
     batch): their q_pe and kv_new rows stay as they were and nothing is stored for them. In a
@@ -194,8 +200,7 @@ def test_rope_zero_length_writes_nothing(key, layout):
     for b in empty:
         assert torch.equal(step.q_pe[b], qpe0[b]) and torch.equal(step.kv_new[b], kv0[b]), b
     assert not torch.equal(step.q_pe[1], qpe0[1])  # the non-empty sequence was rotated
-    row = case.dims.row
-    changed = (cache.rows != rows0).reshape(-1, row).any(dim=1)
+    changed = (cache.rows != rows0).reshape(-1, cache.rows.shape[-1]).any(dim=1)
     if sc0 is not None:
         changed |= (cache.scales != sc0).reshape(-1)
     pos = T[1] - 1
@@ -209,7 +214,7 @@ def test_rope_zero_length_writes_nothing(key, layout):
 
 
 def test_paged_equals_contiguous():
-    for key in ("2", "4f8"):
+    for key in ("2", "4f8", "4f6"):
         pc = _case(key, 3, [300, 64, 129], layout="paged", stress=True)
         cc = _case(key, 3, [300, 64, 129], layout="contiguous", stress=True)
         for b in range(3):
@@ -246,6 +251,43 @@ def test_batch_independence_and_determinism():
     assert rel_l2(s3.u[0].double().cpu().numpy(), s1.u[1].double().cpu().numpy()) < 2e-3
 
 
+def test_fp6_cache_store_bit_exact():
+    """The library's fp6 encoder (mla_cache_store) writes the oracle's packed bytes and scales."""
+    from oracle import pack_e2m3, quantize_rows_e2m3
+    for layout in ("contiguous", "paged"):
+        case = _case("4f6", 3, [200, 1, 70], layout=layout)
+        cache = build_cache(case)
+        torch.cuda.synchronize()
+        for b in range(3):
+            n = int(case.seq_lens[b]) - 1
+            src = case.prefix_rows(b).float().cpu().numpy()
+            codes, scales = quantize_rows_e2m3(src)
+            packed = pack_e2m3(codes)
+            if layout == "contiguous":
+                g_rows = cache.rows[b, :n].cpu().numpy()
+                g_sc = cache.scales[b, :n].cpu().numpy()
+            else:
+                ps = case.cfg.page_size
+                pages = case.block_table[b, : (n + ps) // ps].long()
+                g_rows = cache.rows[pages].reshape(-1, cache.rows.shape[-1])[:n].cpu().numpy()
+                g_sc = cache.scales[pages].reshape(-1)[:n].cpu().numpy()
+            assert np.array_equal(g_rows, packed), (layout, b)
+            assert np.array_equal(g_sc.view(np.uint32), scales.view(np.uint32)), (layout, b)
+
+
+@pytest.mark.parametrize("key,B,T,splits", [("1", 4, [500, 1, 100, 2049], 16), ("0", 3, [64, 1, 33], 4)])
+def test_fp6_generic_kernel(key, B, T, splits):
+    """An fp6 cache at the running model's dims (float32 generic kernel, 6-bit codes read in place)."""
+    cfg = get_config(key, stress=True)
+    for layout in ("contiguous", "paged"):
+        case = make_case(cfg, device="cuda", B=B, T=T, layout=layout, cdtype="fp6_e2m3")
+        print(f"case cfg={key} fp6 layout={layout} T={T} splits={splits}", flush=True)
+        step, _ = run_gpu(case, splits)
+        ref = run_oracle(case)
+        u_ref = np.stack([ref[b]["u"] for b in range(B)])
+        check_u(step.u.double().cpu().numpy(), u_ref, "fp6_e2m3", f"cfg{key} fp6 {layout}")
+
+
 def test_fp8_cache_store_bit_exact():
     for layout in ("contiguous", "paged"):
         case = _case("4f8", 3, [200, 1, 70], layout=layout)
@@ -271,7 +313,7 @@ def test_appended_row_storage():
     """The row mla_rope appends is the oracle's row rounded to the storage type: float32 to
     rounding, bf16 within one code step for elements whose float32 value sits on a rounding
     boundary, fp8 codes within one step and the scale within float32 rounding."""
-    for key in ("0", "2", "4f8"):
+    for key in ("0", "2", "4f8", "4f6"):
         case = _case(key, 3, [40, 1, 7], stress=True)
         step, cache = run_gpu(case, 2)
         ref = run_oracle(case, want_u=False, heads=[0])
@@ -285,6 +327,14 @@ def test_appended_row_storage():
                 g = cache.rows[b, pos].view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int64)
                 r = bf16_encode(row_ref).astype(np.int64)
                 assert np.max(np.abs(g - r)) <= 1 and np.mean(g != r) < 0.02
+            elif case.cfg.cdtype == "fp6_e2m3":
+                from oracle import e2m3_decode, quantize_rows_e2m3, unpack_e2m3
+                g = unpack_e2m3(cache.rows[b, pos].cpu().numpy(), case.dims.row)
+                codes, scale = quantize_rows_e2m3(row_ref.astype(np.float32)[None, :])
+                assert abs(float(cache.scales[b, pos]) - float(scale[0])) <= 1e-6 * float(scale[0])
+                dv = np.abs(e2m3_decode(g) - e2m3_decode(codes[0]))
+                assert np.mean(g != codes[0]) < 0.02
+                assert np.all(dv <= np.abs(e2m3_decode(codes[0])) * 2.0 ** -3 + 2.0 ** -3)
             else:
                 g = cache.rows[b, pos].cpu().numpy()
                 codes, scale = quantize_rows_e4m3(row_ref.astype(np.float32)[None, :])
@@ -321,7 +371,8 @@ def spike_budget(case, ref, mult):
     return np.stack(lse_bar), np.array(u_bar)
 
 
-@pytest.mark.parametrize("key,mult", [("0", 64), ("1", 64), ("2", 8), ("2", 64), ("4f8", 8), ("4f8", 64)])
+@pytest.mark.parametrize("key,mult", [("0", 64), ("1", 64), ("2", 8), ("2", 64), ("4f8", 8), ("4f8", 64),
+                                      ("4f6", 64)])
 def test_late_score_spike(key, mult):
     """A cached row far along a range with a score far above everything before it: the attention
     kernels take the first tile's maximum as their softmax reference, and a score more than 2^64
@@ -366,7 +417,8 @@ def test_late_score_spike(key, mult):
     assert np.all(lse_err <= lse_bar), float(np.max(lse_err - lse_bar))
 
 
-@pytest.mark.parametrize("key,ps", [("2", 32), ("2", 256), ("4f8", 32), ("4f8", 128), ("1", 16), ("0", 8)])
+@pytest.mark.parametrize("key,ps", [("2", 32), ("2", 256), ("4f8", 32), ("4f8", 128), ("4f6", 32), ("4f6", 256),
+                                    ("1", 16), ("0", 8)])
 def test_page_sizes(key, ps):
     """Paged caches with other page sizes than the configs' 64: the MFMA kernels take any power of
     two >= 32 (a 32-token tile spans at most two pages), the generic kernel any size. Ragged

@@ -26,6 +26,7 @@ CASES = [
     ("2", [40, 1, 300], 33, True, 5),
     ("3", [70, 129], 1, True, 3),
     ("4f8", [50, 3], 9, True, 0),
+    ("4f6", [50, 3], 9, True, 0),
     ("0", [20, 0, 63], 5, True, 4),
     ("1", [10, 200], 12, False, 0),
 ]
