@@ -11,6 +11,8 @@
 // range p is one workgroup. A range may cover the end of one sequence and the start of the next;
 // each (range, sequence) piece writes a normalised partial o and its log-sum-exp into slot p + b
 // of the workspace (slots are unique: ranges and sequences both advance with the token order).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1645,6 +1647,265 @@ __global__ __launch_bounds__(256) void k_decode_generic(int n_h, int d_c, int d_
 }
 
 // ================================================================================================
+// MFMA kernel for a few heads (n_h <= 16; the running model has 8) over 16-bit caches (fp16 or
+// bf16 rows of 32*KS elements, d_c = 16*CB). Same equations as above ("DeepSeek-V2 from Scratch"
+// section 5.3: scores of the absorbed query against the cached latent rows, softmax, latent-weighted
+// sum); with so few heads a tile is little math, so the kernel is organised around the stream of
+// rows instead of around the accumulators:
+//   - a workgroup of two waves owns a range of tokens; each wave takes every other 32-token tile of
+//     the range's segments and keeps its own online softmax, so waves never wait for each other
+//     inside the loop (one merge per segment at the end);
+//   - each wave copies its tiles straight into its own ring of LDS slots (global->LDS copies, rows
+//     padded to an odd number of 16-byte chunks), three tiles in flight;
+//   - scores: S^T[16 tok x 16 heads] blocks with MFMA 16x16x32 (rows of the tile as A, the query
+//     of the lane's head as B, heads past n_h zero); the accumulator layout gives lane (g, n) the
+//     scores of head n for tokens 4g..4g+3 and 16+4g..16+4g+3, which are exactly the eight values
+//     the PV product needs from that lane as its B operand (the reduction runs over the tile's
+//     tokens in that order), so P never leaves the registers;
+//   - PV: O^T[16 columns x 16 heads] += V^T P^T per 16 latent columns, V^T gathered with the
+//     transposing 16-bit LDS read (rows 4g.. and 16+4g.. of the lane's column).
+// The query is scaled by a power of two per head (its largest element just below 2^14) before it is
+// rounded to the 16-bit type, so fp16 neither overflows nor loses precision to small magnitudes;
+// the scores are scaled back exactly. Partial outputs are float32 (format 0).
+namespace smh {
+constexpr int NW = 2;       // waves per workgroup
+constexpr int TT = 32;      // tokens per tile
+constexpr int NSLOT = 3;    // tile slots per wave
+}
+template <int KS>
+struct SmCfg {
+  static constexpr int CH = 4 * KS;                          // 16-byte chunks per cached row
+  static constexpr int CHP = CH + 1;                         // padded LDS row stride in chunks (odd)
+  static constexpr int NCP = (smh::TT * CHP + 63) / 64;      // copy instructions per tile (1 KB each)
+  static constexpr int SLOTB = NCP * 1024;                   // bytes of one tile slot
+  static constexpr int RB = CH * 16;                         // bytes of one cached row
+};
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int CDT, int KS, int CB, bool PAGED>
+__global__ __launch_bounds__(128) void k_decode_small(int n_h, const float* __restrict__ q_lat,
+                                                      const float* __restrict__ q_pe, CacheArgs cache,
+                                                      const int32_t* __restrict__ seq_lens, int B, int G,
+                                                      int64_t* __restrict__ cu_out, int32_t* __restrict__ fmt_out,
+                                                      float qscale, float* __restrict__ lse_part,
+                                                      float* __restrict__ o_part) {
+  using Cfg = SmCfg<KS>;
+  using namespace smh;
+  constexpr int DC = 16 * CB, DR = 32 * KS - DC, CHP = Cfg::CHP, NCP = Cfg::NCP, SLOTB = Cfg::SLOTB, RB = Cfg::RB;
+  static_assert(DR > 0 && DC % 8 == 0, "row split");
+  static_assert(NCP - 1 + (NSLOT - 1) * NCP <= 63, "vmcnt range");
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef typename std::conditional<CDT == MLA_F16, h8, bf16x8>::type op8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NW * NSLOT * SLOTB];
+  __shared__ float mw[NW][16], lw[NW][16];
+  // the wave index is uniform: kept in a scalar register, so the tile addresses are too
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int p = range_for_block(blockIdx.x, G);
+  if (blockIdx.x == 0 && w == 1) write_prefix(seq_lens, B, 0, cu_out, fmt_out, lane);
+  const RangeStart rp = locate_range(seq_lens, B, G, p, lane);
+  int64_t start = rp.start;
+  const int64_t end = rp.end;
+  if (start >= end) return;
+  int b = rp.b;
+  int64_t s0 = rp.s0, s1 = rp.s1;
+  uint8_t* const slots = lds + w * NSLOT * SLOTB;
+  const uint32_t slots_lds = (uint32_t)(uintptr_t)(MLA_LDS void*)slots;
+  const uint8_t* rows_b = (const uint8_t*)cache.rows;
+
+  // copy plan: LDS chunk q = 64 i + lane of a slot holds chunk q % CHP of tile row q / CHP (the pad
+  // chunk and the rows past the tile take a harmless duplicate)
+  uint32_t plan[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int q = 64 * i + lane, r = q / CHP, c = q % CHP;
+    plan[i] = (uint32_t)((r < TT ? r : TT - 1) << 8) | (uint32_t)(c < Cfg::CH ? c : 0);
+  }
+
+  while (start < end) {
+    if (s1 <= start) {
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+      continue;
+    }
+    const int64_t seg_end = end < s1 ? end : s1;
+    const int64_t t0 = start - s0, t1 = seg_end - s0;
+    const int64_t slot = (int64_t)p + b;
+    const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+    const int nk = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // this wave's tiles: w, w + NW, ...
+    Rows<PAGED> rows;
+    rows.init(cache, b);
+
+    // the copies of this wave's k-th tile into slot k % NSLOT (rows past the segment repeat its last row)
+    auto issue = [&](int k) __attribute__((always_inline)) {
+      const int64_t tt0 = t0 + (int64_t)(w + NW * k) * TT;
+      const int last = (int)((t1 - 1 - tt0) < (TT - 1) ? (t1 - 1 - tt0) : (TT - 1));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(slots_lds + (uint32_t)((k % NSLOT) * SLOTB));
+      if constexpr (PAGED) rows.tile(tt0, tt0 + last);
+      // every earlier LDS read of the slot has completed before it is overwritten
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        int r = (int)(plan[i] >> 8);
+        r = r < last ? r : last;
+        const uint32_t cb16 = (plan[i] & 0xffu) << 4;
+        if constexpr (PAGED) {
+          dma16(rows_b + rows.row(tt0 + r) * RB + cb16, dst + i * 1024);
+        } else {
+          dma16_s(rows_b + (rows.base_row + tt0) * RB, (uint32_t)(r * RB) + cb16, dst + i * 1024);
+        }
+      }
+    };
+
+    if (nk > 0) issue(0);
+    // query of head n (zero past n_h), dims 32 ks + 8 g .. + 7, times qscale, as 16-bit B fragments
+    // scaled by 2^(14 - e_h) (e_h: exponent of the head's largest element)
+    f32x4 qv[KS][2];
+    float qmax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      if (n < n_h) {
+        const float* src = d0 < DC ? q_lat + ((int64_t)b * n_h + n) * DC + d0 : q_pe + ((int64_t)b * n_h + n) * DR + (d0 - DC);
+        qv[ks][0] = *(const f32x4*)src * qscale;
+        qv[ks][1] = *(const f32x4*)(src + 4) * qscale;
+      } else {
+        qv[ks][0] = qv[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qmax = fmaxf(qmax, fmaxf(fabsf(qv[ks][0][j]), fabsf(qv[ks][1][j])));
+    }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+    int qe = 0;
+    if (qmax > 0.f) (void)frexpf(qmax, &qe);
+    const float up = ldexpf(1.f, 14 - qe), down = ldexpf(1.f, qe - 14);
+    op8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (j < 4 ? qv[ks][0][j] : qv[ks][1][j - 4]) * up;
+        if constexpr (CDT == MLA_F16) qf[ks][j] = (_Float16)x;
+        else qf[ks][j] = (__bf16)x;
+      }
+#pragma unroll
+    for (int k = 1; k < NSLOT; ++k)
+      if (k < nk) issue(k);
+
+    float m_run = -__builtin_inff(), l_run = 0.f;
+    f32x4 O[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) O[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k = 0; k < nk; ++k) {
+      // tile k landed (the copies of at most NSLOT - 1 later tiles still in flight)
+      const int later = (nk - 1 - k) < (NSLOT - 1) ? (nk - 1 - k) : (NSLOT - 1);
+      if (later >= 2) vm_wait<2 * NCP>();
+      else if (later == 1) vm_wait<NCP>();
+      else vm_wait<0>();
+      const uint8_t* tile = slots + (k % NSLOT) * SLOTB;
+      const int64_t tt0 = t0 + (int64_t)(w + NW * k) * TT;
+      const int valid = (int)((t1 - tt0) < TT ? (t1 - tt0) : TT);
+      // scores of tokens 0..15 (S0) and 16..31 (S1): lane (g, n) gets head n, tokens 4g + r
+      f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const op8 a0 = *(const op8*)(tile + (n * CHP + 4 * ks + g) * 16);
+        const op8 a1 = *(const op8*)(tile + ((16 + n) * CHP + 4 * ks + g) * 16);
+        if constexpr (CDT == MLA_F16) {
+          S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[ks], S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[ks], S1, 0, 0, 0);
+        } else {
+          S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], S1, 0, 0, 0);
+        }
+      }
+      float tm = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        S0[r] = 4 * g + r < valid ? S0[r] * down : -__builtin_inff();
+        S1[r] = 16 + 4 * g + r < valid ? S1[r] * down : -__builtin_inff();
+        tm = fmaxf(tm, fmaxf(S0[r], S1[r]));
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+      const float m_new = fmaxf(m_run, tm);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float rs = 0.f;
+      op8 pf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e0 = __builtin_amdgcn_exp2f(S0[r] - m_new), e1 = __builtin_amdgcn_exp2f(S1[r] - m_new);
+        rs += e0 + e1;
+        if constexpr (CDT == MLA_F16) { pf[r] = (_Float16)e0; pf[4 + r] = (_Float16)e1; }
+        else { pf[r] = (__bf16)e0; pf[4 + r] = (__bf16)e1; }
+      }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      // V^T of the lane's column 16 cb + n: rows 4g + 0..3 and 16 + 4g + 0..3 (transposing reads:
+      // lane j of each 16-lane group supplies row j / 4, columns 4 (j % 4) .. + 3 of the block)
+      const uint8_t* va = tile + (4 * g + (n >> 2)) * CHP * 16 + (n & 3) * 8;
+      const uint8_t* vb = va + 16 * CHP * 16;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(va + 32 * cb));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(vb + 32 * cb));
+        const op8 av = __builtin_bit_cast(op8, u32x4{__builtin_bit_cast(u32x2, x0).x, __builtin_bit_cast(u32x2, x0).y,
+                                                     __builtin_bit_cast(u32x2, x1).x, __builtin_bit_cast(u32x2, x1).y});
+        const f32x4 o = O[cb] * alpha;
+        if constexpr (CDT == MLA_F16) O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf, o, 0, 0, 0);
+        else O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf, o, 0, 0, 0);
+      }
+      if (k + NSLOT < nk) issue(k + NSLOT);
+    }
+
+    // merge the waves: O of wave w (head n, columns 16 cb + 4 g + r) to its own slots, then every
+    // thread combines four consecutive columns of one head
+    __syncthreads();  // both waves are past their last tile reads
+    float* ow = (float*)slots;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) *(f32x4*)(ow + n * DC + 16 * cb + 4 * g) = O[cb];
+    if (g == 0) {
+      mw[w][n] = m_run;
+      lw[w][n] = l_run;
+    }
+    __syncthreads();
+    for (int i4 = tid; i4 < n_h * DC / 4; i4 += 64 * NW) {
+      const int h = (4 * i4) / DC, c = 4 * i4 - h * DC;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, mw[v][h]);
+      float L = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float wt = __builtin_amdgcn_exp2f(mw[v][h] - M);
+        L += wt * lw[v][h];
+        acc += *(const f32x4*)((const float*)(lds + v * NSLOT * SLOTB) + h * DC + c) * wt;
+      }
+      *(f32x4*)(o_part + (slot * n_h + h) * DC + c) = acc * (1.f / L);
+      if (c == 0) lse_part[slot * n_h + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+    }
+    __syncthreads();  // the slots are reused by the next segment
+
+    start = seg_end;
+    if (start < end) {
+      ++b;
+      s0 = s1;
+      s1 = s0 + seq_lens[b];
+    }
+  }
+}
+
+// ================================================================================================
 // Combine: per sequence, merge the pieces of the ranges that cover it. One block = one sequence
 // and CH heads; the piece list and the per-(piece, head) weights exp(lse_s - M) / sum are built
 // once in LDS, then every output element is a weighted sum over the pieces (fixed order).
@@ -1881,8 +2142,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 static bool is_v2(const mla_dims& d) { return d.n_h == v2::NH && d.d_c == v2::DC && d.d_r == v2::DR; }
 static bool v2_page_ok(int ps) { return ps == 0 || (ps >= 32 && (ps & (ps - 1)) == 0); }
 
+// the few-head MFMA kernel: the running model's row split (d_c = 128, d_r = 32) over 16-bit caches
+static bool small_shape(const mla_dims& d, int cdt, int page_size) {
+  return d.n_h <= 16 && d.d_c == 128 && d.d_r == 32 && (cdt == MLA_F16 || cdt == MLA_BF16) && v2_page_ok(page_size);
+}
+
 bool decode_supported(const mla_dims& d, int cdt, int page_size) {
   if (is_v2(d) && (cdt == MLA_BF16 || cdt == MLA_FP8_E4M3 || cdt == MLA_FP6_E2M3)) return v2_page_ok(page_size);
+  if (small_shape(d, cdt, page_size)) return true;
   const int rw = d.d_c + d.d_r;
   return d.n_h * rw <= 16384 && rw <= 512 && d.n_h <= 64 && d.n_h * d.d_c <= 256 * gen::OPT;
 }
@@ -1922,6 +2189,14 @@ hipError_t launch_decode(const mla_dims& d, int B, const float* q_lat, const flo
     }
 #undef MLA_FP8
 #undef MLA_V3
+  } else if (small_shape(d, c.dtype, c.page_size)) {
+    const bool paged = c.page_size > 0;
+#define MLA_SMALL(CDT, PG)                                                                                    \
+    hipLaunchKernelGGL((k_decode_small<CDT, 5, 8, PG>), dim3(G), dim3(64 * smh::NW), 0, st, d.n_h, q_lat, q_pe, c, \
+                       seq_lens, B, G, cu, fmt, qscale, lse_part, o_part)
+    if (c.dtype == MLA_F16) { if (paged) MLA_SMALL(MLA_F16, true); else MLA_SMALL(MLA_F16, false); }
+    else { if (paged) MLA_SMALL(MLA_BF16, true); else MLA_SMALL(MLA_BF16, false); }
+#undef MLA_SMALL
   } else {
     const int rw = d.d_c + d.d_r;
     size_t smem = (size_t)(d.n_h * rw + gen::TT * (rw + 4) + d.n_h * gen::TT + 3 * d.n_h) * 4;

@@ -27,6 +27,10 @@ SMALL_CASES = [
     ("0", 2, [64, 17], None, False, 256),
     ("1", 4, [4096, 1, 100, 2049], None, False, 0),
     ("1", 3, [500, 1000, 3], None, True, 16),
+    # few-head MFMA kernel: paged rows, and more ranges than tokens
+    ("1", 3, [500, 1000, 3], "paged", True, 16),
+    ("1", 2, [3, 40], None, True, 64),
+    ("1", 3, [70, 33, 1], "paged", False, 37),
     ("2", 3, [300, 1, 77], None, False, 4),
     ("2", 3, [300, 1, 77], None, True, 4),
     ("2", 2, [1000, 65], "paged", True, 5),
@@ -288,6 +292,23 @@ def test_fp6_generic_kernel(key, B, T, splits):
         check_u(step.u.double().cpu().numpy(), u_ref, "fp6_e2m3", f"cfg{key} fp6 {layout}")
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_small_heads_bf16(layout):
+    """A bf16 cache at the running model's dims (the few-head MFMA kernel in its bf16 form)."""
+    cfg = get_config("1", stress=True)
+    B, T = 3, [1200, 65, 2]
+    case = make_case(cfg, device="cuda", B=B, T=T, layout=layout, cdtype="bf16")
+    print(f"case cfg=1 bf16 layout={layout} T={T} splits=0", flush=True)
+    step, _ = run_gpu(case, 0)
+    ref = run_oracle(case)
+    u_ref = np.stack([ref[b]["u"] for b in range(B)])
+    check_u(step.u.double().cpu().numpy(), u_ref, "bf16", f"cfg1 bf16 {layout}")
+    o_ref = np.stack([ref[b]["o_lat"] for b in range(B)])
+    o_err = rel_l2(step.o_lat.double().cpu().numpy(), o_ref)
+    print(f"  o_lat rel-L2 {o_err:.3e}", flush=True)
+    assert o_err <= 5e-3
+
+
 def test_fp8_cache_store_bit_exact():
     for layout in ("contiguous", "paged"):
         case = _case("4f8", 3, [200, 1, 70], layout=layout)
@@ -418,7 +439,7 @@ def test_late_score_spike(key, mult):
 
 
 @pytest.mark.parametrize("key,ps", [("2", 32), ("2", 256), ("4f8", 32), ("4f8", 128), ("4f6", 32), ("4f6", 256),
-                                    ("1", 16), ("0", 8)])
+                                    ("1", 16), ("1", 32), ("1", 128), ("0", 8)])
 def test_page_sizes(key, ps):
     """Paged caches with other page sizes than the configs' 64: the MFMA kernels take any power of
     two >= 32 (a 32-token tile spans at most two pages), the generic kernel any size. Ragged
