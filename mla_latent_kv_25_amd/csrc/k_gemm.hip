@@ -600,6 +600,84 @@ __global__ __launch_bounds__(256) void k_gemm_valu(VSeg sg, int N, int K, int64_
   }
 }
 
+// ================================================================================================
+// Small products at decode batch sizes (N <= 64), any weight type, on float32 MFMA:
+//   Y[n][m] = sum_k A(m, k) X[n][k],  A(m, k) = TRANS ? W[k*lda + m] : W[m*lda + k].
+// The running model's projections are a few hundred rows by a few hundred k: too little work to
+// fill the chip, so their time is latency. A workgroup owns a 16 (m) x 16 (n) output tile and its
+// four waves split K in 32-k chunks (wave w: chunks w, w + 4, ...); one LDS reduction at the end.
+// v_mfma_f32_16x16x4_f32 multiplies the widened weights and float32 activations exactly, as the
+// VALU kernel does. Lane (g, r) supplies row m0 + r of A and row n0 + r of X for k = 32c + 8g + e
+// in the e-th MFMA of chunk c (the same k on both sides), so each lane reads 8 consecutive k
+// (one vector load when aligned; TRANS weights: the 16 lanes of a group read 16 consecutive m).
+// Stacked segments as in VSeg, with tile starts in units of 16 rows.
+template <int DT>
+__device__ __forceinline__ void load8(const typename Elem<DT>::T* p, bool vec, int valid, float (&v)[8]) {
+  if (vec && valid >= 8) {
+    if constexpr (DT == MLA_F32) {
+      const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    } else {
+      const u32x4 a = *(const u32x4*)p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = Elem<DT>::cvt((uint16_t)(a[e] & 0xffffu));
+        v[2 * e + 1] = Elem<DT>::cvt((uint16_t)(a[e] >> 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < valid ? Elem<DT>::ld(p, e) : 0.f;
+  }
+}
+
+template <int ADT, int XDT, bool TRANS>
+__global__ __launch_bounds__(256) void k_gemm_tiny(VSeg sg, int N, int K, int64_t lda, int64_t zW,
+                                                  const void* __restrict__ Xv, int64_t ldx, int64_t zX, int64_t zY,
+                                                  int wvec, int xvec) {
+  __shared__ f32x4 red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int mt = blockIdx.x;
+  const int s = sg.n > 2 && mt >= sg.t0[2] ? 2 : (sg.n > 1 && mt >= sg.t0[1] ? 1 : 0);
+  const int M = sg.M[s];
+  const int m0 = (mt - sg.t0[s]) * 16, n0 = blockIdx.y * 16, z = blockIdx.z;
+  const typename Elem<ADT>::T* W = (const typename Elem<ADT>::T*)sg.W[s] + (int64_t)z * zW;
+  const typename Elem<XDT>::T* X = (const typename Elem<XDT>::T*)Xv + (int64_t)z * zX;
+  const int m = min(m0 + r, M - 1), n = min(n0 + r, N - 1);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (K + 31) / 32;
+  for (int c = w; c < nchunk; c += 4) {
+    const int kb = 32 * c + 8 * g;
+    const int valid = K - kb < 8 ? (K - kb > 0 ? K - kb : 0) : 8;
+    float a[8], x[8];
+    if constexpr (TRANS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = e < valid ? Elem<ADT>::ld(W, (int64_t)(kb + e) * lda + m) : 0.f;
+    } else {
+      load8<ADT>(W + (int64_t)m * lda + kb, wvec != 0, valid, a);
+    }
+    load8<XDT>(X + (int64_t)n * ldx + kb, xvec != 0, valid, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], x[e], acc, 0, 0, 0);
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 v = red[0][lane];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) v += red[ww][lane];
+    // lane (g, r): column n0 + r, rows m0 + 4g .. + 3
+    if (n0 + r < N) {
+      float* Y = sg.Y[s] + (int64_t)z * zY + (int64_t)(n0 + r) * sg.ldy[s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (m0 + 4 * g + i < M) Y[m0 + 4 * g + i] = v[i];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch helpers
 static VSeg vseg1(int M, const void* W, float* Y, int64_t ldy) {
   VSeg sg{};
@@ -613,9 +691,28 @@ static VSeg vseg1(int M, const void* W, float* Y, int64_t ldy) {
   return sg;
 }
 
+// decode batch sizes take the small-product MFMA kernel (16-row tiles), wider N the VALU tiles
+constexpr int TINY_N = 64;
 template <int ADT, int XDT, bool TRANS>
 static void valu_seg(hipStream_t st, const VSeg& sg, int N, int K, int64_t lda, int64_t zW, const void* X,
                      int64_t ldx, int64_t zX, int64_t zY, int Z) {
+  if (N <= TINY_N) {
+    VSeg t = sg;
+    t.t0[0] = 0;
+    for (int i = 0; i < sg.n; ++i) t.t0[i + 1] = t.t0[i] + (sg.M[i] + 15) / 16;
+    // 16-byte vector loads of 8 consecutive k: row strides and bases must keep them aligned
+    auto al = [](const void* ptr, int64_t ld, int64_t zs, int es) {
+      return (int)(((uintptr_t)ptr % 16) == 0 && (ld * es) % 16 == 0 && (zs * es) % 16 == 0);
+    };
+    constexpr int EA = ADT == MLA_F32 ? 4 : 2, EX = XDT == MLA_F32 ? 4 : 2;
+    int wv = !TRANS;
+    for (int i = 0; i < sg.n; ++i) wv &= al(sg.W[i], lda, zW, EA);
+    const int xv = al(X, ldx, zX, EX);
+    dim3 grid(t.t0[t.n], (N + 15) / 16, Z);
+    hipLaunchKernelGGL((k_gemm_tiny<ADT, XDT, TRANS>), grid, dim3(256), 0, st, t, N, K, lda, zW, X, ldx, zX, zY,
+                       wv, xv);
+    return;
+  }
   dim3 grid(sg.t0[sg.n], (N + 15) / 16, Z);
   hipLaunchKernelGGL((k_gemm_valu<ADT, XDT, TRANS>), grid, dim3(256), 0, st, sg, N, K, lda, zW, X, ldx, zX, zY);
 }
@@ -642,6 +739,24 @@ static void valu_stacked(int wdt, hipStream_t st, int N, int K, const void* X, i
   if (wdt == MLA_F32) valu_seg<MLA_F32, MLA_F32, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
   else if (wdt == MLA_F16) valu_seg<MLA_F16, MLA_F16, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
   else valu_seg<MLA_BF16, MLA_BF16, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
+}
+
+// Two products Y_s[n][m] = sum_k W_s[m][k] X[n][k] sharing a float32 X (W_s row-major, lda = K) in
+// one launch.
+static void valu_pair_f32x(int wdt, hipStream_t st, int N, int K, const float* X, int64_t ldx, const void* W0,
+                           int M0, float* Y0, int64_t ldy0, const void* W1, int M1, float* Y1, int64_t ldy1) {
+  VSeg sg{};
+  sg.n = 2;
+  sg.t0[0] = 0;
+  sg.t0[1] = (M0 + 63) / 64;
+  sg.t0[2] = sg.t0[1] + (M1 + 63) / 64;
+  sg.W[0] = W0; sg.W[1] = W1;
+  sg.Y[0] = Y0; sg.Y[1] = Y1;
+  sg.ldy[0] = ldy0; sg.ldy[1] = ldy1;
+  sg.M[0] = M0; sg.M[1] = M1;
+  if (wdt == MLA_F32) valu_seg<MLA_F32, MLA_F32, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
+  else if (wdt == MLA_F16) valu_seg<MLA_F16, MLA_F32, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
+  else valu_seg<MLA_BF16, MLA_F32, false>(st, sg, N, K, K, 0, X, ldx, 0, 0, 1);
 }
 
 // Y[n][m] = sum_k A(m,k) X[n][k] with runtime weight dtype; X is float32 or the weight dtype.
@@ -672,7 +787,7 @@ static void valu_any(int wdt, bool x_is_w, bool trans, hipStream_t st, int M, in
 // not split into slices of at least 32.
 static void valu_splitk(int wdt, hipStream_t st, int M, int N, int K, const void* W, const float* X, float* Y,
                         int64_t ldy, int S, float* part) {
-  if (S < 2 || K % S != 0 || K / S < 32 || M % 4 != 0 || part == nullptr) {
+  if (N <= TINY_N || S < 2 || K % S != 0 || K / S < 32 || M % 4 != 0 || part == nullptr) {
     valu_any(wdt, false, false, st, M, N, K, W, K, 0, X, K, 0, Y, ldy, 0, 1);
     return;
   }
@@ -768,9 +883,8 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
   // VALU path (any dims, float32/float16/bf16 weights); W^DQ, W^DKV and W^KR share h: one launch
   valu_stacked(wdt, st, B, d.d, h, d.d, W_dq, d.d_cq, cq, d.d_cq, W_dkv, d.d_c, kv_new, rw, W_kr, d.d_r,
                kv_new + d.d_c, rw);
-  valu_any(wdt, false, false, st, nhdh, B, d.d_cq, W_uq, d.d_cq, 0, cq, d.d_cq, 0, qc, nhdh, 0, 1);
-  valu_any(wdt, false, false, st, d.n_h * d.d_r, B, d.d_cq, W_qr, d.d_cq, 0, cq, d.d_cq, 0, q_pe,
-           (int64_t)d.n_h * d.d_r, 0, 1);
+  valu_pair_f32x(wdt, st, B, d.d_cq, cq, d.d_cq, W_uq, nhdh, qc, nhdh, W_qr, d.n_h * d.d_r, q_pe,
+                 (int64_t)d.n_h * d.d_r);
   // per head: q_lat[n][i][c] = sum_e W_uk[i*d_h + e][c] qC[n][i*d_h + e]  (transposed access)
   valu_any(wdt, false, true, st, d.d_c, B, d.d_h, W_uk, d.d_c, (int64_t)d.d_h * d.d_c, qc, nhdh, d.d_h, q_lat,
            (int64_t)d.n_h * d.d_c, d.d_c, d.n_h);
@@ -924,9 +1038,8 @@ hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h,
   }
   valu_stacked(wdt, st, B, d.d, h, d.d, W_dq, d.d_cq, cq, d.d_cq, W_dkv, d.d_c, kv_new, rw, W_kr, d.d_r,
                kv_new + d.d_c, rw);
-  valu_any(wdt, false, false, st, nhdc, B, d.d_cq, Wq_pre, d.d_cq, 0, cq, d.d_cq, 0, q_lat, nhdc, 0, 1);
-  valu_any(wdt, false, false, st, d.n_h * d.d_r, B, d.d_cq, W_qr, d.d_cq, 0, cq, d.d_cq, 0, q_pe,
-           (int64_t)d.n_h * d.d_r, 0, 1);
+  valu_pair_f32x(wdt, st, B, d.d_cq, cq, d.d_cq, Wq_pre, nhdc, q_lat, nhdc, W_qr, d.n_h * d.d_r, q_pe,
+                 (int64_t)d.n_h * d.d_r);
   return hipGetLastError();
 }
 

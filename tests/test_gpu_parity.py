@@ -365,16 +365,17 @@ def test_appended_row_storage():
                 assert np.all(dv <= np.abs(e4m3_decode(codes[0])) * 2.0 ** -3 + 2.0 ** -9)
 
 
-def spike_budget(case, ref, mult):
+def spike_budget(case, ref, mult, rel=2.0 ** -7):
     """Error budget of the late-spike case (reading R10 of the design notes), from the oracle's own
-    query and stored rows. The MFMA kernels hold the query as bf16 (or as two e4m3 parts with the
-    same 8 significant bits) and the probabilities as bf16: each is rounded with a relative error of
-    at most 2^-8, so
+    query and stored rows. The V2-shape MFMA kernels hold the query as bf16 (or as two e4m3 parts
+    with the same 8 significant bits) and the probabilities as bf16: each is rounded with a relative
+    error of at most 2^-8, so
       score s_ij:  |ds_ij| <= 2^-8 * scale * sum_k |q_ik c_jk|, and lse_i moves by at most max_j |ds_ij|;
       u:           one dominating row carries its rounded weight into every output, |du| <= 2^-8 |u|,
                    plus 2^-11 for the float16 partial rows.
-    The bars are the benchmark spec's absolute ones plus twice these terms (2^-7), and they grow with the
-    spike: 8x more from x8 to x64."""
+    The bars are the benchmark spec's absolute ones plus twice these terms (rel = 2^-7), and they grow with
+    the spike: 8x more from x8 to x64. The few-head kernel over an fp16 cache rounds the query and
+    the probabilities to fp16 (unit roundoff 2^-11): rel = 2^-10."""
     import numpy as np
     from oracle import OracleDims, absorbed_query, score_scale
     dims = OracleDims.of(case.dims)
@@ -387,8 +388,8 @@ def spike_budget(case, ref, mult):
         q = np.abs(np.concatenate([q_lat, q_pe], axis=1))                       # [n_h, 576]
         from gpu_helpers import oracle_prefix
         rows = np.abs(np.vstack([oracle_prefix(case, b), ref[b]["read_new"][None, :]]))  # [T, 576]
-        lse_bar.append(2e-2 + 2.0 ** -7 * scale * (rows @ q.T).max(axis=0))   # per head
-        u_bar.append(2e-2 + 2.0 ** -7 * float(np.max(np.abs(ref[b]["u"]))))
+        lse_bar.append(2e-2 + rel * scale * (rows @ q.T).max(axis=0))   # per head
+        u_bar.append(2e-2 + rel * float(np.max(np.abs(ref[b]["u"]))))
     return np.stack(lse_bar), np.array(u_bar)
 
 
@@ -401,8 +402,8 @@ def test_late_score_spike(key, mult):
     is scaled by `mult` (exact in every storage type, and the fp8 scale follows it); with 4 ranges
     over T = [1000, 300], both rows sit in later tiles of their ranges. At x64 the spike dominates
     some heads by far more than 2^64 (second pass), at x8 it does not; u is up to ~50x larger than in
-    the standard workloads. The MFMA kernels (configs 2, 4f8) are held to the error budget of
-    spike_budget, the float32 generic kernel (configs 0, 1) to the plain bars."""
+    the standard workloads. The MFMA kernels (configs 1, 2, 4f8, 4f6) are held to the error budget of
+    spike_budget, the float32 generic kernel (config 0) to the plain bars."""
     import numpy as np
     case = _case(key, 2, [1000, 300], stress=True)
     src = case.row_source()
@@ -424,14 +425,14 @@ def test_late_score_spike(key, mult):
     assert rl <= tr, rl
     if mult == 64:  # the second pass is reached
         assert float(np.max(lse_ref)) > 100.0, float(np.max(lse_ref))
-    if case.cfg.cdtype in ("f32", "f16"):
+    if case.cfg.cdtype == "f32":
         # float32 arithmetic on the stored values throughout: the absolute bars plus a float32
         # budget of 2^-16 relative (unit roundoff 2^-24 grown by sums of up to a few thousand terms)
         assert np.all(u_err <= ta + 2.0 ** -16 * np.max(np.abs(u_ref), axis=1)), u_err
-        lse_tol = (1e-4 if case.cfg.cdtype == "f32" else 2e-2) + 2.0 ** -16 * np.abs(lse_ref)
+        lse_tol = 1e-4 + 2.0 ** -16 * np.abs(lse_ref)
         assert np.all(lse_err <= lse_tol), float(np.max(lse_err - lse_tol))
         return
-    lse_bar, u_bar = spike_budget(case, ref, mult)
+    lse_bar, u_bar = spike_budget(case, ref, mult, 2.0 ** -10 if case.cfg.cdtype == "f16" else 2.0 ** -7)
     print(f"  budget: u max-abs <= {u_bar}, lse max-abs <= {lse_bar.min():.3e} .. {lse_bar.max():.3e}; "
           f"worst lse use {float(np.max(lse_err / lse_bar)):.2f} of its bar", flush=True)
     assert np.all(u_err <= u_bar), (u_err, u_bar)
