@@ -51,6 +51,28 @@ static OSplits o_splits(const mla_dims& d, int B) {
   return {1, split_for(cdiv(d.d, o_wide(B) ? 2 * gm::MT : gm::MT) * col_tiles(B), d.n_h * d.d_h / gm::KC, 1)};
 }
 
+// Wide products (N >= cgm::MIN_N: chunked prefill) run on the compute-shaped kernel k_cgemm:
+// 256 (or, for products of at most 128 rows, 128) rows x 128 columns per workgroup, two
+// workgroups per CU. Its K split only tops a small tile count up to about two workgroups per CU.
+namespace cgm {
+constexpr int MIN_N = 256;   // columns from which a product takes the compute-shaped kernel
+constexpr int BN = 128;      // columns per workgroup
+constexpr int BK = 32;       // k per stage
+}
+static int cg_bm(int Mtot) { return Mtot <= 128 ? 128 : 256; }
+// 256 x 256 tiles (one workgroup per CU) for long-K products with many rows: half the operand
+// traffic per MFMA of the 256 x 128 tile
+static bool cg_big(int Mtot, int K) { return Mtot >= 2048 && K >= 8192; }
+static int cg_split(int Mtot, int N, int K, int Z) {
+  const bool big = cg_big(Mtot, K);
+  const int slots = big ? 256 : 512;   // resident workgroups
+  const int tiles = cdiv(Mtot, cg_bm(Mtot)) * cdiv(N, big ? 2 * cgm::BN : cgm::BN) * Z;
+  if (tiles >= 3 * slots / 4) return 1;
+  int sk = (slots + tiles / 2) / tiles;
+  const int smax = K / 512 > 1 ? K / 512 : 1;   // at least 16 stages per slice
+  return sk < 1 ? 1 : (sk > smax ? smax : sk);
+}
+
 AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
   AbsorbQLayout L;
   const int sk1 = q_splits(d, B).sk1;
@@ -58,6 +80,11 @@ AbsorbQLayout absorb_q_layout(const mla_dims& d, int B) {
   L.off_qc = al256h((size_t)B * d.d_cq * 4);
   L.off_part = L.off_qc + al256h((size_t)B * d.n_h * d.d_h * 4);
   L.part_floats = sk1 > 1 ? (size_t)sk1 * B * (d.d_cq + d.d_c + d.d_r) : 0;
+  if (B >= cgm::MIN_N) {
+    const int m1 = d.d_cq + d.d_c + d.d_r, c1 = cg_split(m1, B, d.d, 1);
+    const size_t pc = c1 > 1 ? (size_t)c1 * B * m1 : 0;
+    if (pc > L.part_floats) L.part_floats = pc;
+  }
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
 }
@@ -67,7 +94,12 @@ AbsorbOutLayout absorb_out_layout(const mla_dims& d, int B) {
   L.off_o = 0;
   L.off_part = al256h((size_t)B * d.n_h * d.d_h * 4);
   const size_t p4 = sp.sk4 > 1 ? (size_t)sp.sk4 * d.n_h * B * d.d_h : 0;
-  const size_t p5 = sp.sk5 > 1 ? (size_t)sp.sk5 * B * d.d : 0;
+  size_t p5 = sp.sk5 > 1 ? (size_t)sp.sk5 * B * d.d : 0;
+  if (B >= cgm::MIN_N) {
+    const int c4 = cg_split(d.d_h, B, d.d_c, d.n_h), c5 = cg_split(d.d, B, d.n_h * d.d_h, 1);
+    if (c5 > 1 && (size_t)c5 * B * d.d > p5) p5 = (size_t)c5 * B * d.d;
+    if (c4 > 1 && (size_t)c4 * d.n_h * B * d.d_h > p5) p5 = (size_t)c4 * d.n_h * B * d.d_h;
+  }
   L.part_floats = p4 > p5 ? p4 : p5;
   L.bytes = L.off_part + al256h(L.part_floats * 4);
   return L;
@@ -83,6 +115,10 @@ AbsorbOutLayout absorb_out_pre_layout(const mla_dims& d, int B) {
   L.off_o = 0;
   L.off_part = 0;
   L.part_floats = sk > 1 ? (size_t)sk * B * d.d : 0;
+  if (B >= cgm::MIN_N) {
+    const int c5 = cg_split(d.d, B, d.n_h * d.d_c, 1);
+    if (c5 > 1 && (size_t)c5 * B * d.d > L.part_floats) L.part_floats = (size_t)c5 * B * d.d;
+  }
   L.bytes = al256h(L.part_floats * 4);
   return L;
 }
@@ -372,6 +408,177 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
         *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)(n0 + n) * seg.ldy[s] + r0 + mloc) = v;
       }
     }
+  }
+}
+
+// ================================================================================================
+// Compute-shaped MFMA GEMM for wide products (chunked prefill: N = chunk tokens, hundreds to
+// thousands): Y[n][m] = sum_k W(m, k) X[n][k], W bf16 row-major (lda = K) in stacked segments, X
+// float32 (split on the fly into bf16 hi + lo, 2 MFMAs) or bf16. Unlike the weight-streaming kernel
+// above, both operands are tiles: a workgroup owns BM = 64 WMB rows x BN = 64 WNB columns, its four
+// waves a 2 x 2 grid of (32 WMB) x (32 WNB) sub-tiles, so every operand fragment read from LDS feeds
+// WNB (rows) or WMB (columns) MFMAs. Stages of 32 k go through an NS-deep LDS ring (global -> LDS
+// copies, NS - 1 stages ahead of the math, one barrier per stage). LDS rows are XOR-swizzled in
+// 16-byte chunks (W and bf16 X: 4 chunks per row, key (row / 4) % 4; float32 X: 8 chunks, key
+// (row / 2) % 8), which makes the 16 lanes of each quarter-wave fragment read hit 16 distinct bank
+// groups. Tiles may straddle segments (each copy lane and each stored row finds its own segment).
+//   split_k > 1: partial sums go to part[(ky * Z + z) * N + n][m] for k_splitk_reduce.
+template <bool XF32, int WMB, int WNB, int NS>
+struct CgCfg {
+  static constexpr int BM = 64 * WMB, BN = 64 * WNB;
+  static constexpr int WB = BM * cgm::BK * 2;                   // W bytes per stage
+  static constexpr int XB = BN * cgm::BK * (XF32 ? 4 : 2);        // X bytes per stage
+  static constexpr int SB = WB + XB;
+  static constexpr int DW = WB / 4096, DX = XB / 4096;          // copies per thread per stage
+  static constexpr int DT = DW + DX;
+};
+
+__device__ __forceinline__ void g2l16_v(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+template <bool XF32, int WMB, int WNB, int NS>
+__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, int N, int ntn, int K, const void* __restrict__ Xv,
+                                                  int64_t ldx, int split_k, float* __restrict__ part, int Mtot,
+                                                  int64_t zW, int64_t zX, int64_t zY) {
+  using C = CgCfg<XF32, WMB, WNB, NS>;
+  constexpr int BM = C::BM, BN = C::BN, BK = cgm::BK, DW = C::DW, DX = C::DX, DT = C::DT;
+  constexpr int ESX = XF32 ? 4 : 2;
+  static_assert((NS - 1) * DT <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * C::SB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm = w & 1, wn = w >> 1;
+  // tile t = row tile * ntn + column tile; consecutive t (the column tiles of one row tile, which
+  // share its W rows) go to one XCD: workgroups are dealt round-robin to the 8 XCDs
+  const int ntm = (Mtot + BM - 1) / BM;
+  const int t = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  if (t >= ntm * ntn) return;  // padding workgroup (uniform)
+  const int mt = t / ntn, nt = t - mt * ntn;
+  const int ky = blockIdx.y, z = blockIdx.z, Z = gridDim.z;
+  const int m_base = mt * BM, n_base = nt * BN;
+  const int S = K / BK;
+  const int st0 = (int)((int64_t)S * ky / split_k), st1 = (int)((int64_t)S * (ky + 1) / split_k);
+  const int ns = st1 - st0;
+
+  // copy plan. W: slot p = 256 i + tid is row p / 4, physical chunk p % 4 (logical chunk
+  // (p % 4) ^ ((row / 4) % 4)); rows past the product re-read its last row.
+  const uint8_t* wsrc[DW];
+#pragma unroll
+  for (int i = 0; i < DW; ++i) {
+    const int p = 256 * i + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+    int m = m_base + row;
+    m = m < Mtot ? m : Mtot - 1;
+    const int sg = seg_of(seg, m);
+    wsrc[i] = (const uint8_t*)seg.W[sg] + ((int64_t)z * zW + (int64_t)(m - seg.m0[sg]) * K + (int64_t)st0 * BK + 8 * lc) * 2;
+  }
+  // X: float32 rows of 8 chunks (key (row / 2) % 8) or bf16 rows of 4 chunks (key (row / 4) % 4)
+  const uint8_t* xsrc[DX];
+#pragma unroll
+  for (int i = 0; i < DX; ++i) {
+    const int p = 256 * i + tid;
+    int row, lc;
+    if constexpr (XF32) { row = p >> 3; lc = (p & 7) ^ ((row >> 1) & 7); }
+    else { row = p >> 2; lc = (p & 3) ^ ((row >> 2) & 3); }
+    int n = n_base + row;
+    n = n < N ? n : N - 1;
+    xsrc[i] = (const uint8_t*)Xv + ((int64_t)z * zX + (int64_t)n * ldx + (int64_t)st0 * BK) * ESX + 16 * lc;
+  }
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    uint8_t* buf = lds + (j % NS) * C::SB;
+    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
+    const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
+#pragma unroll
+    for (int i = 0; i < DW; ++i) g2l16_v(wsrc[i] + (int64_t)j * BK * 2, wl + i * 4096);
+#pragma unroll
+    for (int i = 0; i < DX; ++i) g2l16_v(xsrc[i] + (int64_t)j * BK * ESX, xl + i * 4096);
+  };
+
+  // fragment offsets: A (m-block mb): row 32 WMB wm + 32 mb + l32, logical chunk 2 ks + g;
+  // B (n-block nb): row 32 WNB wn + 32 nb + l32, float32: logical chunks 4 ks + 2 g and + 1; bf16: 2 ks + g
+  auto a_off = [&](int mb, int ks) -> uint32_t {
+    const int row = 32 * WMB * wm + 32 * mb + l32;
+    return (uint32_t)(row * 64 + (((2 * ks + g) ^ ((row >> 2) & 3)) << 4));
+  };
+  auto b_off = [&](int nb, int ks, int h) -> uint32_t {
+    const int row = 32 * WNB * wn + 32 * nb + l32;
+    if constexpr (XF32) return (uint32_t)(C::WB + row * 128 + (((4 * ks + 2 * g + h) ^ ((row >> 1) & 7)) << 4));
+    else return (uint32_t)(C::WB + row * 64 + (((2 * ks + g) ^ ((row >> 2) & 3)) << 4));
+  };
+
+  f32x16 acc[WMB][WNB];
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) acc[mb][nb] = f32x16{};
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < ns) issue(j);
+  for (int j = 0; j < ns; ++j) {
+    // stage j landed (later stages may still be in flight); every wave is done with stage j - 1
+    const int ahead = (ns - 1 - j) < (NS - 2) ? (ns - 1 - j) : (NS - 2);
+    if (ahead >= 2) wait_copies_barrier<2 * DT>();
+    else if (ahead == 1) wait_copies_barrier<DT>();
+    else wait_copies_barrier<0>();
+    if (j + NS - 1 < ns) issue(j + NS - 1);   // into the buffer stage j - 1 used
+    const uint8_t* buf = lds + (j % NS) * C::SB;
+    // every fragment of the stage is requested at once, in the order of use (LDS reads complete in
+    // order, so the first MFMAs wait only for their own operands)
+    bf16x8 a[BK / 16][WMB];
+    f32x4 xr[BK / 16][WNB][XF32 ? 2 : 1];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) a[ks][mb] = *(const bf16x8*)(buf + a_off(mb, ks));
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int h = 0; h < (XF32 ? 2 : 1); ++h) xr[ks][nb][h] = *(const f32x4*)(buf + b_off(nb, ks, h));
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        if constexpr (XF32) {
+          bf16x8 bh, bl;
+          split_hi_lo(xr[ks][nb][0], xr[ks][nb][1], bh, bl);
+#pragma unroll
+          for (int mb = 0; mb < WMB; ++mb) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], bh, acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], bl, acc[mb][nb], 0, 0, 0);
+          }
+        } else {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, xr[ks][nb][0]);
+#pragma unroll
+          for (int mb = 0; mb < WMB; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b, acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // accumulator element r of lane (g, l32): column 32 WNB wn + 32 nb + l32, row 32 WMB wm + 32 mb +
+  // 8 (r / 4) + 4 g + r % 4 (four consecutive rows per r / 4; segment boundaries are multiples of 4)
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb) {
+    const int n = n_base + 32 * WNB * wn + 32 * nb + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int m = m_base + 32 * WMB * wm + 32 * mb + 8 * r4 + 4 * g;
+        if (m >= Mtot) continue;
+        const f32x4 v = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
+        if (split_k > 1) {
+          *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m) = v;
+        } else {
+          const int sg = seg_of(seg, m);
+          *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg])) = v;
+        }
+      }
   }
 }
 
@@ -825,6 +1032,23 @@ template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
                       float* part, int Z, int64_t zW, int64_t zX, int64_t zY, int mb = 4) {
   const int Mtot = sg.m0[sg.nseg];
+  if (N >= cgm::MIN_N) {
+    // wide product: compute-shaped tiles, with their own K split (the caller's is for the skinny shape)
+    const bool big = cg_big(Mtot, K);
+    const int bm = cg_bm(Mtot), ntn = cdiv(N, big ? 2 * cgm::BN : cgm::BN);
+    // a K split needs the caller's partial buffer (the layouts size it for the products that pass one)
+    const int sk = part != nullptr ? cg_split(Mtot, N, K, Z) : 1;
+    dim3 g2((unsigned)((cdiv(Mtot, bm) * ntn + 7) & ~7), sk, Z);
+    if (big) hipLaunchKernelGGL((k_cgemm<XF32, 4, 4, 3>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    else if (bm == 128) hipLaunchKernelGGL((k_cgemm<XF32, 2, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    else hipLaunchKernelGGL((k_cgemm<XF32, 4, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    if (sk > 1) {
+      const int64_t tot = (int64_t)N * (Mtot / 4);
+      hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((tot + 255) / 256), Z), dim3(256), 0, st, sg, N, Mtot,
+                         sk, part, zY);
+    }
+    return;
+  }
   mb = tile_mb(mb, N);
   dim3 grid(cdiv(Mtot, 32 * mb), split_k, Z);
   if (mb == 8) {
