@@ -215,7 +215,8 @@ MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
  * MLA_NOALLOC_SCRATCH_BYTES bytes per GPU (each GPU the library runs on holds it until the process
  * ends). The call allocates and frees nothing.
  *   Rejects (MLA_E_WORKSPACE, nothing launched) a B whose mla_absorb_out_workspace_bytes(dims, B)
- *   exceeds MLA_NOALLOC_SCRATCH_BYTES (at the DeepSeek-V2 shape: any B above 315).
+ *   exceeds MLA_NOALLOC_SCRATCH_BYTES (at the DeepSeek-V2 shape: any B above 255; from 256 columns
+ *   on, W^O takes the wide-product kernel, whose K-split partials outgrow the array).
  *   Every call on one GPU uses that GPU's one array: calls that overlap on the same GPU (other
  *   streams, other threads) race and must be ordered by the caller. */
 #define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)

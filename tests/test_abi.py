@@ -143,9 +143,9 @@ def test_absorb_out_noalloc_validation(L):
     assert L.mla_absorb_out_noalloc(ctypes.byref(d), 0, 0, None, None, None, None, None) == 0
     v2 = _dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
     limit = 32 << 20
-    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 315) <= limit
-    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 316) > limit
-    assert L.mla_absorb_out_noalloc(ctypes.byref(v2), 316, 2, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 255) <= limit
+    assert L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 256) > limit
+    assert L.mla_absorb_out_noalloc(ctypes.byref(v2), 256, 2, FAKE, FAKE, FAKE, FAKE, None) == 3
     assert b"scratch" in L.mla_last_error()
 
 

@@ -43,7 +43,7 @@ def test_absorb_out_noalloc_matches_workspace_call(key):
 def test_absorb_out_noalloc_rejects_oversized_batch():
     case = make_case(get_config("2"), device="cuda", B=1, T=2)
     d = mla.Dims.of(case.dims)
-    B = 316
+    B = 256
     o_lat = torch.zeros((B, 128, 512), dtype=torch.float32, device="cuda")
     u = torch.zeros((B, 5120), dtype=torch.float32, device="cuda")
     with pytest.raises(mla.MLAError, match="scratch"):
