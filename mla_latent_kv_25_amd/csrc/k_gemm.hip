@@ -153,6 +153,11 @@ __device__ __forceinline__ void g2l16_nt(const void* sbase, uint32_t voff, uint3
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+// The same copy from a per-lane 64-bit address (rows of different stacked products in one tile).
+__device__ __forceinline__ void g2l16_v_nt(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
 // At most N copies of this wave still in flight, this wave's LDS reads done, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_copies_barrier() {
@@ -248,28 +253,29 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
   const int n0 = nt * 32 * NB;                         // first column of this tile
   const int NL = (N - n0) < 32 * NB ? (N - n0) : 32 * NB;
   const int m_base = mt * MT;
-  const int s = seg_of(seg, m_base);
-  const int r0 = m_base - seg.m0[s];                  // first tile row inside its segment
-  const int seg_rows = seg.m0[s + 1] - seg.m0[s];
   const int S = K / KC;
   const int st0 = (int)((int64_t)S * ky / split_k), st1 = (int)((int64_t)S * (ky + 1) / split_k);
   const int ns = st1 - st0;
   constexpr int ESX = XF32 ? 4 : 2;
-  const uint8_t* Wb = (const uint8_t*)seg.W[s] + ((int64_t)z * zW + (int64_t)r0 * K) * 2;
   const uint8_t* Xb = (const uint8_t*)Xv + ((int64_t)z * zX + (int64_t)n0 * ldx) * ESX;
 
   // Copy plan: thread tid fills 16-byte LDS slots p = 256 i + tid. W slot p: row p / 8, physical
-  // chunk p % 8, which holds logical chunk (p % 8) ^ ((row / 2) % 8). X slot (bf16): same with
-  // 8 chunks per row; X slot (float32): 16 chunks per row, logical chunk (p % 16) ^ (row % 16).
+  // chunk p % 8, which holds logical chunk (p % 8) ^ ((row / 2) % 8); each W lane addresses its row
+  // in its own segment (a tile may straddle two stacked products), rows past the last one re-read
+  // it. X slot (bf16): same with 8 chunks per row; X slot (float32): 16 chunks per row, logical
+  // chunk (p % 16) ^ (row % 16).
   // Rows past the segment / past N re-read the last valid row (their results are dropped).
   uint32_t ofs[DT];
+  const uint8_t* wrow[C::DW];
   {
     const int wc = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
     for (int i = 0; i < C::DW; ++i) {
-      int row = i * 32 + (tid >> 3);
-      if (row > seg_rows - r0 - 1) row = seg_rows - r0 - 1;
-      ofs[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(wc << 4);
+      int m = m_base + i * 32 + (tid >> 3);
+      if (m > Mtot - 1) m = Mtot - 1;
+      const int sg = seg_of(seg, m);
+      wrow[i] = (const uint8_t*)seg.W[sg] + ((int64_t)z * zW + (int64_t)(m - seg.m0[sg]) * K) * 2 + (wc << 4);
+      ofs[i] = 0;
     }
 #pragma unroll
     for (int i = 0; i < C::DX; ++i) {
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
     uint8_t* buf = lds + (j % NS) * C::SB;
     if (i < C::DW) {
       const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + w * 1024));
-      g2l16_nt(Wb + (int64_t)kst * 2, ofs[i], wl + i * 4096);
+      g2l16_v_nt(wrow[i] + (int64_t)kst * 2, wl + i * 4096);
     } else {
       const uint32_t xl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS void*)(buf + C::WB + w * 1024));
       g2l16(Xb + (int64_t)kst * ESX, ofs[i], xl + (i - C::DW) * 4096);
@@ -401,11 +407,12 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
         const f32x4 x = reg[((ww * NB + jb) * 4 + r4) * 64 + ln];
         v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
       }
-      if (n >= NL || r0 + mloc >= seg_rows) continue;
+      if (n >= NL || m_base + mloc >= Mtot) continue;
       if (split_k > 1) {
         *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n0 + n) * Mtot + m_base + mloc) = v;
       } else {
-        *(f32x4*)(seg.Y[s] + (int64_t)z * zY + (int64_t)(n0 + n) * seg.ldy[s] + r0 + mloc) = v;
+        const int m = m_base + mloc, sg = seg_of(seg, m);  // segment boundaries are multiples of 4
+        *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)(n0 + n) * seg.ldy[sg] + (m - seg.m0[sg])) = v;
       }
     }
   }
@@ -1023,10 +1030,10 @@ static void wgemm_nb(hipStream_t st, dim3 grid, const Seg& sg, int N, int K, con
                      zW, zX, zY);
 }
 
-// Y = W X over stacked segments (segment boundaries on multiples of the row tile). Row tiles of
-// 32*mb rows: mb = 8 halves the X traffic per W byte (N <= 64 only), mb = 2 doubles the workgroup
-// count of short problems; otherwise 128 rows. N above 128 runs as 128-column tiles in the same
-// launch.
+// Y = W X over stacked segments (segment boundaries on multiples of 4; a tile may straddle them).
+// Row tiles of 32*mb rows: mb = 8 halves the X traffic per W byte (N <= 64 only), mb = 2 doubles
+// the workgroup count of short problems, mb = 3 gives the V2 shape's W^UQ/W^QR product one 96-row
+// tile per CU (256); otherwise 128 rows. N above 128 runs as 128-column tiles in the same launch.
 static int tile_mb(int mb, int N) { return (mb == 8 && N > 64) ? 4 : mb; }
 template <bool XF32>
 static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int split_k,
@@ -1054,6 +1061,10 @@ static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X
   if (mb == 8) {
     if (N <= 32) wgemm_nb<1, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
     else wgemm_nb<2, XF32, 8>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+  } else if (mb == 3) {
+    if (N <= 32) wgemm_nb<1, XF32, 3>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else if (N <= 64) wgemm_nb<2, XF32, 3>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
+    else wgemm_nb<4, XF32, 3>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
   } else if (mb == 2) {
     if (N <= 32) wgemm_nb<1, XF32, 2>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
     else if (N <= 64) wgemm_nb<2, XF32, 2>(st, grid, sg, N, K, X, ldx, split_k, part, Mtot, zW, zX, zY);
@@ -1094,7 +1105,7 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     s2.Y[0] = qc; s2.ldy[0] = nhdh;
     s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
     s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
-    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
+    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0, 3);
     // stage 3: q_lat_i = (W^UK_i)^T q^C_i, batch rows in chunks of up to 128 along grid z
     dim3 g3(d.d_c / absq::TC, d.n_h, cdiv(B, gm::MAXB));
     const uint16_t* wuk = (const uint16_t*)W_uk;
@@ -1257,7 +1268,7 @@ hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h,
     s2.Y[0] = q_lat; s2.ldy[0] = nhdc;
     s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
     s2.m0[0] = 0; s2.m0[1] = nhdc; s2.m0[2] = nhdc + d.n_h * d.d_r; s2.nseg = 2;
-    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0);
+    mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0, 3);
     return hipGetLastError();
   }
   valu_stacked(wdt, st, B, d.d, h, d.d, W_dq, d.d_cq, cq, d.d_cq, W_dkv, d.d_c, kv_new, rw, W_kr, d.d_r,
