@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="C",
                     help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
                          "(a separate JSON line; the default run is the decode step)")
+    ap.add_argument("--naive", action="store_true",
+                    help="with --prefill: the naive execution form (keys and values expanded per head)")
+    ap.add_argument("--prefix", type=int, default=2048, help="with --prefill: stored rows per sequence")
     ap.add_argument("--precombined", action="store_true",
                     help="the pre-combined absorption variant: W~^Q and W~^O built once, then one product each "
                          "in place of the two-step projections (a separate JSON line)")
@@ -181,10 +184,11 @@ def decode_subrecord(mla, key, splits):
 
 
 def prefill_bench(args):
-    """Chunked prefill of C tokens per sequence (B=16, 2048 stored rows each, bf16 V2 shape, paged):
-    mla_prefill_tables + the five decode calls over B*C causal pseudo-sequences. Throughput in chunk
-    tokens/s; the dominant kernel (decode_attn over the pseudo-sequences) is priced against the
-    dense bf16 MFMA peak."""
+    """Chunked prefill of C tokens per sequence (B=16, 2048 stored rows each by default, bf16 V2
+    shape, paged). Absorbed form: mla_prefill_tables + the five decode calls over B*C causal
+    pseudo-sequences, the dominant call (decode_attn) priced against the dense bf16 MFMA peak.
+    Naive form (--naive): tables, absorb_q_naive + rope, prefill_naive_attn (gather, K/V expansion,
+    attention), output_proj; the attention call priced likewise. Throughput in chunk tokens/s."""
     import numpy as np
     import torch
 
@@ -193,13 +197,32 @@ def prefill_bench(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mla.lib()
-    C, B, P0 = args.prefill, 16, 2048
+    C, B, P0 = args.prefill, 16, args.prefix
     cfg = get_config("3")
     case = make_prefill_case(cfg, [P0] * B, C, device="cuda")
     dims = case.dims
     cache = build_cache(mla, case)
-    pf = mla.PrefillStep(dims, B, C, int(case.block_table.shape[1]), args.splits)
+    pf = mla.PrefillStep(dims, B, C, int(case.block_table.shape[1]), args.splits, naive=args.naive,
+                         max_ctx=P0 + C if args.naive else None)
     W = case.weights
+
+    def one_naive(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mla.prefill_tables(cache, B, C, case.p0, pf.seq_lens, pf.block_table)
+        view = mla.LatentCache(cache.rows, cache.dtype, cache.t_cap, cache.scales, pf.block_table, cache.page_size)
+        st, d = pf.step, pf.dims
+        mla.absorb_q_naive(d, case.h_chunk.view(B * C, -1), W, st.ws_q, pf.q_c, st.q_pe, st.kv_new)
+        mla.rope(d, pf.seq_lens, st.q_pe, st.kv_new, view)
+        if ev is not None:
+            ev[1].record()
+        mla.prefill_naive_attn(d, B, C, pf.q_c, st.q_pe, cache, case.p0, pf.max_ctx, W["W_uk"], W["W_uv"], pf.ws_n,
+                               pf.o)
+        if ev is not None:
+            ev[2].record()
+        mla.output_proj(d, pf.o, W["W_o"], pf.ws_p, st.u)
+        if ev is not None:
+            ev[3].record()
 
     def one(ev=None):
         if ev is not None:
@@ -219,6 +242,8 @@ def prefill_bench(args):
         if ev is not None:
             ev[3].record()
 
+    if args.naive:
+        one = one_naive  # noqa: F811
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
@@ -235,21 +260,32 @@ def prefill_bench(args):
     torch.cuda.synchronize()
     st = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) * 1e-3 for k in range(3)]
     pairs = B * (C * P0 + C * (C + 1) // 2)                     # (query, key) pairs of the chunk
-    flops = pairs * 2 * dims.n_h * (dims.row + dims.d_c)         # 278,528 flop per pair at V2
+    if args.naive:
+        rows = B * (P0 + C)                                      # context rows expanded to K^C and V
+        flops = pairs * 2 * dims.n_h * (dims.d_h + dims.d_r + dims.d_h) + rows * 4 * dims.n_h * dims.d_h * dims.d_c
+        per_unit = (f"81,920 flop per (query, key) pair x {pairs} pairs + 33,554,432 flop per expanded row x "
+                    f"{rows} rows")
+        kern = "prefill_naive_attn"
+        names = ("tables+absorb_q_naive+rope", "prefill_naive_attn", "output_proj")
+    else:
+        flops = pairs * 2 * dims.n_h * (dims.row + dims.d_c)     # 278,528 flop per pair at V2
+        per_unit = f"278,528 flop per (query, key) pair x {pairs} pairs"
+        kern = "decode_attn"
+        names = ("tables+absorb_q+rope", "decode_attn", "combine+absorb_out")
     achieved = flops / st[1] / 1e12
     out = {
         "metric": "MLA chunked-prefill tokens/s (chunk tokens), 1 MI355X",
         "value": B * C / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 attention shape)",
-        "config": {"workload": f"chunked prefill: B={B} sequences x {P0} stored rows, chunk C={C}, bf16 paged "
-                               f"cache (64-row pages), DeepSeek-V2 shape", "batch": B, "chunk": C, "prefix": P0,
-                   "pseudo_sequences": B * C},
-        "kernels_us": {"tables+absorb_q+rope": st[0] * 1e6, "decode_attn": st[1] * 1e6,
-                       "combine+absorb_out": st[2] * 1e6, "step": ms * 1e3},
+        "config": {"workload": f"chunked prefill ({'naive' if args.naive else 'absorbed'} form): B={B} sequences "
+                               f"x {P0} stored rows, chunk C={C}, bf16 paged cache (64-row pages), DeepSeek-V2 "
+                               f"shape", "batch": B, "chunk": C, "prefix": P0, "pseudo_sequences": B * C,
+                   "form": "naive" if args.naive else "absorbed"},
+        "kernels_us": {names[0]: st[0] * 1e6, names[1]: st[1] * 1e6, names[2]: st[2] * 1e6, "step": ms * 1e3},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "decode_attn",
-                     "flops_per_launch": flops, "per_unit": f"278,528 flop per (query, key) pair x {pairs} pairs"},
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": kern,
+                     "flops_per_launch": flops, "per_unit": per_unit},
     }
     print(json.dumps(out), flush=True)
 

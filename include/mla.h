@@ -11,7 +11,8 @@
  * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
  * (chunked prefill: mla_prefill_tables, then the same five calls over the pseudo-sequences;
  *  pre-combined absorption: mla_precombine once, then mla_absorb_q_pre / mla_absorb_out_pre in
- *  place of mla_absorb_q / mla_absorb_out)
+ *  place of mla_absorb_q / mla_absorb_out; naive-form chunked prefill: mla_absorb_q_naive ->
+ *  mla_rope -> mla_prefill_naive_attn -> mla_output_proj)
  *
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers unless the comment says host. Tensors and workspaces must be
@@ -272,6 +273,57 @@ MLA_API size_t mla_absorb_out_pre_workspace_bytes(const mla_dims* dims, int32_t 
 MLA_API mla_status mla_absorb_out_pre(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
                               const void* Wo_pre, void* workspace, size_t ws_bytes, float* u,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Naive-form chunked prefill — the other execution path for a chunk of many query tokens.
+ * "DeepSeek-V2/V3: The Two Bills Behind MLA and MoE" (section "The First Bill") names two ways to
+ * run MLA: one that expands the keys and values, one that absorbs the up-projections. Here the
+ * cache stays latent either way; this path expands, per call, the keys and values of every
+ * context token of the chunk's sequences ("DeepSeek-V2 from Scratch" section 2.2:
+ * k^C_{j,i} = W^UK_i c^KV_j, v_{j,i} = W^UV_i c^KV_j; section 4.2: k_{j,i} = [k^C_{j,i}; k^R_j]) and
+ * runs attention per head on them (section 4.4) with the un-absorbed query
+ * q_{t,i} = [q^C_{t,i}; q^R_{t,i}]. Outputs equal those of the absorbed path up to rounding
+ * (section 5 of the same page: absorption is exact). Per (query, key) pair this form costs
+ * 2 n_h (d_h + d_r + d_h) flop against 2 n_h (d_c + d_r + d_c) absorbed, plus 4 n_h d_h d_c flop to
+ * expand each context token once per call: it wins for long chunks (the compute-bound regime).
+ *
+ * A chunk is:  mla_prefill_tables -> mla_absorb_q_naive -> mla_rope (the tables' lengths and
+ * view of the cache, as for the absorbed chunk) -> mla_prefill_naive_attn -> mla_output_proj.
+ * Kernels exist for d_h = 128, d_c = 512, d_r = 64 with the MFMA GEMM shapes (d and d_cq multiples
+ * of 256, n_h d_h a multiple of 256), bfloat16 weights and a bfloat16 cache; other cases return
+ * MLA_E_UNSUPPORTED.
+ *
+ * mla_absorb_q_naive — mla_absorb_q without the W^UK step: writes q_c [B, n_h, d_h] float32 (the
+ * content query q^C_{t,i}) in place of q_lat; q_pe and kv_new as mla_absorb_q (raw rotary parts).
+ * Workspace: mla_absorb_q_workspace_bytes(dims, B). W_uk is not read. */
+MLA_API mla_status mla_absorb_q_naive(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h,
+                              const void* W_dq, const void* W_uq, const void* W_qr, const void* W_dkv,
+                              const void* W_kr, void* workspace, size_t ws_bytes, float* q_c, float* q_pe,
+                              float* kv_new, hipStream_t stream);
+
+/* mla_prefill_naive_attn — causal attention of a C-token chunk per sequence over its expanded
+ * context. Token t of sequence b (row b * C + t of q_c / q_pe / o, position p0[b] + t) attends to
+ * cache rows 0 .. p0[b] + t, which must already hold the chunk's rows (mla_rope appends them).
+ *   q_c [B * C, n_h, d_h], q_pe [B * C, n_h, d_r] (rotated) float32; o [B * C, n_h, d_h] float32
+ *   (o_{t,i} of the page's section 4.4, before W^O);
+ *   cache: the sequences' own cache (block table [B, max_pages] when paged), bfloat16 rows;
+ *   p0: device int32 [B]; max_ctx (host): bound on every p0[b] + C, at most the cache capacity.
+ *   Keys beyond max_ctx are not read (a caller error leaves such outputs unspecified).
+ * Workspace (mla_prefill_naive_workspace_bytes(dims, B, max_ctx)): the gathered latent rows
+ * [B, max_ctx, d_c + d_r] and the expanded K^C and V [B * max_ctx, n_h d_h], all bfloat16. */
+MLA_API size_t mla_prefill_naive_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_ctx);
+MLA_API mla_status mla_prefill_naive_attn(const mla_dims* dims, int32_t B, int32_t C, int32_t wdtype,
+                                  const float* q_c, const float* q_pe, const mla_cache* cache,
+                                  const int32_t* p0, int32_t max_ctx, const void* W_uk, const void* W_uv,
+                                  void* workspace, size_t ws_bytes, float* o, hipStream_t stream);
+
+/* mla_output_proj — u = W^O [o_1; ...; o_nh] ("DeepSeek-V2 from Scratch" section 1, the output
+ * projection) for N rows of per-head outputs o [N, n_h * d_h] float32; u [N, d] float32. The
+ * workspace (K-split partial sums) needs mla_output_proj_workspace_bytes(dims, N) bytes, which may
+ * be 0 (then workspace may be NULL). */
+MLA_API size_t mla_output_proj_workspace_bytes(const mla_dims* dims, int32_t N);
+MLA_API mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, const float* o,
+                           const void* W_o, void* workspace, size_t ws_bytes, float* u, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_cache_store — write given rows into a cache (prefix fill; not part of a decode step).

@@ -79,6 +79,11 @@ def lib():
         "mla_absorb_out_pre_workspace_bytes": (SZ, [D, I32]),
         "mla_absorb_out_pre": (I32, [D, I32, I32, P, P, P, SZ, P, ST]),
         "mla_cache_store": (I32, [D, C, I32, P, I32, P, I64, ST]),
+        "mla_absorb_q_naive": (I32, [D, I32, I32, P, P, P, P, P, P, P, SZ, P, P, P, ST]),
+        "mla_prefill_naive_workspace_bytes": (SZ, [D, I32, I32]),
+        "mla_prefill_naive_attn": (I32, [D, I32, I32, I32, P, P, C, P, I32, P, P, P, SZ, P, ST]),
+        "mla_output_proj_workspace_bytes": (SZ, [D, I32]),
+        "mla_output_proj": (I32, [D, I32, I32, P, P, P, SZ, P, ST]),
         "mla_status_str": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
         "mla_version": (ctypes.c_char_p, []),
@@ -95,7 +100,9 @@ EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_deco
            "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
            "mla_absorb_out_noalloc",
            "mla_prefill_tables", "mla_precombine", "mla_absorb_q_pre", "mla_absorb_out_pre_workspace_bytes",
-           "mla_absorb_out_pre", "mla_cache_store", "mla_status_str", "mla_last_error", "mla_version")
+           "mla_absorb_out_pre", "mla_cache_store", "mla_absorb_q_naive", "mla_prefill_naive_workspace_bytes",
+           "mla_prefill_naive_attn", "mla_output_proj_workspace_bytes", "mla_output_proj",
+           "mla_status_str", "mla_last_error", "mla_version")
 
 
 def _check(status: int):
@@ -271,6 +278,46 @@ def cache_store(dims: Dims, cache: LatentCache, n_rows, max_rows: int, src, src_
                                  _ptr(src, torch.float32, "src"), src_stride, _stream()))
 
 
+def absorb_q_naive(dims: Dims, h, W, workspace, q_c, q_pe, kv_new):
+    """Query and KV pathways without the W^UK absorption: q_c [B, n_h, d_h] float32."""
+    wdt = DTYPE_CODE[h.dtype]
+    _check(lib().mla_absorb_q_naive(ctypes.byref(dims), h.shape[0], wdt, _ptr(h, name="h"),
+                                    _ptr(W["W_dq"], h.dtype, "W_dq"), _ptr(W["W_uq"], h.dtype, "W_uq"),
+                                    _ptr(W["W_qr"], h.dtype, "W_qr"), _ptr(W["W_dkv"], h.dtype, "W_dkv"),
+                                    _ptr(W["W_kr"], h.dtype, "W_kr"), _ptr(workspace, name="workspace"),
+                                    workspace.numel(), _ptr(q_c, torch.float32, "q_c"),
+                                    _ptr(q_pe, torch.float32, "q_pe"), _ptr(kv_new, torch.float32, "kv_new"),
+                                    _stream()))
+
+
+def prefill_naive_workspace_bytes(dims: Dims, B: int, max_ctx: int) -> int:
+    return lib().mla_prefill_naive_workspace_bytes(ctypes.byref(dims), B, max_ctx)
+
+
+def prefill_naive_attn(dims: Dims, B: int, C: int, q_c, q_pe, cache: LatentCache, p0, max_ctx: int, W_uk, W_uv,
+                       workspace, o):
+    """Causal attention of a C-token chunk per sequence on the expanded keys and values."""
+    cc = cache.c()
+    _check(lib().mla_prefill_naive_attn(ctypes.byref(dims), B, C, DTYPE_CODE[W_uk.dtype],
+                                        _ptr(q_c, torch.float32, "q_c"), _ptr(q_pe, torch.float32, "q_pe"),
+                                        ctypes.byref(cc), _ptr(p0, torch.int32, "p0"), max_ctx,
+                                        _ptr(W_uk, name="W_uk"), _ptr(W_uv, W_uk.dtype, "W_uv"),
+                                        _ptr(workspace, name="workspace"), workspace.numel(),
+                                        _ptr(o, torch.float32, "o"), _stream()))
+
+
+def output_proj_workspace_bytes(dims: Dims, N: int) -> int:
+    return lib().mla_output_proj_workspace_bytes(ctypes.byref(dims), N)
+
+
+def output_proj(dims: Dims, o, W_o, workspace, u):
+    """u = W^O o for o [N, n_h * d_h] float32."""
+    _check(lib().mla_output_proj(ctypes.byref(dims), o.shape[0], DTYPE_CODE[W_o.dtype], _ptr(o, torch.float32, "o"),
+                                 _ptr(W_o, name="W_o"), _ptr(workspace, name="workspace") if workspace is not None
+                                 else None, 0 if workspace is None else workspace.numel(),
+                                 _ptr(u, torch.float32, "u"), _stream()))
+
+
 def version() -> str:
     return lib().mla_version().decode()
 
@@ -329,16 +376,30 @@ class PrecombinedStep(DecodeStep):
 
 class PrefillStep:
     """Chunked prefill: C new tokens per sequence (positions p0[b] .. p0[b] + C - 1) as B * C causal
-    pseudo-sequences sharing their sequence's pages (mla_prefill_tables), run through the five
-    decode calls. Every chunk token's row is appended, and each token gets its causal output u."""
+    pseudo-sequences sharing their sequence's pages (mla_prefill_tables). Every chunk token's row is
+    appended, and each token gets its causal output u.
+      absorbed form (naive=False): the five decode calls over the pseudo-sequences;
+      naive form (naive=True): absorb_q_naive -> rope -> prefill_naive_attn -> output_proj, with
+      keys and values expanded for contexts of up to max_ctx rows (p0[b] + C <= max_ctx)."""
 
     def __init__(self, dims, B: int, C: int, max_pages: int, num_splits: int = 0, device="cuda",
-                 sm_scale: float = 0.0):
+                 sm_scale: float = 0.0, naive: bool = False, max_ctx: Optional[int] = None):
         self.B, self.C = B, C
+        self.naive = naive
         self.step = DecodeStep(dims, B * C, num_splits, device, sm_scale)
         self.dims = self.step.dims
         self.seq_lens = torch.empty(B * C, dtype=torch.int32, device=device)
         self.block_table = torch.empty((B * C, max_pages), dtype=torch.int32, device=device)
+        if naive:
+            if max_ctx is None:
+                raise MLAError("the naive form needs max_ctx (bound on p0[b] + C)")
+            self.max_ctx = max_ctx
+            f32 = dict(dtype=torch.float32, device=device)
+            self.q_c = torch.empty((B * C, dims.n_h, dims.d_h), **f32)
+            self.o = torch.empty((B * C, dims.n_h * dims.d_h), **f32)
+            u8 = dict(dtype=torch.uint8, device=device)
+            self.ws_n = torch.empty(max(1, prefill_naive_workspace_bytes(self.dims, B, max_ctx)), **u8)
+            self.ws_p = torch.empty(max(1, output_proj_workspace_bytes(self.dims, B * C)), **u8)
 
     def run(self, h_chunk, W, cache: LatentCache, p0):
         """h_chunk [B, C, d] (weight dtype); cache: paged, holding p0[b] rows of sequence b."""
@@ -346,5 +407,14 @@ class PrefillStep:
             raise MLAError("chunked prefill needs a paged cache")
         prefill_tables(cache, self.B, self.C, p0, self.seq_lens, self.block_table)
         view = LatentCache(cache.rows, cache.dtype, cache.t_cap, cache.scales, self.block_table, cache.page_size)
-        u = self.step.run(h_chunk.reshape(self.B * self.C, -1).contiguous(), W, view, self.seq_lens)
-        return u.view(self.B, self.C, -1)
+        h = h_chunk.reshape(self.B * self.C, -1).contiguous()
+        if not self.naive:
+            u = self.step.run(h, W, view, self.seq_lens)
+            return u.view(self.B, self.C, -1)
+        st = self.step
+        absorb_q_naive(self.dims, h, W, st.ws_q, self.q_c, st.q_pe, st.kv_new)
+        rope(self.dims, self.seq_lens, st.q_pe, st.kv_new, view)
+        prefill_naive_attn(self.dims, self.B, self.C, self.q_c, st.q_pe, cache, p0, self.max_ctx, W["W_uk"],
+                           W["W_uv"], self.ws_n, self.o)
+        output_proj(self.dims, self.o, W["W_o"], self.ws_p, st.u)
+        return st.u.view(self.B, self.C, -1)

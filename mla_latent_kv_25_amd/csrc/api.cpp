@@ -371,6 +371,93 @@ mla_status mla_prefill_tables(const mla_cache* cache, int32_t B, int32_t C, cons
                                                block_table_out, stream), fn);
 }
 
+mla_status mla_absorb_q_naive(const mla_dims* dims, int32_t B, int32_t wdtype, const void* h, const void* W_dq,
+                              const void* W_uq, const void* W_qr, const void* W_dkv, const void* W_kr,
+                              void* workspace, size_t ws_bytes, float* q_c, float* q_pe, float* kv_new,
+                              hipStream_t stream) {
+  const char* fn = "mla_absorb_q_naive";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (wdtype != MLA_BF16 || !mla::naive_supported(*dims))
+    return fail(MLA_E_UNSUPPORTED, "%s: the naive form needs bf16 weights, d_h=128, d_c=512, d_r=64", fn);
+  if (B == 0) return ok();
+  if (!h || !W_dq || !W_uq || !W_qr || !W_dkv || !W_kr || !q_c || !q_pe || !kv_new)
+    return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(h, W_dq, W_uq, W_qr, W_dkv, W_kr, q_c, q_pe, kv_new, workspace))
+    return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  if (!workspace || ws_bytes < mla_absorb_q_workspace_bytes(dims, B))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, mla_absorb_q_workspace_bytes(dims, B));
+  return hip_status(mla::launch_absorb_q_naive(*dims, B, h, W_dq, W_uq, W_qr, W_dkv, W_kr, workspace, q_c, q_pe,
+                                               kv_new, stream),
+                    fn);
+}
+
+size_t mla_prefill_naive_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_ctx) {
+  if (!dims || B <= 0 || max_ctx <= 0 || dims->n_h <= 0) return 0;
+  return mla::naive_layout(dims->n_h, B, max_ctx).bytes;
+}
+
+mla_status mla_prefill_naive_attn(const mla_dims* dims, int32_t B, int32_t C, int32_t wdtype, const float* q_c,
+                                  const float* q_pe, const mla_cache* cache, const int32_t* p0, int32_t max_ctx,
+                                  const void* W_uk, const void* W_uv, void* workspace, size_t ws_bytes, float* o,
+                                  hipStream_t stream) {
+  const char* fn = "mla_prefill_naive_attn";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  mla::CacheArgs c{};
+  s = check_cache(cache, fn, &c);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (C < 1) return fail(MLA_E_ARG, "%s: chunk length C must be >= 1", fn);
+  if (max_ctx < C) return fail(MLA_E_ARG, "%s: max_ctx must be >= C", fn);
+  if ((int64_t)max_ctx > c.t_cap) return fail(MLA_E_ARG, "%s: max_ctx exceeds the cache capacity", fn);
+  if ((int64_t)B * C > (int64_t)INT32_MAX / 2 || (int64_t)B * max_ctx > (int64_t)INT32_MAX / 2)
+    return fail(MLA_E_ARG, "%s: B * C or B * max_ctx too large", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (wdtype != MLA_BF16 || c.dtype != MLA_BF16 || !mla::naive_supported(*dims))
+    return fail(MLA_E_UNSUPPORTED, "%s: the naive form needs bf16 weights and cache, d_h=128, d_c=512, d_r=64", fn);
+  if (B == 0) return ok();
+  if (!q_c || !q_pe || !p0 || !W_uk || !W_uv || !o) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(q_c, q_pe, W_uk, W_uv, o, workspace) || misaligned4(p0))
+    return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = mla_prefill_naive_workspace_bytes(dims, B, max_ctx);
+  if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  const mla::NaiveLayout L = mla::naive_layout(dims->n_h, B, max_ctx);
+  char* ws = (char*)workspace;
+  hipError_t e = mla::launch_gather_rows(c, B, C, p0, max_ctx, ws + L.off_ctx, stream);
+  if (e == hipSuccess)
+    e = mla::launch_materialize_kv(*dims, B * max_ctx, ws + L.off_ctx, W_uk, W_uv, ws + L.off_kc, ws + L.off_v, stream);
+  if (e == hipSuccess)
+    e = mla::launch_mha_prefill(B, C, max_ctx, dims->n_h, p0, q_c, q_pe, workspace,
+                                resolve_scale(dims) * 1.4426950408889634f, o, stream);
+  return hip_status(e, fn);
+}
+
+size_t mla_output_proj_workspace_bytes(const mla_dims* dims, int32_t N) {
+  if (!dims || N <= 0) return 0;
+  return mla::output_proj_layout(*dims, N).bytes;
+}
+
+mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, const float* o, const void* W_o,
+                           void* workspace, size_t ws_bytes, float* u, hipStream_t stream) {
+  const char* fn = "mla_output_proj";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (N < 0) return fail(MLA_E_ARG, "%s: N < 0", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (wdtype != MLA_BF16 || !mla::naive_supported(*dims))
+    return fail(MLA_E_UNSUPPORTED, "%s: needs bf16 weights and the MFMA GEMM shapes", fn);
+  if (N == 0) return ok();
+  if (!o || !W_o || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(o, W_o, u, workspace)) return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = mla_output_proj_workspace_bytes(dims, N);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  return hip_status(mla::launch_output_proj(*dims, N, o, W_o, workspace, u, stream), fn);
+}
+
 mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t B, const int32_t* n_rows,
                            int32_t max_rows, const float* src, int64_t src_stride, hipStream_t stream) {
   const char* fn = "mla_cache_store";

@@ -445,7 +445,7 @@ __device__ __forceinline__ void g2l16_v(const void* src, uint32_t lds_addr) {
                :: "v"(src), "s"(lds_addr) : "memory", "m0");
 }
 
-template <bool XF32, int WMB, int WNB, int NS>
+template <bool XF32, int WMB, int WNB, int NS, bool OB16 = false>
 __global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, int N, int ntn, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part, int Mtot,
                                                   int64_t zW, int64_t zX, int64_t zY) {
@@ -581,6 +581,11 @@ __global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, i
         const f32x4 v = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
         if (split_k > 1) {
           *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m) = v;
+        } else if constexpr (OB16) {
+          // bf16 output (round to nearest even): Y holds uint16 elements, ldy in elements
+          const int sg = seg_of(seg, m);
+          uint16_t* y = (uint16_t*)seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg]);
+          *(u32x2*)y = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
           const int sg = seg_of(seg, m);
           *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg])) = v;
@@ -1152,6 +1157,83 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
   // W^O: the layout's partial area holds sk5 * B * d floats
   const int sk5 = o_splits(d, B).sk5;
   valu_splitk(wdt, st, d.d, B, nhdh, W_o, o, u, d.d, sk5, sk5 > 1 ? part : nullptr);
+  return hipGetLastError();
+}
+
+// ================================================================================================
+// Naive-form prefill pieces (k_naive.hip holds the attention): the query pathway without the W^UK
+// absorption, the keys and values of every context token, and W^O on the per-head outputs.
+
+// [c^Q | c^KV | k^R raw] = [W^DQ; W^DKV; W^KR] h, then [q^C | q^R raw] = [W^UQ; W^QR] c^Q, with q^C
+// written to the caller's buffer (the absorbed form goes on to W^UK instead).
+hipError_t launch_absorb_q_naive(const mla_dims& d, int B, const void* h, const void* W_dq, const void* W_uq,
+                                 const void* W_qr, const void* W_dkv, const void* W_kr, void* ws, float* q_c,
+                                 float* q_pe, float* kv_new, hipStream_t st) {
+  AbsorbQLayout L = absorb_q_layout(d, B);
+  float* cq = (float*)((char*)ws + L.off_cq);
+  float* part = (float*)((char*)ws + L.off_part);
+  const int rw = d.d_c + d.d_r;
+  const int nhdh = d.n_h * d.d_h;
+  Seg s1{};
+  s1.W[0] = W_dq; s1.W[1] = W_dkv; s1.W[2] = W_kr;
+  s1.Y[0] = cq; s1.ldy[0] = d.d_cq;
+  s1.Y[1] = kv_new; s1.ldy[1] = rw;
+  s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
+  s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
+  mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+  Seg s2{};
+  s2.W[0] = W_uq; s2.W[1] = W_qr;
+  s2.Y[0] = q_c; s2.ldy[0] = nhdh;
+  s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
+  s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
+  mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0, 3);
+  return hipGetLastError();
+}
+
+// K^C[r][i d_h + e] = sum_c W^UK[i d_h + e][c] ctx[r][c] and V[r][...] likewise with W^UV, for the
+// R gathered rows (576 elements each, latent first): one product of [W^UK; W^UV] with bf16 output.
+hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, const void* W_uk, const void* W_uv,
+                                 void* kc, void* vv, hipStream_t st) {
+  const int nhdh = d.n_h * d.d_h;
+  Seg sg{};
+  sg.W[0] = W_uk; sg.W[1] = W_uv;
+  sg.Y[0] = (float*)kc; sg.ldy[0] = nhdh;
+  sg.Y[1] = (float*)vv; sg.ldy[1] = nhdh;
+  sg.m0[0] = 0; sg.m0[1] = nhdh; sg.m0[2] = 2 * nhdh; sg.nseg = 2;
+  const int Mtot = 2 * nhdh, ntn = cdiv(R, cgm::BN);
+  dim3 g2((unsigned)((cdiv(Mtot, 256) * ntn + 7) & ~7), 1, 1);
+  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 2, true>), g2, dim3(256), 0, st, sg, R, ntn, d.d_c, ctx,
+                     (int64_t)(d.d_c + d.d_r), 1, (float*)nullptr, Mtot, (int64_t)0, (int64_t)0, (int64_t)0);
+  return hipGetLastError();
+}
+
+// dims the naive-form path has kernels for: the MFMA GEMM shapes and the attention kernel's d_h, d_c, d_r
+bool naive_supported(const mla_dims& d) {
+  return mfma_dims_ok(d) && d.d_h == 128 && d.d_c == 512 && d.d_r == 64;
+}
+
+// u = W^O o for per-head outputs o [N, n_h d_h] (float32); the workspace holds only K-split partials
+AbsorbOutLayout output_proj_layout(const mla_dims& d, int N) {
+  AbsorbOutLayout L;
+  const int sk5 = o_splits(d, N).sk5;
+  L.off_o = 0;
+  L.off_part = 0;
+  L.part_floats = sk5 > 1 ? (size_t)sk5 * N * d.d : 0;
+  if (N >= cgm::MIN_N) {
+    const int c5 = cg_split(d.d, N, d.n_h * d.d_h, 1);
+    if (c5 > 1 && (size_t)c5 * N * d.d > L.part_floats) L.part_floats = (size_t)c5 * N * d.d;
+  }
+  L.bytes = al256h(L.part_floats * 4);
+  return L;
+}
+hipError_t launch_output_proj(const mla_dims& d, int N, const float* o, const void* W_o, void* ws, float* u,
+                              hipStream_t st) {
+  float* part = (float*)ws;
+  const int nhdh = d.n_h * d.d_h;
+  Seg s5{};
+  s5.W[0] = W_o; s5.Y[0] = u; s5.ldy[0] = d.d;
+  s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
+  mfma_gemm<true>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
   return hipGetLastError();
 }
 

@@ -71,6 +71,24 @@ hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h,
 hipError_t launch_absorb_out_pre(const mla_dims& d, int B, int wdt, const float* o_lat, const void* Wo_pre, void* ws,
                                  float* u, hipStream_t st);
 
+// Naive-form prefill (k_naive.hip, k_gemm.hip): workspace of gathered rows [B, max_ctx, d_c + d_r]
+// bf16, K^C [B * max_ctx, n_h d_h] bf16 and V [B * max_ctx, n_h d_h] bf16 (d_h = 128, d_c = 512, d_r = 64).
+struct NaiveLayout { size_t off_ctx, off_kc, off_v, bytes; };
+NaiveLayout naive_layout(int n_h, int B, int max_ctx);
+hipError_t launch_gather_rows(const CacheArgs& c, int B, int C, const int32_t* p0, int max_ctx, void* ctx,
+                              hipStream_t st);
+hipError_t launch_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t* p0, const float* q_c,
+                              const float* q_pe, const void* ws, float qscale, float* o, hipStream_t st);
+hipError_t launch_absorb_q_naive(const mla_dims& d, int B, const void* h, const void* W_dq, const void* W_uq,
+                                 const void* W_qr, const void* W_dkv, const void* W_kr, void* ws, float* q_c,
+                                 float* q_pe, float* kv_new, hipStream_t st);
+hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, const void* W_uk, const void* W_uv,
+                                 void* kc, void* vv, hipStream_t st);
+AbsorbOutLayout output_proj_layout(const mla_dims& d, int N);
+hipError_t launch_output_proj(const mla_dims& d, int N, const float* o, const void* W_o, void* ws, float* u,
+                              hipStream_t st);
+bool naive_supported(const mla_dims& d);
+
 int device_cu_count();
 
 }  // namespace mla

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -183,6 +183,48 @@ def test_prefill_tables_validation(L):
     assert L.mla_prefill_tables(ctypes.byref(paged), 2, 4, None, FAKE, FAKE, None) == 1
     assert L.mla_prefill_tables(ctypes.byref(paged), 2, 4, ctypes.c_void_p(0x1002), FAKE, FAKE, None) == 1
     assert L.mla_prefill_tables(ctypes.byref(paged), 0, 4, None, None, None, None) == 0     # empty batch
+
+
+def test_naive_prefill_validation(L):
+    """The naive-form prefill calls check their arguments, and refuse shapes and types they have no
+    kernels for, before touching the device."""
+    v2 = _dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
+    run = _dims()
+    paged = _cache(page_size=64, t_cap=4096, block_table=0x3000, max_pages=64, num_pages=64)
+    W = [FAKE] * 5
+    need_q = L.mla_absorb_q_workspace_bytes(ctypes.byref(v2), 4)
+    # absorb_q_naive: bf16 weights at the V2 head shape only
+    assert L.mla_absorb_q_naive(ctypes.byref(run), 4, 2, FAKE, *W, FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == 2
+    assert L.mla_absorb_q_naive(ctypes.byref(v2), 4, 0, FAKE, *W, FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == 2
+    assert L.mla_absorb_q_naive(ctypes.byref(v2), 4, 2, None, *W, FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == 1
+    assert L.mla_absorb_q_naive(ctypes.byref(v2), 4, 2, FAKE, *W, FAKE, need_q - 1, FAKE, FAKE, FAKE, None) == 3
+    assert L.mla_absorb_q_naive(ctypes.byref(v2), 0, 2, *[None] * 6, None, 0, None, None, None, None) == 0
+    # workspace: gathered rows (d_c + d_r bf16) plus expanded K and V (2 n_h d_h bf16) per context row
+    need = L.mla_prefill_naive_workspace_bytes(ctypes.byref(v2), 2, 1000)
+    assert need >= 2 * 1000 * (576 * 2 + 2 * 16384 * 2)
+    assert L.mla_prefill_naive_workspace_bytes(ctypes.byref(v2), 0, 1000) == 0
+    attn = L.mla_prefill_naive_attn
+    ok = (FAKE, FAKE, ctypes.byref(paged), FAKE)
+    assert attn(ctypes.byref(v2), 2, 64, 2, *ok, 1000, FAKE, FAKE, FAKE, need - 1, FAKE, None) == 3
+    assert attn(ctypes.byref(v2), 2, 64, 2, *ok, 5000, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 1  # > capacity
+    assert b"capacity" in L.mla_last_error()
+    assert attn(ctypes.byref(v2), 2, 64, 2, *ok, 32, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 1    # max_ctx < C
+    assert attn(ctypes.byref(v2), 2, 0, 2, *ok, 1000, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 1   # C >= 1
+    fp8 = _cache(dtype=3, scales=0x2000, page_size=64, t_cap=4096, block_table=0x3000, max_pages=64, num_pages=64)
+    assert attn(ctypes.byref(v2), 2, 64, 2, FAKE, FAKE, ctypes.byref(fp8), FAKE, 1000, FAKE, FAKE, FAKE, 1 << 40,
+                FAKE, None) == 2                                                                    # bf16 cache only
+    assert attn(ctypes.byref(run), 2, 64, 2, *ok, 1000, FAKE, FAKE, FAKE, 1 << 40, FAKE, None) == 2
+    assert attn(ctypes.byref(v2), 2, 64, 2, FAKE, FAKE, ctypes.byref(paged), None, 1000, FAKE, FAKE, FAKE, 1 << 40,
+                FAKE, None) == 1                                                                    # p0 NULL
+    assert attn(ctypes.byref(v2), 0, 64, 2, None, None, ctypes.byref(paged), None, 1000, None, None, None, 0, None,
+                None) == 0
+    # output projection
+    need_o = L.mla_output_proj_workspace_bytes(ctypes.byref(v2), 512)
+    assert L.mla_output_proj(ctypes.byref(v2), 512, 2, None, FAKE, FAKE, need_o, FAKE, None) == 1
+    if need_o > 0:
+        assert L.mla_output_proj(ctypes.byref(v2), 512, 2, FAKE, FAKE, FAKE, need_o - 1, FAKE, None) == 3
+    assert L.mla_output_proj(ctypes.byref(v2), 512, 0, FAKE, FAKE, FAKE, need_o, FAKE, None) == 2
+    assert L.mla_output_proj(ctypes.byref(v2), 0, 2, None, None, None, 0, None, None) == 0
 
 
 def test_alignment_validation(L):
