@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="C",
                     help="chunked-prefill mode: C new tokens per sequence after 2048 stored rows, B=16 "
                          "(a separate JSON line; the default run is the decode step)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run mla_combine + mla_absorb_out instead of the fused mla_combine_absorb_out")
     ap.add_argument("--naive", action="store_true",
                     help="with --prefill: the naive execution form (keys and values expanded per head)")
     ap.add_argument("--prefix", type=int, default=2048, help="with --prefill: stored rows per sequence")
@@ -315,10 +317,13 @@ def main():
     case = make_case(cfg, device="cuda")
     B = case.B
     caches = [build_cache(mla, case) for _ in range(max(1, args.rotate))]
+    # the fused combine + W^UV call where it has kernels (DeepSeek-V2 head shape, bf16 weights)
+    fused = (not args.unfused and not args.precombined and dims.d_h == 128 and dims.d_c == 512 and dims.d_r == 64
+             and case.weights["W_uv"].dtype == torch.bfloat16)
     if args.precombined:
         step = mla.PrecombinedStep(dims, B, args.splits, case.weights)
     else:
-        step = mla.DecodeStep(dims, B, args.splits)
+        step = mla.DecodeStep(dims, B, args.splits, fused=fused)
     torch.cuda.synchronize()
     W, h, seq_lens = case.weights, case.h, case.seq_lens
     d = step.dims
@@ -348,6 +353,12 @@ def main():
         mla.decode_attn(d, step.q_lat, step.q_pe, cache, seq_lens, args.splits, step.ws_d)
         if ev is not None:
             ev[3].record()
+        if fused:
+            mla.combine_absorb_out(d, args.splits, step.ws_d, W["W_uv"], W["W_o"], step.ws_o, step.u, step.lse)
+            if ev is not None:
+                ev[4].record()
+                ev[5].record()
+            return
         mla.combine(d, args.splits, seq_lens, step.ws_d, step.o_lat, step.lse)
         if ev is not None:
             ev[4].record()
@@ -424,12 +435,17 @@ def main():
                    "n_h": dims.n_h, "d_c": dims.d_c, "d_r": dims.d_r, "d": dims.d,
                    "decode_splits": args.splits or ("one per CU" if dims.n_h == 128 else "two per CU"), "cache_copies_cycled": len(caches),
                    "hip_graph": bool(graphs),
-                   "absorption": "pre-combined" if args.precombined else "two-step"},
-        "latent_cache_gbps": cache_bytes / (t_dec + t_comb) / 1e9,
-        "latent_cache_pct_hbm_peak": 100.0 * cache_bytes / (t_dec + t_comb) / 1e9 / HBM_PEAK_GBPS,
-        "kernels_us": {"absorb_q": stage[0] * 1e6, "rope_append": stage[1] * 1e6, "decode_attn": t_dec * 1e6,
-                       "combine": t_comb * 1e6, "absorb_out": stage[4] * 1e6, "step": ms_step * 1e3},
-        "weights_gbps": {"absorb_q": wq_bytes / stage[0] / 1e9, "absorb_out": wo_bytes / stage[4] / 1e9},
+                   "absorption": "pre-combined" if args.precombined else "two-step",
+                   "combine": "fused with W^UV (mla_combine_absorb_out)" if fused else "separate call"},
+        # decode_attn + combine (fused runs: decode_attn alone, the merge being inside the output call)
+        "latent_cache_gbps": cache_bytes / (t_dec + (0.0 if fused else t_comb)) / 1e9,
+        "latent_cache_pct_hbm_peak": 100.0 * cache_bytes / (t_dec + (0.0 if fused else t_comb)) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": ({"absorb_q": stage[0] * 1e6, "rope_append": stage[1] * 1e6, "decode_attn": t_dec * 1e6,
+                        "combine_absorb_out": t_comb * 1e6, "step": ms_step * 1e3} if fused else
+                       {"absorb_q": stage[0] * 1e6, "rope_append": stage[1] * 1e6, "decode_attn": t_dec * 1e6,
+                        "combine": t_comb * 1e6, "absorb_out": stage[4] * 1e6, "step": ms_step * 1e3}),
+        "weights_gbps": {"absorb_q": wq_bytes / stage[0] / 1e9,
+                         "absorb_out": wo_bytes / (t_comb if fused else stage[4]) / 1e9},
         "weight_bytes": {"absorb_q": wq_bytes, "absorb_out": wo_bytes},
         "attn_mfma_tflops": flops_attn / t_dec / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -9,6 +9,7 @@
  * attention runs against the latents directly and the full keys/values are never formed.
  *
  * A full step is:  mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine -> mla_absorb_out
+ * (or, fused: mla_absorb_q -> mla_rope -> mla_decode_attn -> mla_combine_absorb_out)
  * (chunked prefill: mla_prefill_tables, then the same five calls over the pseudo-sequences;
  *  pre-combined absorption: mla_precombine once, then mla_absorb_q_pre / mla_absorb_out_pre in
  *  place of mla_absorb_q / mla_absorb_out; naive-form chunked prefill: mla_absorb_q_naive ->
@@ -223,6 +224,21 @@ MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
 #define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
 MLA_API mla_status mla_absorb_out_noalloc(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
                                   const void* W_uv, const void* W_o, float* u, hipStream_t stream);
+
+/* mla_combine_absorb_out — mla_combine followed by mla_absorb_out in one call, with the merge of
+ * the pieces fused into the per-head W^UV product: for each head i and sequence b the pieces'
+ * partials are merged ("DeepSeek-V2 from Scratch" section 4.4, the softmax regrouped) and
+ * multiplied by W^UV_i (section 5.2) without writing o_lat, then u = W^O [o_1; ...; o_nh]
+ * (section 6). Same results as the two calls up to rounding.
+ *   dec_workspace: the workspace mla_decode_attn filled (same B and num_splits);
+ *   workspace: mla_absorb_out_workspace_bytes(dims, B) bytes; u [B, d] float32;
+ *   lse: optional [B, n_h] float32 (NULL to skip), as mla_combine writes it.
+ * Kernels exist for bf16 weights with d_h = 128, d_c = 512, d_r = 64 (and the MFMA GEMM shapes);
+ * other cases return MLA_E_UNSUPPORTED and the caller uses mla_combine + mla_absorb_out. */
+MLA_API mla_status mla_combine_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, int32_t num_splits,
+                                  const void* dec_workspace, size_t dec_ws_bytes, const void* W_uv,
+                                  const void* W_o, void* workspace, size_t ws_bytes, float* u, float* lse,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_prefill_tables — chunked prefill through the decode calls.

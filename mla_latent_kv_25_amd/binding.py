@@ -79,6 +79,7 @@ def lib():
         "mla_absorb_out_pre_workspace_bytes": (SZ, [D, I32]),
         "mla_absorb_out_pre": (I32, [D, I32, I32, P, P, P, SZ, P, ST]),
         "mla_cache_store": (I32, [D, C, I32, P, I32, P, I64, ST]),
+        "mla_combine_absorb_out": (I32, [D, I32, I32, I32, P, SZ, P, P, P, SZ, P, P, ST]),
         "mla_absorb_q_naive": (I32, [D, I32, I32, P, P, P, P, P, P, P, SZ, P, P, P, ST]),
         "mla_prefill_naive_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_prefill_naive_attn": (I32, [D, I32, I32, I32, P, P, C, P, I32, P, P, P, SZ, P, ST]),
@@ -100,7 +101,7 @@ EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_deco
            "mla_decode_attn", "mla_combine", "mla_absorb_out_workspace_bytes", "mla_absorb_out",
            "mla_absorb_out_noalloc",
            "mla_prefill_tables", "mla_precombine", "mla_absorb_q_pre", "mla_absorb_out_pre_workspace_bytes",
-           "mla_absorb_out_pre", "mla_cache_store", "mla_absorb_q_naive", "mla_prefill_naive_workspace_bytes",
+           "mla_absorb_out_pre", "mla_cache_store", "mla_combine_absorb_out", "mla_absorb_q_naive", "mla_prefill_naive_workspace_bytes",
            "mla_prefill_naive_attn", "mla_output_proj_workspace_bytes", "mla_output_proj",
            "mla_status_str", "mla_last_error", "mla_version")
 
@@ -222,6 +223,15 @@ def absorb_out(dims: Dims, o_lat, W_uv, W_o, workspace, u):
                                 _ptr(u, torch.float32, "u"), _stream()))
 
 
+def combine_absorb_out(dims: Dims, num_splits: int, dec_workspace, W_uv, W_o, workspace, u, lse=None):
+    """mla_combine + mla_absorb_out fused: u [B, d] (and lse [B, n_h] if given) from the pieces."""
+    _check(lib().mla_combine_absorb_out(ctypes.byref(dims), u.shape[0], DTYPE_CODE[W_uv.dtype], num_splits,
+                                        _ptr(dec_workspace, name="dec_workspace"), dec_workspace.numel(),
+                                        _ptr(W_uv, name="W_uv"), _ptr(W_o, W_uv.dtype, "W_o"),
+                                        _ptr(workspace, name="workspace"), workspace.numel(),
+                                        _ptr(u, torch.float32, "u"), _ptr(lse, torch.float32, "lse"), _stream()))
+
+
 def absorb_out_noalloc(dims: Dims, o_lat, W_uv, W_o, u):
     """absorb_out with the library's static scratch in place of a workspace (no allocation)."""
     wdt = DTYPE_CODE[W_uv.dtype]
@@ -324,12 +334,14 @@ def version() -> str:
 
 # ------------------------------------------------------------------------------------------------
 class DecodeStep:
-    """Buffers for the five calls of one decode step, allocated once (torch), reused per step."""
+    """Buffers for the five calls of one decode step, allocated once (torch), reused per step.
+    fused=True runs combine and absorb_out as the one call mla_combine_absorb_out."""
 
-    def __init__(self, dims, B: int, num_splits: int, device="cuda", sm_scale: float = 0.0):
+    def __init__(self, dims, B: int, num_splits: int, device="cuda", sm_scale: float = 0.0, fused: bool = False):
         self.dims = Dims.of(dims, sm_scale)
         self.B = B
         self.num_splits = num_splits
+        self.fused = fused
         f32 = dict(dtype=torch.float32, device=device)
         self.q_lat = torch.empty((B, dims.n_h, dims.d_c), **f32)
         self.q_pe = torch.empty((B, dims.n_h, dims.d_r), **f32)
@@ -347,8 +359,11 @@ class DecodeStep:
         absorb_q(self.dims, h, W, self.ws_q, self.q_lat, self.q_pe, self.kv_new)
         rope(self.dims, seq_lens, self.q_pe, self.kv_new, cache)
         decode_attn(self.dims, self.q_lat, self.q_pe, cache, seq_lens, self.num_splits, self.ws_d)
-        combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
-        absorb_out(self.dims, self.o_lat, W["W_uv"], W["W_o"], self.ws_o, self.u)
+        if self.fused:
+            combine_absorb_out(self.dims, self.num_splits, self.ws_d, W["W_uv"], W["W_o"], self.ws_o, self.u, self.lse)
+        else:
+            combine(self.dims, self.num_splits, seq_lens, self.ws_d, self.o_lat, self.lse)
+            absorb_out(self.dims, self.o_lat, W["W_uv"], W["W_o"], self.ws_o, self.u)
         return self.u
 
 

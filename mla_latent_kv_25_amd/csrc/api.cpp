@@ -279,6 +279,34 @@ mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const
   return hip_status(mla::launch_absorb_out(*dims, B, wdtype, o_lat, W_uv, W_o, workspace, u, stream), fn);
 }
 
+mla_status mla_combine_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, int32_t num_splits,
+                                  const void* dec_workspace, size_t dec_ws_bytes, const void* W_uv, const void* W_o,
+                                  void* workspace, size_t ws_bytes, float* u, float* lse, hipStream_t stream) {
+  const char* fn = "mla_combine_absorb_out";
+  mla_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (B < 0) return fail(MLA_E_ARG, "%s: B < 0", fn);
+  if (num_splits < 0 || num_splits > 1024) return fail(MLA_E_ARG, "%s: num_splits must be in [0, 1024]", fn);
+  if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  const int G = resolve_splits(dims, num_splits);
+  if (wdtype != MLA_BF16 || !mla::naive_supported(*dims) || !mla::combine_uv_supported(*dims, G))
+    return fail(MLA_E_UNSUPPORTED, "%s: needs bf16 weights, d_h=128, d_c=512, d_r=64 (use mla_combine + "
+                "mla_absorb_out)", fn);
+  if (B == 0) return ok();
+  if (!dec_workspace || !W_uv || !W_o || !u) return fail(MLA_E_ARG, "%s: NULL tensor pointer", fn);
+  if (misaligned(dec_workspace, W_uv, W_o, u, workspace) || misaligned4(lse))
+    return fail(MLA_E_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need_d = mla::decode_layout(*dims, B, G).bytes;
+  if (dec_ws_bytes < need_d) return fail(MLA_E_WORKSPACE, "%s: decode workspace needs %zu bytes", fn, need_d);
+  const size_t need = mla_absorb_out_workspace_bytes(dims, B);
+  if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  const mla::AbsorbOutLayout L = mla::absorb_out_layout(*dims, B);
+  float* o = (float*)((char*)workspace + L.off_o);
+  hipError_t e = mla::launch_combine_uv(*dims, B, G, dec_workspace, W_uv, o, lse, stream);
+  if (e == hipSuccess) e = mla::launch_output_proj(*dims, B, o, W_o, (char*)workspace + L.off_part, u, stream);
+  return hip_status(e, fn);
+}
+
 mla_status mla_absorb_out_noalloc(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
                                   const void* W_uv, const void* W_o, float* u, hipStream_t stream) {
   const char* fn = "mla_absorb_out_noalloc";

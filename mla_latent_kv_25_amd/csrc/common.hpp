@@ -154,6 +154,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Partition of the batch's tokens into G contiguous ranges of (nearly) equal length:
 // range p covers global tokens [start(p), start(p+1)) with start(p) = floor(p * total / G).
+// Eight float32 values as two bf16 octets whose sum carries ~16 significant bits: hi is the
+// round-to-nearest bf16 of each value, lo the bf16 of what hi leaves over (MFMA on both halves
+// keeps a float32 operand's precision on the bf16 datapath).
+__device__ __forceinline__ void split_hi_lo(const f32x4& v0, const f32x4& v1, bf16x8& bh, bf16x8& bl) {
+  uint32_t hv[4], lv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
+    const float x1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
+    const uint32_t h = pack_bf16x2(x0, x1);
+    hv[e] = h;
+    lv[e] = pack_bf16x2(x0 - __builtin_bit_cast(float, h << 16), x1 - __builtin_bit_cast(float, h & 0xffff0000u));
+  }
+  bh = __builtin_bit_cast(bf16x8, u32x4{hv[0], hv[1], hv[2], hv[3]});
+  bl = __builtin_bit_cast(bf16x8, u32x4{lv[0], lv[1], lv[2], lv[3]});
+}
+
 __device__ __forceinline__ int64_t range_start(int64_t p, int64_t total, int64_t G) {
   return (p * total) / G;
 }

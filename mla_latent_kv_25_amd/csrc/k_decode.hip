@@ -2139,6 +2139,180 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 // ================================================================================================
+// Combine fused with the per-head value up-projection ("DeepSeek-V2 from Scratch" section 4.4 for
+// the softmax regrouped over pieces, section 5.2 for o_i = W^UV_i o_lat_i): workgroup = (head i,
+// 32 sequences). It merges the pieces of its sequences for head i alone (o_lat_i never goes to
+// HBM) and multiplies by W^UV_i on MFMA, writing o [B, n_h d_h] float32 for the W^O product.
+//   phase 0: every wave requests its 32 rows of W^UV_i as A fragments (32 k-steps of 16, kept in
+//            registers), so the weight read overlaps the combine;
+//   phase 1: lane j of wave 0 lists the pieces of sequence j and their weights (as k_combine);
+//   phase 2: 8 threads per sequence sum the pieces' rows (piece by piece) into LDS as bf16 hi/lo;
+//   phase 3: D[e][b] = sum_c W^UV_i[e][c] o_lat_i[b][c] on 32x32x16 bf16 MFMA, hi then lo part.
+namespace cuv {
+constexpr int DC = 512, DH = 128, SB = 32;   // d_c, d_h, sequences per workgroup
+constexpr int PITCH = DC + 8;                // bf16 elements per o_lat row in LDS
+constexpr int MAXP = 1024 + SB;              // pieces of SB sequences: at most G + SB - 1
+}
+__global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, int ntiles, const int64_t* __restrict__ cu,
+                                                       const int32_t* __restrict__ fmt,
+                                                       const float* __restrict__ lse_part,
+                                                       const float* __restrict__ sc_part, const void* __restrict__ o_part,
+                                                       const uint16_t* __restrict__ W_uv, float* __restrict__ o,
+                                                       float* __restrict__ lse_out) {
+  using namespace cuv;
+  __shared__ __attribute__((aligned(16))) uint16_t hi[SB * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t lo[SB * PITCH];
+  __shared__ int slots[MAXP];
+  __shared__ float wts[MAXP];   // lse of each piece, then its weight
+  __shared__ float scs[MAXP];
+  __shared__ int pbeg[SB + 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // tile t = head * nslices + slice; consecutive tiles (the slices of one head, sharing W^UV_i)
+  // go to one XCD (workgroups are dealt round-robin to the 8 XCDs)
+  const int t = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  const int nsl = (B + SB - 1) / SB;
+  const int i = t / nsl, sl = t - i * nsl;
+  const int b0 = sl * SB;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // phase 0: A fragments of rows 32 w + l32 of W^UV_i, k = 16 ks + 8 g .. + 7
+  bf16x8 a[DC / 16];
+  const uint16_t* wrow = W_uv + ((int64_t)i * DH + 32 * w + l32) * DC + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < DC / 16; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
+
+  // phase 1: pieces and weights per sequence (lane j of wave 0 owns sequence b0 + j)
+  const bool f16 = *fmt == 2;
+  const int64_t total = cu[B];
+  if (w == 0) {
+    int np = 0;
+    int64_t plo = 0, phi = -1;
+    const int b = b0 + lane;
+    if (lane < SB && b < B) {
+      const int64_t s0 = cu[b], s1 = cu[b + 1];
+      if (s1 > s0) {
+        plo = range_of(s0, total, G);
+        phi = range_of(s1 - 1, total, G);
+        for (int64_t p = plo; p <= phi; ++p) np += range_start(p, total, G) != range_start(p + 1, total, G);
+      }
+    }
+    // exclusive prefix of np over the 32 sequences
+    int incl = np;
+#pragma unroll
+    for (int o2 = 1; o2 < 32; o2 <<= 1) {
+      const int x = __shfl_up(incl, o2, 64);
+      if ((lane & 31) >= o2) incl += x;
+    }
+    const int beg = incl - np;
+    if (lane < SB) pbeg[lane] = beg < MAXP ? beg : MAXP;
+    if (lane == SB - 1) pbeg[SB] = incl < MAXP ? incl : MAXP;
+    if (lane < SB) {
+      // one pass of loads (lse and scale of every piece), then the weights from LDS
+      int k = beg;
+      for (int64_t p = plo; p <= phi; ++p)
+        if (range_start(p, total, G) != range_start(p + 1, total, G) && k < MAXP) {
+          const int64_t r = (p + b) * n_h + i;
+          slots[k] = (int)(p + b);
+          wts[k] = lse_part[r];
+          scs[k] = f16 ? sc_part[r] : 1.f;
+          ++k;
+        }
+      float M = -__builtin_inff();
+      for (int q = beg; q < k; ++q) M = fmaxf(M, wts[q]);
+      float sum = 0.f;
+      for (int q = beg; q < k; ++q) sum += __expf(wts[q] - M);
+      const float inv = 1.f / sum;
+      for (int q = beg; q < k; ++q) wts[q] = __expf(wts[q] - M) * inv * scs[q];
+      if (lse_out && b < B) lse_out[(int64_t)b * n_h + i] = k > beg ? M + __logf(sum) : -__builtin_inff();
+    }
+  }
+  __syncthreads();
+
+  // phase 2: thread (j = tid / 8, u = tid % 8) sums columns 64 k + 8 u .. + 7 (k = 0..7) of
+  // sequence b0 + j's pieces; a sequence past the batch or with no pieces gives zeros
+  {
+    const int j = tid >> 3, u = tid & 7;
+    const int q0 = pbeg[j], q1 = pbeg[j + 1];
+    f32x4 acc[8][2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k][0] = acc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t pst = (int64_t)n_h * DC;
+    const _Float16* ph = (const _Float16*)o_part + (int64_t)i * DC + 8 * u;
+    auto add16 = [&](float wk, const f16x8 (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][0][e] += wk * (float)x[k][e];
+          acc[k][1][e] += wk * (float)x[k][4 + e];
+        }
+    };
+    int q = q0;
+    if (f16) {
+      // two pieces' rows requested together, then added in piece order
+      for (; q + 1 < q1; q += 2) {
+        f16x8 x0[8], x1[8];
+        const _Float16* s0p = ph + (int64_t)slots[q] * pst;
+        const _Float16* s1p = ph + (int64_t)slots[q + 1] * pst;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x0[k] = *(const f16x8*)(s0p + 64 * k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x1[k] = *(const f16x8*)(s1p + 64 * k);
+        add16(wts[q], x0);
+        add16(wts[q + 1], x1);
+      }
+    }
+    for (; q < q1; ++q) {
+      const float wk = wts[q];
+      const int64_t base = (int64_t)slots[q] * pst + (int64_t)i * DC + 8 * u;
+      if (f16) {
+        f16x8 x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = *((const f16x8*)((const _Float16*)o_part + base + 64 * k));
+        add16(wk, x);
+      } else {
+        const float* src = (const float*)o_part + base;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const f32x4 x0 = *(const f32x4*)(src + 64 * k), x1 = *(const f32x4*)(src + 64 * k + 4);
+          acc[k][0] += wk * x0;
+          acc[k][1] += wk * x1;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      bf16x8 bh, bl;
+      split_hi_lo(acc[k][0], acc[k][1], bh, bl);
+      const int off = j * PITCH + 64 * k + 8 * u;
+      *(bf16x8*)(hi + off) = bh;
+      *(bf16x8*)(lo + off) = bl;
+    }
+  }
+  __syncthreads();
+
+  // phase 3: D[e = 32 w + row][b = l32], B operand column l32, k = 16 ks + 8 g .. + 7
+  f32x16 D = {};
+  const int boff = l32 * PITCH + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < DC / 16; ++ks) {
+    const bf16x8 bh = *(const bf16x8*)(hi + boff + 16 * ks);
+    const bf16x8 bl = *(const bf16x8*)(lo + boff + 16 * ks);
+    D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bh, D, 0, 0, 0);
+    D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bl, D, 0, 0, 0);
+  }
+  // element r of lane (g, l32): row 8 (r / 4) + 4 g + r % 4, column l32
+  const int b = b0 + l32;
+  if (b < B) {
+    float* dst = o + (int64_t)b * n_h * DH + (int64_t)i * DH + 32 * w + 4 * g;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *(f32x4*)(dst + 8 * r4) = f32x4{D[4 * r4], D[4 * r4 + 1], D[4 * r4 + 2], D[4 * r4 + 3]};
+  }
+}
+
+// ================================================================================================
 static bool is_v2(const mla_dims& d) { return d.n_h == v2::NH && d.d_c == v2::DC && d.d_r == v2::DR; }
 static bool v2_page_ok(int ps) { return ps == 0 || (ps >= 32 && (ps & (ps - 1)) == 0); }
 
@@ -2240,6 +2414,23 @@ hipError_t launch_combine(const mla_dims& d, int B, int G, const void* ws, float
   hipLaunchKernelGGL(k_combine, grid, dim3(256), smem, st, d.n_h, d.d_c, ch, d.d_c / nchunk, (const int64_t*)(base + L.off_cu), B, G,
                      (const int32_t*)(base + L.off_fmt), (const float*)(base + L.off_lse),
                      (const float*)(base + L.off_sc), (const void*)(base + L.off_o), o_lat, lse);
+  return hipGetLastError();
+}
+
+bool combine_uv_supported(const mla_dims& d, int G) {
+  return d.d_c == cuv::DC && d.d_h == cuv::DH && G + cuv::SB - 1 <= cuv::MAXP;
+}
+
+hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, const void* W_uv, float* o, float* lse,
+                             hipStream_t st) {
+  if (!combine_uv_supported(d, G)) return hipErrorNotSupported;
+  DecodeLayout L = decode_layout(d, B, G);
+  const char* base = (const char*)ws;
+  const int ntiles = d.n_h * ((B + cuv::SB - 1) / cuv::SB);
+  hipLaunchKernelGGL(k_combine_uv, dim3((unsigned)((ntiles + 7) & ~7)), dim3(256), 0, st, d.n_h, B, G, ntiles,
+                     (const int64_t*)(base + L.off_cu), (const int32_t*)(base + L.off_fmt),
+                     (const float*)(base + L.off_lse), (const float*)(base + L.off_sc), (const void*)(base + L.off_o),
+                     (const uint16_t*)W_uv, o, lse);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -225,6 +225,25 @@ def test_naive_prefill_validation(L):
         assert L.mla_output_proj(ctypes.byref(v2), 512, 2, FAKE, FAKE, FAKE, need_o - 1, FAKE, None) == 3
     assert L.mla_output_proj(ctypes.byref(v2), 512, 0, FAKE, FAKE, FAKE, need_o, FAKE, None) == 2
     assert L.mla_output_proj(ctypes.byref(v2), 0, 2, None, None, None, 0, None, None) == 0
+
+
+def test_combine_absorb_out_validation(L):
+    """The fused combine + absorb_out call checks both workspaces and refuses the shapes it has no
+    kernel for (the caller then uses mla_combine + mla_absorb_out)."""
+    v2 = _dims(d=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_r=64)
+    run = _dims()
+    f = L.mla_combine_absorb_out
+    need_d = L.mla_decode_workspace_bytes(ctypes.byref(v2), 4, 8)
+    need_o = L.mla_absorb_out_workspace_bytes(ctypes.byref(v2), 4)
+    assert f(ctypes.byref(run), 4, 2, 8, FAKE, 1 << 40, FAKE, FAKE, FAKE, 1 << 40, FAKE, None, None) == 2
+    assert f(ctypes.byref(v2), 4, 0, 8, FAKE, 1 << 40, FAKE, FAKE, FAKE, 1 << 40, FAKE, None, None) == 2
+    assert f(ctypes.byref(v2), 4, 2, 8, FAKE, need_d - 1, FAKE, FAKE, FAKE, need_o, FAKE, None, None) == 3
+    assert f(ctypes.byref(v2), 4, 2, 8, FAKE, need_d, FAKE, FAKE, FAKE, need_o - 1, FAKE, None, None) == 3
+    assert f(ctypes.byref(v2), 4, 2, 8, None, need_d, FAKE, FAKE, FAKE, need_o, FAKE, None, None) == 1
+    assert f(ctypes.byref(v2), 4, 2, 8, FAKE, need_d, FAKE, FAKE, FAKE, need_o, FAKE, ctypes.c_void_p(0x1002),
+             None) == 1                                                                             # lse alignment
+    assert f(ctypes.byref(v2), 4, 2, 2000, FAKE, need_d, FAKE, FAKE, FAKE, need_o, FAKE, None, None) == 1
+    assert f(ctypes.byref(v2), 0, 2, 8, None, 0, None, None, None, 0, None, None, None) == 0
 
 
 def test_alignment_validation(L):

@@ -1,0 +1,64 @@
+"""GPU: mla_combine_absorb_out (the combine fused with the per-head W^UV product) against the
+oracle, and against mla_combine + mla_absorb_out on the same decode workspace.
+
+Cases: DeepSeek-V2 shape with bf16, fp8 and fp6 caches (f16 partials), ragged and single-token
+contexts, more ranges than tokens, batches that leave the last 32-sequence slice partly empty,
+and the full config-2 batch (B = 64) on short contexts.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mla_latent_kv_25_amd as mla  # noqa: E402
+from synth import get_config, make_case  # noqa: E402
+
+from gpu_helpers import build_cache, check_u, rel_l2, run_oracle  # noqa: E402
+
+CASES = [
+    # (config, B, lengths, layout override, stress, num_splits)
+    ("2", 3, [300, 1, 77], None, True, 4),
+    ("2", 2, [3, 40], None, True, 64),
+    ("3", 4, [700, 129, 31, 1500], None, True, 7),
+    ("4f8", 3, [900, 64, 2], "paged", True, 5),
+    ("4f6", 2, [2000, 33], None, True, 3),
+    ("2", 33, None, None, False, 0),
+]
+
+
+@pytest.mark.parametrize("key,B,T,layout,stress,splits", CASES,
+                         ids=[f"cfg{c[0]}-B{c[1]}-S{c[5]}" for c in CASES])
+def test_fused_combine_absorb_out(key, B, T, layout, stress, splits):
+    T = T if T is not None else [int(x) for x in np.random.default_rng(5).integers(1, 400, size=B)]
+    cfg = get_config(key, stress=stress)
+    case = make_case(cfg, device="cuda", B=B, T=T, layout=layout)
+    print(f"fused case cfg={key} B={B} T={T[:6]} splits={splits}", flush=True)
+    c1, c2 = build_cache(case), build_cache(case)
+    s1 = mla.DecodeStep(case.dims, B, splits)
+    s2 = mla.DecodeStep(case.dims, B, splits, fused=True)
+    u1 = s1.run(case.h, case.weights, c1, case.seq_lens).clone()
+    u2 = s2.run(case.h, case.weights, c2, case.seq_lens).clone()
+    torch.cuda.synchronize()
+    # same decode workspace contents: the two orders of the same sums agree to float32 rounding
+    assert rel_l2(u2.double().cpu().numpy(), u1.double().cpu().numpy()) < 1e-5
+    assert float((s1.lse - s2.lse).abs().max()) <= 1e-6
+    if B <= 4:
+        ref = run_oracle(case)
+        check_u(u2.double().cpu().numpy(), np.stack([ref[b]["u"] for b in range(B)]), case.cfg.cdtype,
+                f"fused cfg{key}")
+
+
+def test_fused_without_lse():
+    """lse is optional: NULL skips it and leaves u unchanged."""
+    case = make_case(get_config("2"), device="cuda", B=2, T=[50, 9])
+    c = build_cache(case)
+    s = mla.DecodeStep(case.dims, 2, 3, fused=True)
+    u_ref = s.run(case.h, case.weights, c, case.seq_lens).clone()
+    u = torch.empty_like(u_ref)
+    mla.combine_absorb_out(s.dims, 3, s.ws_d, case.weights["W_uv"], case.weights["W_o"], s.ws_o, u, None)
+    torch.cuda.synchronize()
+    assert torch.equal(u, u_ref)
