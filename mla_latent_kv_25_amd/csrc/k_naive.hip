@@ -10,7 +10,7 @@
 //                  (rows past a sequence's context zero-filled, so that the keys and values built from
 //                  them are finite zeros);
 //   K^C and V:     one product (k_gemm.hip, bf16 output) of the gathered latents with [W^UK ; W^UV];
-//   k_mha_prefill: per (query block, head, sequence) workgroup, flash-style attention on MFMA.
+//   k_mha_prefill: per (128-query block, head, sequence) workgroup, flash-style attention on MFMA.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,21 +42,26 @@ __global__ __launch_bounds__(256) void k_gather_rows(CacheArgs c, int B, int C, 
 }
 
 // ------------------------------------------------------------------------------------ attention
-// Workgroup = 4 waves over QB = 64 NQB queries of one (sequence b, head i); wave w owns queries
-// 16 NQB w .. + 16 NQB. The keys come in 32-key tiles shared by the four waves through a 3-slot LDS
-// ring (global -> LDS copies; each wave issues 6 of the 24 1-KB copies of a tile, one barrier per
-// tile). A tile holds the keys' rows [k^C (128) | k^R (64)] (25 chunks per row, an odd stride, so the
-// row reads of 16 lanes hit 16 distinct bank groups) and their value rows (18 chunks per row, which
-// makes the transposing reads conflict-free).
-//   scores: S^T[16 keys x 16 queries] blocks on MFMA 16x16x32 (key rows as A, the queries of the
-//     lane's column as B, 6 k-steps over 192 dims, the scale folded into the query); lane (g, n) gets
-//     query n's scores of keys 4g..4g+3 and 16+4g..16+4g+3, which are the eight values the PV product
-//     needs from that lane as its B operand (the reduction runs over the tile's keys in that order);
-//   softmax: online, per query, in float32 (base 2);
-//   PV: O^T[16 value columns x 16 queries] += V^T P^T per 16 columns, V^T by transposing 16-bit reads.
+// Workgroup = 4 waves over 128 queries of one (sequence b, head i); wave w owns queries
+// tq0 + 32 w .. + 31, two waves per SIMD (two workgroups per CU). The keys come in 32-key tiles
+// shared by the four waves through a 3-slot LDS ring (global -> LDS copies; each wave issues 6 of
+// the 24 1-KB copies of a tile, one barrier per tile). A tile holds the keys' rows
+// [k^C (128) | k^R (64)] (25 chunks per row, an odd stride, so the row reads of 16 lanes hit 16
+// distinct bank groups) and their value rows (18 chunks per row, which makes the transposing
+// reads conflict-free).
+//   scores: S^T[32 keys x 32 queries] on MFMA 32x32x16 (key rows as A, the wave's queries as B,
+//     12 k-steps over 192 dims, the scale folded into the bf16 query); lane (g, n) gets query n's
+//     scores of keys 8 (r / 4) + 4 g + r % 4, r = 0..15: values r = 0..7 and 8..15 are that lane's
+//     B operand for the two 16-key steps of the PV product (the reduction runs over the keys in
+//     that order);
+//   softmax: online, per query, in float32 (base 2); the rescale of O is skipped when no query of
+//     the wave raised its maximum;
+//   PV: O^T[32 value columns x 32 queries] += V^T P^T per 32 columns, V^T by transposing 16-bit
+//     reads (rows 16 kk + 4 g .. + 3 and 16 kk + 8 + 4 g .. + 3 for lane half g).
 // Causal: query t (position p0[b] + t) sees keys 0 .. p0[b] + t.
 namespace nv {
 constexpr int DH = 128, DR = 64, DC = 512;  // d_h, d_r, d_c (the DeepSeek-V2 shape; any head count)
+constexpr int QB = 128;                // queries per workgroup
 constexpr int TT = 32;                 // keys per tile
 constexpr int KCHP = 25;               // LDS stride of a key row in 16-byte chunks (24 used)
 constexpr int VCHP = 18;               // LDS stride of a value row in chunks (16 used)
@@ -67,8 +72,7 @@ constexpr int NSLOT = 3;
 constexpr int NCP = 6;                 // copies per wave per tile
 }
 
-template <int NQB>
-__global__ __launch_bounds__(256, NQB == 1 ? 2 : 1) void k_mha_prefill(int C, int max_ctx, int n_h, const int32_t* __restrict__ p0,
+__global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int n_h, const int32_t* __restrict__ p0,
                                                         const float* __restrict__ q_c, const float* __restrict__ q_pe,
                                                         const uint16_t* __restrict__ ctx, const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vv, float qscale,
@@ -76,12 +80,12 @@ __global__ __launch_bounds__(256, NQB == 1 ? 2 : 1) void k_mha_prefill(int C, in
   using namespace nv;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NSLOT * SLOT];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, n = lane & 15;
+  const int g = lane >> 5, n = lane & 31;
   const int qb = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int NHD = n_h * DH;
   const int P0 = p0[b] > 0 ? p0[b] : 0;
-  const int tq0 = 64 * NQB * qb;                              // first query of the workgroup
-  const int tqe = C < tq0 + 64 * NQB ? C : tq0 + 64 * NQB;    // one past its last
+  const int tq0 = QB * qb;                                    // first query of the workgroup
+  const int tqe = C < tq0 + QB ? C : tq0 + QB;                // one past its last
   // keys 0 .. P0 + tqe - 1 (held to the gathered rows: a context beyond max_ctx is a caller error)
   const int nkeys = P0 + tqe < max_ctx ? P0 + tqe : max_ctx;
   const int ntiles = (nkeys + TT - 1) / TT;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256, NQB == 1 ? 2 : 1) void k_mha_prefill(int C, in
 #pragma unroll
   for (int k = 0; k < NCP; ++k) {
     const int q = 64 * (4 * k + w) + lane;
-    int row, src;  // src: byte offset inside the source row (bit 15 set: value rows)
+    int row, src;  // src: byte offset inside the source row (bit 15 set: value rows, bit 14: k^R)
     if (q < TT * KCHP) {
       row = q / KCHP;
       const int cc = q % KCHP;
@@ -131,36 +135,31 @@ __global__ __launch_bounds__(256, NQB == 1 ? 2 : 1) void k_mha_prefill(int C, in
   };
 
   if (ntiles > 0) issue(0);
-  // queries of the wave: query block qq (16 queries), lane column n: t = tq0 + 16 (NQB w + qq) + n;
-  // dims 32 ks + 8 g .. + 7 of [q^C (128) | q^R (64)], times qscale, as bf16 B fragments
-  bf16x8 qf[NQB][6];
-  int tpos[NQB];
-#pragma unroll
-  for (int qq = 0; qq < NQB; ++qq) {
-    const int t = tq0 + 16 * (NQB * w + qq) + n;
-    tpos[qq] = t < C ? P0 + t : -1;
+  // the wave's queries: lane column n: t = tq0 + 32 w + n; B fragment ks holds dims
+  // 16 ks + 8 g .. + 7 of [q^C (128) | q^R (64)], times qscale, in bf16
+  const int t = tq0 + 32 * w + n;
+  const int tpos = t < C ? P0 + t : -1;
+  bf16x8 qf[12];
+  {
     const int tc = t < C ? t : C - 1;
     const int64_t tok = (int64_t)b * C + tc;
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) {
-      const int d0 = 32 * ks + 8 * g;
+    for (int ks = 0; ks < 12; ++ks) {
+      const int d0 = 16 * ks + 8 * g;
       const float* src = d0 < DH ? q_c + tok * NHD + (int64_t)i * DH + d0 : q_pe + (tok * n_h + i) * DR + (d0 - DH);
       const f32x4 a = *(const f32x4*)src * qscale, c4 = *(const f32x4*)(src + 4) * qscale;
-      qf[qq][ks] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                          (__bf16)c4[0], (__bf16)c4[1], (__bf16)c4[2], (__bf16)c4[3]};
+      qf[ks] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                      (__bf16)c4[0], (__bf16)c4[1], (__bf16)c4[2], (__bf16)c4[3]};
     }
   }
   if (ntiles > 1) issue(1);
+  // first query position of the wave: tiles wholly at or below it need no mask
+  const int wpos0 = tq0 + 32 * w < C ? P0 + tq0 + 32 * w : -1;
 
-  float m_run[NQB], l_run[NQB];
-  f32x4 O[NQB][8];
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x16 O[4];
 #pragma unroll
-  for (int qq = 0; qq < NQB; ++qq) {
-    m_run[qq] = -__builtin_inff();
-    l_run[qq] = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) O[qq][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int vb = 0; vb < 4; ++vb) O[vb] = f32x16{};
 
   for (int it = 0; it < ntiles; ++it) {
     // tile it landed (tile it + 1 may be in flight); every wave is done with tile it - 1
@@ -169,73 +168,68 @@ __global__ __launch_bounds__(256, NQB == 1 ? 2 : 1) void k_mha_prefill(int C, in
     if (it + 2 < ntiles) issue(it + 2);  // into the slot tile it - 1 used
     const uint8_t* tile = lds + (it % NSLOT) * SLOT;
     const int j0 = TT * it;
-    // key fragments (shared by the query blocks): rows n and 16 + n, chunk 4 ks + g
-    bf16x8 ka[2][6];
+    // scores: key row n, chunk 2 ks + g
+    f32x16 S = {};
+    const uint8_t* krow = tile + (n * KCHP + g) * 16;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < 12; ++ks)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + 32 * ks), qf[ks], S, 0, 0, 0);
+    // causal mask (tiles that reach past the wave's first query position)
+    if (j0 + TT - 1 > wpos0) {
+      const int lim = tpos - j0;
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) ka[kb][ks] = *(const bf16x8*)(tile + ((16 * kb + n) * KCHP + 4 * ks + g) * 16);
-    // value fragments: rows 4g + n/4 and 16 + 4g + n/4, columns 16 cb + 4 (n % 4)
-    const uint8_t* va = tile + VOFF + (4 * g + (n >> 2)) * VCHP * 16 + (n & 3) * 8;
-    bf16x8 vf[8];
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(va + 32 * cb));
-      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(va + 16 * VCHP * 16 + 32 * cb));
-      vf[cb] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, x0).x, __builtin_bit_cast(u32x2, x0).y,
-                                                __builtin_bit_cast(u32x2, x1).x, __builtin_bit_cast(u32x2, x1).y});
+      for (int r = 0; r < 16; ++r) S[r] = 8 * (r >> 2) + 4 * g + (r & 3) <= lim ? S[r] : -__builtin_inff();
     }
+    float tm = S[0];
 #pragma unroll
-    for (int qq = 0; qq < NQB; ++qq) {
-      f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 1; r < 16; ++r) tm = fmaxf(tm, S[r]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    const float m_new = fmaxf(m_run, tm);
+    // a query that sees no key of this tile keeps its state (and a query past the chunk sees none)
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    float rs = 0.f;
+    bf16x8 pf[2];
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][ks], qf[qq][ks], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][ks], qf[qq][ks], S1, 0, 0, 0);
-      }
-      // causal mask: key j0 + 4g + r (S0) / j0 + 16 + 4g + r (S1) is seen iff it is <= the query's position
-      const int lim = tpos[qq] - j0;
-      float tm = -__builtin_inff();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S0[r] = 4 * g + r <= lim ? S0[r] : -__builtin_inff();
-        S1[r] = 16 + 4 * g + r <= lim ? S1[r] : -__builtin_inff();
-        tm = fmaxf(tm, fmaxf(S0[r], S1[r]));
-      }
-      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-      const float m_new = fmaxf(m_run[qq], tm);
-      // a query that sees no key of this tile keeps its state (and a query past the chunk sees none)
-      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qq] - m_use);
-      float rs = 0.f;
-      bf16x8 pf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e0 = __builtin_amdgcn_exp2f(S0[r] - m_use), e1 = __builtin_amdgcn_exp2f(S1[r] - m_use);
-        rs += e0 + e1;
-        pf[r] = (__bf16)e0;
-        pf[4 + r] = (__bf16)e1;
-      }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[qq] = l_run[qq] * alpha + rs;
-      m_run[qq] = m_new;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        O[qq][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cb], pf, O[qq][cb] * alpha, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(S[r] - m_use);
+      rs += e;
+      pf[r >> 3][r & 7] = (__bf16)e;
     }
+    rs += __shfl_xor(rs, 32, 64);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) O[vb] *= alpha;
+    }
+    l_run += rs;
+    m_run = m_new;
+    // PV: value rows 16 kk + 4 g + (j16 / 4) (+ 8), columns 32 vb + 16 (n / 16) + 4 (j16 % 4)
+    const int j16 = lane & 15;
+    const uint8_t* va = tile + VOFF + (4 * g + (j16 >> 2)) * VCHP * 16 + (16 * (n >> 4) + 4 * (j16 & 3)) * 2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const uint8_t* pa = va + 16 * kk * VCHP * 16 + 64 * vb;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)pa);
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(pa + 8 * VCHP * 16));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, x0).x, __builtin_bit_cast(u32x2, x0).y,
+                                                           __builtin_bit_cast(u32x2, x1).x, __builtin_bit_cast(u32x2, x1).y});
+        O[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], O[vb], 0, 0, 0);
+      }
   }
-  // o[b * C + t][i * 128 + 16 cb + 4 g .. + 3] = O / l
-#pragma unroll
-  for (int qq = 0; qq < NQB; ++qq) {
-    const int t = tq0 + 16 * (NQB * w + qq) + n;
-    if (t >= C) continue;
-    const float inv = 1.f / l_run[qq];
+  // o[b * C + t][i * 128 + 32 vb + 8 (r / 4) + 4 g + r % 4] = O / l
+  if (t < C) {
+    const float inv = 1.f / l_run;
     float* dst = o + ((int64_t)b * C + t) * NHD + (int64_t)i * DH + 4 * g;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) *(f32x4*)(dst + 16 * cb) = O[qq][cb] * inv;
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(f32x4*)(dst + 32 * vb + 8 * r4) =
+            f32x4{O[vb][4 * r4], O[vb][4 * r4 + 1], O[vb][4 * r4 + 2], O[vb][4 * r4 + 3]} * inv;
   }
 }
 
@@ -264,13 +258,8 @@ hipError_t launch_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t*
   const uint16_t* ctx = (const uint16_t*)((const char*)ws + L.off_ctx);
   const uint16_t* kc = (const uint16_t*)((const char*)ws + L.off_kc);
   const uint16_t* vv = (const uint16_t*)((const char*)ws + L.off_v);
-  if (C > 64) {
-    hipLaunchKernelGGL(k_mha_prefill<2>, dim3((unsigned)((C + 127) / 128), n_h, B), dim3(256), 0, st, C, max_ctx, n_h,
-                       p0, q_c, q_pe, ctx, kc, vv, qscale, o);
-  } else {
-    hipLaunchKernelGGL(k_mha_prefill<1>, dim3((unsigned)((C + 63) / 64), n_h, B), dim3(256), 0, st, C, max_ctx, n_h,
-                       p0, q_c, q_pe, ctx, kc, vv, qscale, o);
-  }
+  hipLaunchKernelGGL(k_mha_prefill, dim3((unsigned)((C + nv::QB - 1) / nv::QB), n_h, B), dim3(256), 0, st, C, max_ctx,
+                     n_h, p0, q_c, q_pe, ctx, kc, vv, qscale, o);
   return hipGetLastError();
 }
 
