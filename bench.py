@@ -239,8 +239,11 @@ def prefill_bench(args):
         mla.decode_attn(d, st.q_lat, st.q_pe, view, pf.seq_lens, args.splits, st.ws_d)
         if ev is not None:
             ev[2].record()
-        mla.combine(d, args.splits, pf.seq_lens, st.ws_d, st.o_lat, st.lse)
-        mla.absorb_out(d, st.o_lat, W["W_uv"], W["W_o"], st.ws_o, st.u)
+        if st.fused and W["W_uv"].dtype == torch.bfloat16:
+            mla.combine_absorb_out(d, args.splits, st.ws_d, W["W_uv"], W["W_o"], st.ws_o, st.u, st.lse)
+        else:
+            mla.combine(d, args.splits, pf.seq_lens, st.ws_d, st.o_lat, st.lse)
+            mla.absorb_out(d, st.o_lat, W["W_uv"], W["W_o"], st.ws_o, st.u)
         if ev is not None:
             ev[3].record()
 

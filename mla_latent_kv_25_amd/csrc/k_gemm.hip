@@ -432,7 +432,7 @@ __device__ __forceinline__ void g2l16_v(const void* src, uint32_t lds_addr) {
 }
 
 template <bool XF32, int WMB, int WNB, int NS, bool OB16 = false>
-__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, int N, int ntn, int K, const void* __restrict__ Xv,
+__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, int N, int ntn, int gm, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part, int Mtot,
                                                   int64_t zW, int64_t zX, int64_t zY) {
   using C = CgCfg<XF32, WMB, WNB, NS>;
@@ -443,12 +443,15 @@ __global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, i
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int wm = w & 1, wn = w >> 1;
-  // tile t = row tile * ntn + column tile; consecutive t (the column tiles of one row tile, which
-  // share its W rows) go to one XCD: workgroups are dealt round-robin to the 8 XCDs
+  // consecutive tiles t go to one XCD (workgroups are dealt round-robin to the 8 XCDs)
   const int ntm = (Mtot + BM - 1) / BM;
   const int t = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
   if (t >= ntm * ntn) return;  // padding workgroup (uniform)
-  const int mt = t / ntn, nt = t - mt * ntn;
+  // bands of gm row tiles, column tile by column tile inside a band: the tiles in flight on one XCD
+  // then share a few W row tiles and a few X column tiles in its L2 (gm = 1: row tile by row tile)
+  const int band = t / (gm * ntn), gmb = (ntm - band * gm) < gm ? (ntm - band * gm) : gm;
+  const int idx = t - band * gm * ntn;
+  const int nt = idx / gmb, mt = band * gm + (idx - nt * gmb);
   const int ky = blockIdx.y, z = blockIdx.z, Z = gridDim.z;
   const int m_base = mt * BM, n_base = nt * BN;
   const int S = K / BK;
@@ -1037,9 +1040,10 @@ static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X
     // a K split needs the caller's partial buffer (the layouts size it for the products that pass one)
     const int sk = part != nullptr ? cg_split(Mtot, N, K, Z) : 1;
     dim3 g2((unsigned)((cdiv(Mtot, bm) * ntn + 7) & ~7), sk, Z);
-    if (big) hipLaunchKernelGGL((k_cgemm<XF32, 4, 4, 3>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
-    else if (bm == 128) hipLaunchKernelGGL((k_cgemm<XF32, 2, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
-    else hipLaunchKernelGGL((k_cgemm<XF32, 4, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    // bands of 4 row tiles: the tiles in flight on one XCD share W and X stages in its L2
+    if (big) hipLaunchKernelGGL((k_cgemm<XF32, 4, 4, 3>), g2, dim3(256), 0, st, sg, N, ntn, 4, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    else if (bm == 128) hipLaunchKernelGGL((k_cgemm<XF32, 2, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, 4, K, X, ldx, sk, part, Mtot, zW, zX, zY);
+    else hipLaunchKernelGGL((k_cgemm<XF32, 4, 2, 2>), g2, dim3(256), 0, st, sg, N, ntn, 4, K, X, ldx, sk, part, Mtot, zW, zX, zY);
     if (sk > 1) {
       const int64_t tot = (int64_t)N * (Mtot / 4);
       hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((tot + 255) / 256), Z), dim3(256), 0, st, sg, N, Mtot,
@@ -1186,9 +1190,13 @@ hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, cons
   sg.Y[0] = (float*)kc; sg.ldy[0] = nhdh;
   sg.Y[1] = (float*)vv; sg.ldy[1] = nhdh;
   sg.m0[0] = 0; sg.m0[1] = nhdh; sg.m0[2] = 2 * nhdh; sg.nseg = 2;
+  // 256 x 128 tiles, a 3-stage ring (K = d_c is only 16 stages of 32: a deeper ring hides more of
+  // each tile's load latency), two workgroups per CU; bands of 4 row tiles, so that the ~64 tiles in
+  // flight per XCD share ~1 MB of [W^UK; W^UV] and ~2 MB of latent rows in its L2 instead of
+  // streaming every row tile's worth of latents from memory again
   const int Mtot = 2 * nhdh, ntn = cdiv(R, cgm::BN);
   dim3 g2((unsigned)((cdiv(Mtot, 256) * ntn + 7) & ~7), 1, 1);
-  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 2, true>), g2, dim3(256), 0, st, sg, R, ntn, d.d_c, ctx,
+  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 3, true>), g2, dim3(256), 0, st, sg, R, ntn, 4, d.d_c, ctx,
                      (int64_t)(d.d_c + d.d_r), 1, (float*)nullptr, Mtot, (int64_t)0, (int64_t)0, (int64_t)0);
   return hipGetLastError();
 }
