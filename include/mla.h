@@ -320,8 +320,8 @@ MLA_API mla_status mla_absorb_q_naive(const mla_dims* dims, int32_t B, int32_t w
 /* mla_prefill_naive_attn — causal attention of a C-token chunk per sequence over its expanded
  * context. Token t of sequence b (row b * C + t of q_c / q_pe / o, position p0[b] + t) attends to
  * cache rows 0 .. p0[b] + t, which must already hold the chunk's rows (mla_rope appends them).
- *   q_c [B * C, n_h, d_h], q_pe [B * C, n_h, d_r] (rotated) float32; o [B * C, n_h, d_h] float32
- *   (o_{t,i} of the page's section 4.4, before W^O);
+ *   q_c [B * C, n_h, d_h], q_pe [B * C, n_h, d_r] (rotated) float32; o [B * C, n_h, d_h] bfloat16
+ *   (o_{t,i} of the page's section 4.4, before W^O, rounded to nearest even);
  *   cache: the sequences' own cache (block table [B, max_pages] when paged), bfloat16 rows;
  *   p0: device int32 [B]; max_ctx (host): bound on every p0[b] + C, at most the cache capacity.
  *   Keys beyond max_ctx are not read (a caller error leaves such outputs unspecified).
@@ -331,15 +331,17 @@ MLA_API size_t mla_prefill_naive_workspace_bytes(const mla_dims* dims, int32_t B
 MLA_API mla_status mla_prefill_naive_attn(const mla_dims* dims, int32_t B, int32_t C, int32_t wdtype,
                                   const float* q_c, const float* q_pe, const mla_cache* cache,
                                   const int32_t* p0, int32_t max_ctx, const void* W_uk, const void* W_uv,
-                                  void* workspace, size_t ws_bytes, float* o, hipStream_t stream);
+                                  void* workspace, size_t ws_bytes, void* o, hipStream_t stream);
 
 /* mla_output_proj — u = W^O [o_1; ...; o_nh] ("DeepSeek-V2 from Scratch" section 1, the output
- * projection) for N rows of per-head outputs o [N, n_h * d_h] float32; u [N, d] float32. The
- * workspace (K-split partial sums) needs mla_output_proj_workspace_bytes(dims, N) bytes, which may
- * be 0 (then workspace may be NULL). */
+ * projection) for N rows of per-head outputs o [N, n_h * d_h] of type odtype (MLA_F32, or MLA_BF16
+ * as mla_prefill_naive_attn writes it); u [N, d] float32. A float32 o keeps ~16 significant bits
+ * on the MFMA path (bf16 hi + lo halves). The workspace (K-split partial sums) needs
+ * mla_output_proj_workspace_bytes(dims, N) bytes, which may be 0 (then workspace may be NULL). */
 MLA_API size_t mla_output_proj_workspace_bytes(const mla_dims* dims, int32_t N);
-MLA_API mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, const float* o,
-                           const void* W_o, void* workspace, size_t ws_bytes, float* u, hipStream_t stream);
+MLA_API mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, int32_t odtype,
+                           const void* o, const void* W_o, void* workspace, size_t ws_bytes, float* u,
+                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_cache_store — write given rows into a cache (prefix fill; not part of a decode step).

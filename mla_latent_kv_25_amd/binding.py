@@ -84,7 +84,7 @@ def lib():
         "mla_prefill_naive_workspace_bytes": (SZ, [D, I32, I32]),
         "mla_prefill_naive_attn": (I32, [D, I32, I32, I32, P, P, C, P, I32, P, P, P, SZ, P, ST]),
         "mla_output_proj_workspace_bytes": (SZ, [D, I32]),
-        "mla_output_proj": (I32, [D, I32, I32, P, P, P, SZ, P, ST]),
+        "mla_output_proj": (I32, [D, I32, I32, I32, P, P, P, SZ, P, ST]),
         "mla_status_str": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
         "mla_version": (ctypes.c_char_p, []),
@@ -313,7 +313,7 @@ def prefill_naive_attn(dims: Dims, B: int, C: int, q_c, q_pe, cache: LatentCache
                                         ctypes.byref(cc), _ptr(p0, torch.int32, "p0"), max_ctx,
                                         _ptr(W_uk, name="W_uk"), _ptr(W_uv, W_uk.dtype, "W_uv"),
                                         _ptr(workspace, name="workspace"), workspace.numel(),
-                                        _ptr(o, torch.float32, "o"), _stream()))
+                                        _ptr(o, torch.bfloat16, "o"), _stream()))
 
 
 def output_proj_workspace_bytes(dims: Dims, N: int) -> int:
@@ -321,8 +321,11 @@ def output_proj_workspace_bytes(dims: Dims, N: int) -> int:
 
 
 def output_proj(dims: Dims, o, W_o, workspace, u):
-    """u = W^O o for o [N, n_h * d_h] float32."""
-    _check(lib().mla_output_proj(ctypes.byref(dims), o.shape[0], DTYPE_CODE[W_o.dtype], _ptr(o, torch.float32, "o"),
+    """u = W^O o for o [N, n_h * d_h] float32 or bf16."""
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise MLAError("o must be float32 or bfloat16")
+    _check(lib().mla_output_proj(ctypes.byref(dims), o.shape[0], DTYPE_CODE[W_o.dtype], DTYPE_CODE[o.dtype],
+                                 _ptr(o, name="o"),
                                  _ptr(W_o, name="W_o"), _ptr(workspace, name="workspace") if workspace is not None
                                  else None, 0 if workspace is None else workspace.numel(),
                                  _ptr(u, torch.float32, "u"), _stream()))
@@ -414,7 +417,7 @@ class PrefillStep:
             self.max_ctx = max_ctx
             f32 = dict(dtype=torch.float32, device=device)
             self.q_c = torch.empty((B * C, dims.n_h, dims.d_h), **f32)
-            self.o = torch.empty((B * C, dims.n_h * dims.d_h), **f32)
+            self.o = torch.empty((B * C, dims.n_h * dims.d_h), dtype=torch.bfloat16, device=device)
             u8 = dict(dtype=torch.uint8, device=device)
             self.ws_n = torch.empty(max(1, prefill_naive_workspace_bytes(self.dims, B, max_ctx)), **u8)
             self.ws_p = torch.empty(max(1, output_proj_workspace_bytes(self.dims, B * C)), **u8)

@@ -303,7 +303,7 @@ mla_status mla_combine_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
   const mla::AbsorbOutLayout L = mla::absorb_out_layout(*dims, B);
   float* o = (float*)((char*)workspace + L.off_o);
   hipError_t e = mla::launch_combine_uv(*dims, B, G, dec_workspace, W_uv, o, lse, stream);
-  if (e == hipSuccess) e = mla::launch_output_proj(*dims, B, o, W_o, (char*)workspace + L.off_part, u, stream);
+  if (e == hipSuccess) e = mla::launch_output_proj(*dims, B, o, false, W_o, (char*)workspace + L.off_part, u, stream);
   return hip_status(e, fn);
 }
 
@@ -429,7 +429,7 @@ size_t mla_prefill_naive_workspace_bytes(const mla_dims* dims, int32_t B, int32_
 
 mla_status mla_prefill_naive_attn(const mla_dims* dims, int32_t B, int32_t C, int32_t wdtype, const float* q_c,
                                   const float* q_pe, const mla_cache* cache, const int32_t* p0, int32_t max_ctx,
-                                  const void* W_uk, const void* W_uv, void* workspace, size_t ws_bytes, float* o,
+                                  const void* W_uk, const void* W_uv, void* workspace, size_t ws_bytes, void* o,
                                   hipStream_t stream) {
   const char* fn = "mla_prefill_naive_attn";
   mla_status s = check_dims(dims, fn);
@@ -468,13 +468,14 @@ size_t mla_output_proj_workspace_bytes(const mla_dims* dims, int32_t N) {
   return mla::output_proj_layout(*dims, N).bytes;
 }
 
-mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, const float* o, const void* W_o,
-                           void* workspace, size_t ws_bytes, float* u, hipStream_t stream) {
+mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, int32_t odtype, const void* o,
+                           const void* W_o, void* workspace, size_t ws_bytes, float* u, hipStream_t stream) {
   const char* fn = "mla_output_proj";
   mla_status s = check_dims(dims, fn);
   if (s) return s;
   if (N < 0) return fail(MLA_E_ARG, "%s: N < 0", fn);
   if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
+  if (odtype != MLA_F32 && odtype != MLA_BF16) return fail(MLA_E_ARG, "%s: o must be F32 or BF16", fn);
   if (wdtype != MLA_BF16 || !mla::naive_supported(*dims))
     return fail(MLA_E_UNSUPPORTED, "%s: needs bf16 weights and the MFMA GEMM shapes", fn);
   if (N == 0) return ok();
@@ -483,7 +484,7 @@ mla_status mla_output_proj(const mla_dims* dims, int32_t N, int32_t wdtype, cons
   const size_t need = mla_output_proj_workspace_bytes(dims, N);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  return hip_status(mla::launch_output_proj(*dims, N, o, W_o, workspace, u, stream), fn);
+  return hip_status(mla::launch_output_proj(*dims, N, o, odtype == MLA_BF16, W_o, workspace, u, stream), fn);
 }
 
 mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t B, const int32_t* n_rows,

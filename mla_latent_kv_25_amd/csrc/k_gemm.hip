@@ -1206,7 +1206,7 @@ bool naive_supported(const mla_dims& d) {
   return mfma_dims_ok(d) && d.d_h == 128 && d.d_c == 512 && d.d_r == 64;
 }
 
-// u = W^O o for per-head outputs o [N, n_h d_h] (float32); the workspace holds only K-split partials
+// u = W^O o for per-head outputs o [N, n_h d_h] (float32, or bf16); the workspace holds only K-split partials
 AbsorbOutLayout output_proj_layout(const mla_dims& d, int N) {
   AbsorbOutLayout L;
   const int sk5 = o_splits(d, N).sk5;
@@ -1220,14 +1220,15 @@ AbsorbOutLayout output_proj_layout(const mla_dims& d, int N) {
   L.bytes = al256h(L.part_floats * 4);
   return L;
 }
-hipError_t launch_output_proj(const mla_dims& d, int N, const float* o, const void* W_o, void* ws, float* u,
-                              hipStream_t st) {
+hipError_t launch_output_proj(const mla_dims& d, int N, const void* o, bool o_bf16, const void* W_o, void* ws,
+                              float* u, hipStream_t st) {
   float* part = (float*)ws;
   const int nhdh = d.n_h * d.d_h;
   Seg s5{};
   s5.W[0] = W_o; s5.Y[0] = u; s5.ldy[0] = d.d;
   s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-  mfma_gemm<true>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
+  if (o_bf16) mfma_gemm<false>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
+  else mfma_gemm<true>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
   return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
                                                         const float* __restrict__ q_c, const float* __restrict__ q_pe,
                                                         const uint16_t* __restrict__ ctx, const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vv, float qscale,
-                                                        float* __restrict__ o) {
+                                                        uint16_t* __restrict__ o) {
   using namespace nv;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NSLOT * SLOT];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,16 +220,16 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
         O[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], O[vb], 0, 0, 0);
       }
   }
-  // o[b * C + t][i * 128 + 32 vb + 8 (r / 4) + 4 g + r % 4] = O / l
+  // o[b * C + t][i * 128 + 32 vb + 8 (r / 4) + 4 g + r % 4] = O / l, rounded to bf16
   if (t < C) {
     const float inv = 1.f / l_run;
-    float* dst = o + ((int64_t)b * C + t) * NHD + (int64_t)i * DH + 4 * g;
+    uint16_t* dst = o + ((int64_t)b * C + t) * NHD + (int64_t)i * DH + 4 * g;
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *(f32x4*)(dst + 32 * vb + 8 * r4) =
-            f32x4{O[vb][4 * r4], O[vb][4 * r4 + 1], O[vb][4 * r4 + 2], O[vb][4 * r4 + 3]} * inv;
+        *(u32x2*)(dst + 32 * vb + 8 * r4) = u32x2{pack_bf16x2(O[vb][4 * r4] * inv, O[vb][4 * r4 + 1] * inv),
+                                                  pack_bf16x2(O[vb][4 * r4 + 2] * inv, O[vb][4 * r4 + 3] * inv)};
   }
 }
 
@@ -253,13 +253,13 @@ hipError_t launch_gather_rows(const CacheArgs& c, int B, int C, const int32_t* p
 }
 
 hipError_t launch_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t* p0, const float* q_c,
-                              const float* q_pe, const void* ws, float qscale, float* o, hipStream_t st) {
+                              const float* q_pe, const void* ws, float qscale, void* o, hipStream_t st) {
   const NaiveLayout L = naive_layout(n_h, B, max_ctx);
   const uint16_t* ctx = (const uint16_t*)((const char*)ws + L.off_ctx);
   const uint16_t* kc = (const uint16_t*)((const char*)ws + L.off_kc);
   const uint16_t* vv = (const uint16_t*)((const char*)ws + L.off_v);
   hipLaunchKernelGGL(k_mha_prefill, dim3((unsigned)((C + nv::QB - 1) / nv::QB), n_h, B), dim3(256), 0, st, C, max_ctx,
-                     n_h, p0, q_c, q_pe, ctx, kc, vv, qscale, o);
+                     n_h, p0, q_c, q_pe, ctx, kc, vv, qscale, (uint16_t*)o);
   return hipGetLastError();
 }
 

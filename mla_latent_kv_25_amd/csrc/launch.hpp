@@ -78,15 +78,15 @@ NaiveLayout naive_layout(int n_h, int B, int max_ctx);
 hipError_t launch_gather_rows(const CacheArgs& c, int B, int C, const int32_t* p0, int max_ctx, void* ctx,
                               hipStream_t st);
 hipError_t launch_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t* p0, const float* q_c,
-                              const float* q_pe, const void* ws, float qscale, float* o, hipStream_t st);
+                              const float* q_pe, const void* ws, float qscale, void* o, hipStream_t st);
 hipError_t launch_absorb_q_naive(const mla_dims& d, int B, const void* h, const void* W_dq, const void* W_uq,
                                  const void* W_qr, const void* W_dkv, const void* W_kr, void* ws, float* q_c,
                                  float* q_pe, float* kv_new, hipStream_t st);
 hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, const void* W_uk, const void* W_uv,
                                  void* kc, void* vv, hipStream_t st);
 AbsorbOutLayout output_proj_layout(const mla_dims& d, int N);
-hipError_t launch_output_proj(const mla_dims& d, int N, const float* o, const void* W_o, void* ws, float* u,
-                              hipStream_t st);
+hipError_t launch_output_proj(const mla_dims& d, int N, const void* o, bool o_bf16, const void* W_o, void* ws,
+                              float* u, hipStream_t st);
 bool naive_supported(const mla_dims& d);
 
 // Combine fused with the W^UV product (k_decode.hip): o [B, n_h d_h] float32 from the decode

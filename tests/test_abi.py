@@ -220,11 +220,12 @@ def test_naive_prefill_validation(L):
                 None) == 0
     # output projection
     need_o = L.mla_output_proj_workspace_bytes(ctypes.byref(v2), 512)
-    assert L.mla_output_proj(ctypes.byref(v2), 512, 2, None, FAKE, FAKE, need_o, FAKE, None) == 1
+    assert L.mla_output_proj(ctypes.byref(v2), 512, 2, 2, None, FAKE, FAKE, need_o, FAKE, None) == 1
     if need_o > 0:
-        assert L.mla_output_proj(ctypes.byref(v2), 512, 2, FAKE, FAKE, FAKE, need_o - 1, FAKE, None) == 3
-    assert L.mla_output_proj(ctypes.byref(v2), 512, 0, FAKE, FAKE, FAKE, need_o, FAKE, None) == 2
-    assert L.mla_output_proj(ctypes.byref(v2), 0, 2, None, None, None, 0, None, None) == 0
+        assert L.mla_output_proj(ctypes.byref(v2), 512, 2, 2, FAKE, FAKE, FAKE, need_o - 1, FAKE, None) == 3
+    assert L.mla_output_proj(ctypes.byref(v2), 512, 0, 0, FAKE, FAKE, FAKE, need_o, FAKE, None) == 2
+    assert L.mla_output_proj(ctypes.byref(v2), 512, 2, 1, FAKE, FAKE, FAKE, need_o, FAKE, None) == 1  # f16 o
+    assert L.mla_output_proj(ctypes.byref(v2), 0, 2, 0, None, None, None, 0, None, None) == 0
 
 
 def test_combine_absorb_out_validation(L):

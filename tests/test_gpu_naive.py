@@ -57,6 +57,7 @@ def test_naive_prefill_parity(key, p0, C, stress):
                 f"naive cfg{key} b={b}")
         # per-head outputs o_{t,i} before W^O
         o_ref = np.stack([o["o"].reshape(-1) for o in outs])
+        print(f"  o rel-L2 {rel_l2(o_gpu[b], o_ref):.3e}", flush=True)
         assert rel_l2(o_gpu[b], o_ref) <= 5e-3, rel_l2(o_gpu[b], o_ref)
 
 
