@@ -441,8 +441,9 @@ mla_status mla_prefill_naive_attn(const mla_dims* dims, int32_t B, int32_t C, in
   if (C < 1) return fail(MLA_E_ARG, "%s: chunk length C must be >= 1", fn);
   if (max_ctx < C) return fail(MLA_E_ARG, "%s: max_ctx must be >= C", fn);
   if ((int64_t)max_ctx > c.t_cap) return fail(MLA_E_ARG, "%s: max_ctx exceeds the cache capacity", fn);
-  if ((int64_t)B * C > (int64_t)INT32_MAX / 2 || (int64_t)B * max_ctx > (int64_t)INT32_MAX / 2)
-    return fail(MLA_E_ARG, "%s: B * C or B * max_ctx too large", fn);
+  if ((int64_t)B * C > (int64_t)INT32_MAX / 2 || (int64_t)B * max_ctx > (int64_t)INT32_MAX / 2 ||
+      (int64_t)((C + 127) / 128) * dims->n_h * B > (int64_t)INT32_MAX - 8)
+    return fail(MLA_E_ARG, "%s: B * C, B * max_ctx or the attention grid too large", fn);
   if (!valid_wdtype(wdtype)) return fail(MLA_E_ARG, "%s: weight dtype must be F32, F16 or BF16", fn);
   if (wdtype != MLA_BF16 || c.dtype != MLA_BF16 || !mla::naive_supported(*dims))
     return fail(MLA_E_UNSUPPORTED, "%s: the naive form needs bf16 weights and cache, d_h=128, d_c=512, d_r=64", fn);

@@ -54,11 +54,34 @@ __global__ __launch_bounds__(256) void k_gather_rows(CacheArgs c, int B, int C, 
 //     scores of keys 8 (r / 4) + 4 g + r % 4, r = 0..15: values r = 0..7 and 8..15 are that lane's
 //     B operand for the two 16-key steps of the PV product (the reduction runs over the keys in
 //     that order);
-//   softmax: online, per query, in float32 (base 2); the rescale of O is skipped when no query of
-//     the wave raised its maximum;
+//   softmax: online, per query, in float32 (base 2); a lane's 16 scores reduce as a tree, the two
+//     lane halves meet through a cross-half swap (maximum per tile, sum once at the end); the
+//     rescale of O is skipped when no query of the wave raised its maximum;
 //   PV: O^T[32 value columns x 32 queries] += V^T P^T per 32 columns, V^T by transposing 16-bit
 //     reads (rows 16 kk + 4 g .. + 3 and 16 kk + 8 + 4 g .. + 3 for lane half g).
 // Causal: query t (position p0[b] + t) sees keys 0 .. p0[b] + t.
+// v of lane l and of lane l ^ 32, through v_permlane32_swap: of the two results, one holds the
+// lane's own value and the other its partner's, so a symmetric combination of both is the same in
+// the two lanes. (The results are copied out element by element: a bit_cast applied straight to
+// an element of the returned pair was compiled as if both elements were the first.)
+__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float halves_max(float v) {
+  float a, b;
+  swap_pair(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  float a, b;
+  swap_pair(v, a, b);
+  return a + b;
+}
+
 namespace nv {
 constexpr int DH = 128, DR = 64, DC = 512;  // d_h, d_r, d_c (the DeepSeek-V2 shape; any head count)
 constexpr int QB = 128;                // queries per workgroup
@@ -72,7 +95,7 @@ constexpr int NSLOT = 3;
 constexpr int NCP = 6;                 // copies per wave per tile
 }
 
-__global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int n_h, const int32_t* __restrict__ p0,
+__global__ __launch_bounds__(256, 2) void k_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t* __restrict__ p0,
                                                         const float* __restrict__ q_c, const float* __restrict__ q_pe,
                                                         const uint16_t* __restrict__ ctx, const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vv, float qscale,
@@ -81,7 +104,13 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
   __shared__ __attribute__((aligned(16))) uint8_t lds[NSLOT * SLOT];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int qb = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  // block t = (b * n_h + i) * nqb + qb: consecutive t go to one XCD (workgroups are dealt
+  // round-robin to the 8 XCDs), so the query blocks of one (sequence, head), which walk the same
+  // keys at about the same pace, and neighbouring heads, which share k^R, read them through one L2
+  const int nqb = (C + QB - 1) / QB;
+  const int tb = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  if (tb >= nqb * n_h * B) return;  // padding workgroup (uniform)
+  const int qb = tb % nqb, i = (tb / nqb) % n_h, b = tb / (nqb * n_h);
   const int NHD = n_h * DH;
   const int P0 = p0[b] > 0 ? p0[b] : 0;
   const int tq0 = QB * qb;                                    // first query of the workgroup
@@ -96,41 +125,55 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
   // column q % 25: 0..15 from k^C, 16..23 from k^R, 24 a duplicate), value chunk 800 <= q < 1376
   // (row, column of q - 800 in rows of 18: 0..15 from v, 16..17 duplicates), q >= 1376 unused
   // (a duplicate); kind 0: k^C / v of the head, 1: k^R
-  uint32_t plan[NCP];
+  // The lane's source for copy k: row rk[k] of the tile, from the key row base gb[k] (k^C or v of
+  // head i, or the shared k^R) at a row stride of gs[k] bytes; gp[k] walks it tile by tile.
+  const uint8_t* gp[NCP];
+  uint32_t gs[NCP];
+  int rk[NCP];
 #pragma unroll
   for (int k = 0; k < NCP; ++k) {
     const int q = 64 * (4 * k + w) + lane;
-    int row, src;  // src: byte offset inside the source row (bit 15 set: value rows, bit 14: k^R)
+    int row, cc;
+    const uint8_t* base;
+    uint32_t stride;
     if (q < TT * KCHP) {
       row = q / KCHP;
-      const int cc = q % KCHP;
-      src = cc < 16 ? cc * 16 : (cc < 24 ? (1 << 14) | ((cc - 16) * 16) : 0);
-    } else if (q < TT * KCHP + TT * VCHP) {
-      const int qq = q - TT * KCHP;
-      row = qq / VCHP;
-      const int cc = qq % VCHP;
-      src = (1 << 15) | ((cc < 16 ? cc : 0) * 16);
+      cc = q % KCHP;
+      if (cc < 16) {
+        base = (const uint8_t*)(kc + rowbase * NHD + (int64_t)i * DH) + cc * 16;
+        stride = (uint32_t)NHD * 2;
+      } else {
+        base = (const uint8_t*)(ctx + rowbase * 576 + DC) + (cc < 24 ? cc - 16 : 0) * 16;
+        stride = 576 * 2;
+      }
     } else {
-      row = 0;
-      src = 0;
+      const int qq = q < TT * KCHP + TT * VCHP ? q - TT * KCHP : 0;
+      row = qq / VCHP;
+      cc = qq % VCHP;
+      base = (const uint8_t*)(vv + rowbase * NHD + (int64_t)i * DH) + (cc < 16 ? cc : 0) * 16;
+      stride = (uint32_t)NHD * 2;
     }
-    plan[k] = ((uint32_t)row << 16) | (uint32_t)src;
+    rk[k] = row;
+    gs[k] = stride;
+    gp[k] = base + (int64_t)row * stride;
   }
+  // copies of tile it (issued in order it = 0, 1, 2, ...): whole tiles advance the row pointers;
+  // the last, partial tile holds its rows to the last key
   auto issue = [&](int it) __attribute__((always_inline)) {
     const int j0 = TT * it;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((it % NSLOT) * SLOT + w * 1024));
+    const bool whole = j0 + TT <= nkeys;
 #pragma unroll
     for (int k = 0; k < NCP; ++k) {
-      int j = j0 + (int)(plan[k] >> 16);
-      j = j < nkeys ? j : nkeys - 1;
-      const uint32_t src = plan[k] & 0xffffu;
-      const int64_t r = rowbase + j;
-      const uint8_t* p;
-      if (src & (1u << 15)) p = (const uint8_t*)(vv + r * NHD + (int64_t)i * DH) + (src & 0x7fffu);
-      else if (src & (1u << 14)) p = (const uint8_t*)(ctx + r * 576 + DC) + (src & 0x3fffu);
-      else p = (const uint8_t*)(kc + r * NHD + (int64_t)i * DH) + src;
+      const uint8_t* p = gp[k];
+      if (!whole) {
+        const int j = j0 + rk[k] < nkeys ? j0 + rk[k] : nkeys - 1;
+        p -= (int64_t)rk[k] * gs[k];
+        p += (int64_t)(j - j0) * gs[k];
+      }
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :: "v"(p), "s"(dst + (uint32_t)(k * 4096)) : "memory", "m0");
+      gp[k] += (int64_t)TT * gs[k];
     }
   };
 
@@ -156,6 +199,9 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
   // first query position of the wave: tiles wholly at or below it need no mask
   const int wpos0 = tq0 + 32 * w < C ? P0 + tq0 + 32 * w : -1;
 
+  // lane part of the value-row read address inside a tile slot
+  const int va_lane = VOFF + (4 * g + ((lane & 15) >> 2)) * VCHP * 16 + (16 * (n >> 4) + 4 * (lane & 3)) * 2;
+
   float m_run = -__builtin_inff(), l_run = 0.f;
   f32x16 O[4];
 #pragma unroll
@@ -180,22 +226,33 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = 8 * (r >> 2) + 4 * g + (r & 3) <= lim ? S[r] : -__builtin_inff();
     }
-    float tm = S[0];
+    // the tile's maximum per query: a tree over the lane's 16 scores, then the other lane half
+    // (lane l and l ^ 32 hold the same query) through a cross-half swap
+    float mx[8];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tm = fmaxf(tm, S[r]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    for (int r = 0; r < 8; ++r) mx[r] = fmaxf(S[r], S[r + 8]);
+#pragma unroll
+    for (int h = 4; h >= 1; h >>= 1)
+#pragma unroll
+      for (int r = 0; r < h; ++r) mx[r] = fmaxf(mx[r], mx[r + h]);
+    const float tm = halves_max(mx[0]);
     const float m_new = fmaxf(m_run, tm);
     // a query that sees no key of this tile keeps its state (and a query past the chunk sees none)
     const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    float rs = 0.f;
+    // probabilities; each lane half keeps the sum over its own 16 keys (the halves are added once,
+    // at the end: both use the same maximum, hence the same rescale factors)
+    float ev[16];
     bf16x8 pf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(S[r] - m_use);
-      rs += e;
-      pf[r >> 3][r & 7] = (__bf16)e;
+      ev[r] = __builtin_amdgcn_exp2f(S[r] - m_use);
+      pf[r >> 3][r & 7] = (__bf16)ev[r];
     }
-    rs += __shfl_xor(rs, 32, 64);
+#pragma unroll
+    for (int h = 8; h >= 1; h >>= 1)
+#pragma unroll
+      for (int r = 0; r < h; ++r) ev[r] += ev[r + h];
+    const float rs = ev[0];
     if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
@@ -204,23 +261,23 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int C, int max_ctx, int 
     }
     l_run += rs;
     m_run = m_new;
-    // PV: value rows 16 kk + 4 g + (j16 / 4) (+ 8), columns 32 vb + 16 (n / 16) + 4 (j16 % 4)
-    const int j16 = lane & 15;
-    const uint8_t* va = tile + VOFF + (4 * g + (j16 >> 2)) * VCHP * 16 + (16 * (n >> 4) + 4 * (j16 & 3)) * 2;
+    // PV: value rows 16 kk + 4 g + (j16 / 4) (+ 8), columns 32 vb + 16 (n / 16) + 4 (j16 % 4); one
+    // LDS-space base per tile, the rest constant offsets of the reads
+    const MLA_LDS uint8_t* va = (const MLA_LDS uint8_t*)lds + (it % NSLOT) * SLOT + va_lane;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
-        const uint8_t* pa = va + 16 * kk * VCHP * 16 + 64 * vb;
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)pa);
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS s16x4*)(uintptr_t)(uint32_t)(uintptr_t)(MLA_LDS void*)(pa + 8 * VCHP * 16));
+        const MLA_LDS uint8_t* pa = va + 16 * kk * VCHP * 16 + 64 * vb;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)pa);
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(pa + 8 * VCHP * 16));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, x0).x, __builtin_bit_cast(u32x2, x0).y,
                                                            __builtin_bit_cast(u32x2, x1).x, __builtin_bit_cast(u32x2, x1).y});
         O[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], O[vb], 0, 0, 0);
       }
   }
   // o[b * C + t][i * 128 + 32 vb + 8 (r / 4) + 4 g + r % 4] = O / l, rounded to bf16
+  l_run = halves_sum(l_run);
   if (t < C) {
     const float inv = 1.f / l_run;
     uint16_t* dst = o + ((int64_t)b * C + t) * NHD + (int64_t)i * DH + 4 * g;
@@ -258,7 +315,9 @@ hipError_t launch_mha_prefill(int B, int C, int max_ctx, int n_h, const int32_t*
   const uint16_t* ctx = (const uint16_t*)((const char*)ws + L.off_ctx);
   const uint16_t* kc = (const uint16_t*)((const char*)ws + L.off_kc);
   const uint16_t* vv = (const uint16_t*)((const char*)ws + L.off_v);
-  hipLaunchKernelGGL(k_mha_prefill, dim3((unsigned)((C + nv::QB - 1) / nv::QB), n_h, B), dim3(256), 0, st, C, max_ctx,
+  // one-dimensional grid of (sequence, head, query block) tiles, padded to a multiple of 8
+  const int64_t tiles = (int64_t)((C + nv::QB - 1) / nv::QB) * n_h * B;
+  hipLaunchKernelGGL(k_mha_prefill, dim3((unsigned)((tiles + 7) & ~(int64_t)7)), dim3(256), 0, st, B, C, max_ctx,
                      n_h, p0, q_c, q_pe, ctx, kc, vv, qscale, (uint16_t*)o);
   return hipGetLastError();
 }
