@@ -557,6 +557,20 @@ __global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, i
 
   // accumulator element r of lane (g, l32): column 32 WNB wn + 32 nb + l32, row 32 WMB wm + 32 mb +
   // 8 (r / 4) + 4 g + r % 4 (four consecutive rows per r / 4; segment boundaries are multiples of 4)
+  // A tile inside one segment (the usual case) looks its segment up once, with scalar values; a
+  // tile across a boundary finds each row's segment.
+  const int m_last = (m_base + BM < Mtot ? m_base + BM : Mtot) - 1;
+  const int sg_lo = seg_of(seg, m_base);
+  const bool one_seg = split_k == 1 && sg_lo == seg_of(seg, m_last);
+  auto store = [&](const f32x4& v, int n, int m, int sg) __attribute__((always_inline)) {
+    if constexpr (OB16) {
+      // bf16 output (round to nearest even): Y holds uint16 elements, ldy in elements
+      uint16_t* y = (uint16_t*)seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg]);
+      *(u32x2*)y = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+      *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg])) = v;
+    }
+  };
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb) {
     const int n = n_base + 32 * WNB * wn + 32 * nb + l32;
@@ -568,17 +582,9 @@ __global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, i
         const int m = m_base + 32 * WMB * wm + 32 * mb + 8 * r4 + 4 * g;
         if (m >= Mtot) continue;
         const f32x4 v = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
-        if (split_k > 1) {
-          *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m) = v;
-        } else if constexpr (OB16) {
-          // bf16 output (round to nearest even): Y holds uint16 elements, ldy in elements
-          const int sg = seg_of(seg, m);
-          uint16_t* y = (uint16_t*)seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg]);
-          *(u32x2*)y = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else {
-          const int sg = seg_of(seg, m);
-          *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)n * seg.ldy[sg] + (m - seg.m0[sg])) = v;
-        }
+        if (split_k > 1) *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n) * Mtot + m) = v;
+        else if (one_seg) store(v, n, m, sg_lo);
+        else store(v, n, m, seg_of(seg, m));
       }
   }
 }
