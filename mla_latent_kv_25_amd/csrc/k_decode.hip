@@ -2145,8 +2145,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // HBM) and multiplies by W^UV_i on MFMA, writing o [B, n_h d_h] float32 for the W^O product.
 //   phase 0: every wave requests its 32 rows of W^UV_i as A fragments (32 k-steps of 16, kept in
 //            registers), so the weight read overlaps the combine;
-//   phase 1: lane j of wave 0 lists the pieces of sequence j and their weights (as k_combine);
-//   phase 2: 8 threads per sequence sum the pieces' rows (piece by piece) into LDS as bf16 hi/lo;
+//   phase 1: lane j of wave 0 lists the pieces of sequence j;
+//   phase 2: 8 threads per sequence request the pieces' rows, lse and scales together, form the
+//            weights (as k_combine) and sum the rows (piece by piece) into LDS as bf16 hi/lo;
 //   phase 3: D[e][b] = sum_c W^UV_i[e][c] o_lat_i[b][c] on 32x32x16 bf16 MFMA, hi then lo part.
 namespace cuv {
 constexpr int DC = 512, DH = 128, SB = 32;   // d_c, d_h, sequences per workgroup
@@ -2163,8 +2164,6 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
   __shared__ __attribute__((aligned(16))) uint16_t hi[SB * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t lo[SB * PITCH];
   __shared__ int slots[MAXP];
-  __shared__ float wts[MAXP];   // lse of each piece, then its weight
-  __shared__ float scs[MAXP];
   __shared__ int pbeg[SB + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // tile t = head * nslices + slice; consecutive tiles (the slices of one head, sharing W^UV_i)
@@ -2182,7 +2181,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
 #pragma unroll
   for (int ks = 0; ks < DC / 16; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
 
-  // phase 1: pieces and weights per sequence (lane j of wave 0 owns sequence b0 + j)
+  // phase 1: the piece list of each sequence (lane j of wave 0 owns sequence b0 + j)
   const bool f16 = *fmt == 2;
   const int64_t total = cu[B];
   if (w == 0) {
@@ -2208,37 +2207,28 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
     if (lane < SB) pbeg[lane] = beg < MAXP ? beg : MAXP;
     if (lane == SB - 1) pbeg[SB] = incl < MAXP ? incl : MAXP;
     if (lane < SB) {
-      // one pass of loads (lse and scale of every piece), then the weights from LDS
       int k = beg;
       for (int64_t p = plo; p <= phi; ++p)
-        if (range_start(p, total, G) != range_start(p + 1, total, G) && k < MAXP) {
-          const int64_t r = (p + b) * n_h + i;
-          slots[k] = (int)(p + b);
-          wts[k] = lse_part[r];
-          scs[k] = f16 ? sc_part[r] : 1.f;
-          ++k;
-        }
-      float M = -__builtin_inff();
-      for (int q = beg; q < k; ++q) M = fmaxf(M, wts[q]);
-      float sum = 0.f;
-      for (int q = beg; q < k; ++q) sum += __expf(wts[q] - M);
-      const float inv = 1.f / sum;
-      for (int q = beg; q < k; ++q) wts[q] = __expf(wts[q] - M) * inv * scs[q];
-      if (lse_out && b < B) lse_out[(int64_t)b * n_h + i] = k > beg ? M + __logf(sum) : -__builtin_inff();
+        if (range_start(p, total, G) != range_start(p + 1, total, G) && k < MAXP) slots[k++] = (int)(p + b);
     }
   }
   __syncthreads();
 
   // phase 2: thread (j = tid / 8, u = tid % 8) sums columns 64 k + 8 u .. + 7 (k = 0..7) of
-  // sequence b0 + j's pieces; a sequence past the batch or with no pieces gives zeros
+  // sequence b0 + j's pieces with their softmax weights exp(lse - M) / sum * scale (every thread
+  // of the sequence forms them itself); a sequence past the batch or with no pieces gives zeros.
+  // Up to PF pieces (every sequence at the decode batch sizes): their rows, lse and scales are all
+  // requested at once; more pieces take a two-pass loop.
   {
+    constexpr int PF = 6;
     const int j = tid >> 3, u = tid & 7;
-    const int q0 = pbeg[j], q1 = pbeg[j + 1];
+    const int q0 = pbeg[j], np = pbeg[j + 1] - q0;
     f32x4 acc[8][2];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k][0] = acc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t pst = (int64_t)n_h * DC;
     const _Float16* ph = (const _Float16*)o_part + (int64_t)i * DC + 8 * u;
+    const float* pf32 = (const float*)o_part + (int64_t)i * DC + 8 * u;
     auto add16 = [&](float wk, const f16x8 (&x)[8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -2248,39 +2238,54 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
           acc[k][1][e] += wk * (float)x[k][4 + e];
         }
     };
-    int q = q0;
-    if (f16) {
-      // two pieces' rows requested together, then added in piece order
-      for (; q + 1 < q1; q += 2) {
-        f16x8 x0[8], x1[8];
-        const _Float16* s0p = ph + (int64_t)slots[q] * pst;
-        const _Float16* s1p = ph + (int64_t)slots[q + 1] * pst;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x0[k] = *(const f16x8*)(s0p + 64 * k);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x1[k] = *(const f16x8*)(s1p + 64 * k);
-        add16(wts[q], x0);
-        add16(wts[q + 1], x1);
-      }
-    }
-    for (; q < q1; ++q) {
-      const float wk = wts[q];
-      const int64_t base = (int64_t)slots[q] * pst + (int64_t)i * DC + 8 * u;
+    auto add_row = [&](float wk, int slot) __attribute__((always_inline)) {
       if (f16) {
         f16x8 x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = *((const f16x8*)((const _Float16*)o_part + base + 64 * k));
+        for (int k = 0; k < 8; ++k) x[k] = *(const f16x8*)(ph + (int64_t)slot * pst + 64 * k);
         add16(wk, x);
       } else {
-        const float* src = (const float*)o_part + base;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const f32x4 x0 = *(const f32x4*)(src + 64 * k), x1 = *(const f32x4*)(src + 64 * k + 4);
-          acc[k][0] += wk * x0;
-          acc[k][1] += wk * x1;
+          const float* src = pf32 + (int64_t)slot * pst + 64 * k;
+          acc[k][0] += wk * *(const f32x4*)src;
+          acc[k][1] += wk * *(const f32x4*)(src + 4);
         }
       }
+    };
+    float M = -__builtin_inff(), sum = 0.f;
+    if (f16 && np <= PF) {
+      f16x8 x[PF][8];
+      float lv[PF], sv[PF];
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        const int slot = q < np ? slots[q0 + q] : 0;
+        lv[q] = q < np ? lse_part[(int64_t)slot * n_h + i] : -__builtin_inff();
+        sv[q] = q < np ? sc_part[(int64_t)slot * n_h + i] : 0.f;
+        if (q < np) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[q][k] = *(const f16x8*)(ph + (int64_t)slot * pst + 64 * k);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < PF; ++q) M = fmaxf(M, lv[q]);
+#pragma unroll
+      for (int q = 0; q < PF; ++q)
+        if (q < np) sum += __expf(lv[q] - M);
+      const float inv = 1.f / sum;
+#pragma unroll
+      for (int q = 0; q < PF; ++q)
+        if (q < np) add16(__expf(lv[q] - M) * inv * sv[q], x[q]);
+    } else {
+      for (int q = 0; q < np; ++q) M = fmaxf(M, lse_part[(int64_t)slots[q0 + q] * n_h + i]);
+      for (int q = 0; q < np; ++q) sum += __expf(lse_part[(int64_t)slots[q0 + q] * n_h + i] - M);
+      const float inv = 1.f / sum;
+      for (int q = 0; q < np; ++q) {
+        const int64_t r = (int64_t)slots[q0 + q] * n_h + i;
+        add_row(__expf(lse_part[r] - M) * inv * (f16 ? sc_part[r] : 1.f), slots[q0 + q]);
+      }
     }
+    if (lse_out && u == 0 && b0 + j < B) lse_out[(int64_t)(b0 + j) * n_h + i] = np > 0 ? M + __logf(sum) : -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       bf16x8 bh, bl;

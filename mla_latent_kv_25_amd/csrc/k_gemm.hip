@@ -371,6 +371,9 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
   __syncthreads();  // every wave is done with the last stage
   constexpr int RB = 4 * NB * 4 * 64;  // float4 slots per region (waves x blocks x r4 x lanes)
   f32x4* red = (f32x4*)lds;
+  // a tile inside one segment looks it up once (uniform values); otherwise row by row
+  const int sg_lo = seg_of(seg, m_base);
+  const bool one_seg = sg_lo == seg_of(seg, (m_base + MT < Mtot ? m_base + MT : Mtot) - 1);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     f32x4* reg = red + (mb & 1) * RB;
@@ -397,7 +400,8 @@ __global__ __launch_bounds__(256, 1) void k_wgemm(Seg seg, int N, int ntiles, in
       if (split_k > 1) {
         *(f32x4*)(part + ((int64_t)(ky * Z + z) * N + n0 + n) * Mtot + m_base + mloc) = v;
       } else {
-        const int m = m_base + mloc, sg = seg_of(seg, m);  // segment boundaries are multiples of 4
+        const int m = m_base + mloc;
+        const int sg = one_seg ? sg_lo : seg_of(seg, m);  // segment boundaries are multiples of 4
         *(f32x4*)(seg.Y[sg] + (int64_t)z * zY + (int64_t)(n0 + n) * seg.ldy[sg] + (m - seg.m0[sg])) = v;
       }
     }
