@@ -229,7 +229,8 @@ MLA_API mla_status mla_absorb_out_noalloc(const mla_dims* dims, int32_t B, int32
  * the pieces fused into the per-head W^UV product: for each head i and sequence b the pieces'
  * partials are merged ("DeepSeek-V2 from Scratch" section 4.4, the softmax regrouped) and
  * multiplied by W^UV_i (section 5.2) without writing o_lat, then u = W^O [o_1; ...; o_nh]
- * (section 6). Same results as the two calls up to rounding.
+ * (section 6), with the per-head outputs o_i rounded to bf16 between the two products (the
+ * two-call path keeps them in float32). Same results as the two calls up to that rounding.
  *   dec_workspace: the workspace mla_decode_attn filled (same B and num_splits);
  *   workspace: mla_absorb_out_workspace_bytes(dims, B) bytes; u [B, d] float32;
  *   lse: optional [B, n_h] float32 (NULL to skip), as mla_combine writes it.

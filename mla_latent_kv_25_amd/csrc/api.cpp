@@ -301,9 +301,9 @@ mla_status mla_combine_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtyp
   const size_t need = mla_absorb_out_workspace_bytes(dims, B);
   if (!workspace || ws_bytes < need) return fail(MLA_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   const mla::AbsorbOutLayout L = mla::absorb_out_layout(*dims, B);
-  float* o = (float*)((char*)workspace + L.off_o);
+  void* o = (char*)workspace + L.off_o;  // bf16 per-head outputs
   hipError_t e = mla::launch_combine_uv(*dims, B, G, dec_workspace, W_uv, o, lse, stream);
-  if (e == hipSuccess) e = mla::launch_output_proj(*dims, B, o, false, W_o, (char*)workspace + L.off_part, u, stream);
+  if (e == hipSuccess) e = mla::launch_output_proj(*dims, B, o, true, W_o, (char*)workspace + L.off_part, u, stream);
   return hip_status(e, fn);
 }
 

@@ -2148,7 +2148,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 //   phase 1: lane j of wave 0 lists the pieces of sequence j;
 //   phase 2: 8 threads per sequence request the pieces' rows, lse and scales together, form the
 //            weights (as k_combine) and sum the rows (piece by piece) into LDS as bf16 hi/lo;
-//   phase 3: D[e][b] = sum_c W^UV_i[e][c] o_lat_i[b][c] on 32x32x16 bf16 MFMA, hi then lo part.
+//   phase 3: D[e][b] = sum_c W^UV_i[e][c] o_lat_i[b][c] on 32x32x16 bf16 MFMA, hi then lo part,
+//            written as bf16 (the W^O product then runs one MFMA per step on half the bytes).
 namespace cuv {
 constexpr int DC = 512, DH = 128, SB = 32;   // d_c, d_h, sequences per workgroup
 constexpr int PITCH = DC + 8;                // bf16 elements per o_lat row in LDS
@@ -2158,7 +2159,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
                                                        const int32_t* __restrict__ fmt,
                                                        const float* __restrict__ lse_part,
                                                        const float* __restrict__ sc_part, const void* __restrict__ o_part,
-                                                       const uint16_t* __restrict__ W_uv, float* __restrict__ o,
+                                                       const uint16_t* __restrict__ W_uv, uint16_t* __restrict__ o,
                                                        float* __restrict__ lse_out) {
   using namespace cuv;
   __shared__ __attribute__((aligned(16))) uint16_t hi[SB * PITCH];
@@ -2310,10 +2311,10 @@ __global__ __launch_bounds__(256, 1) void k_combine_uv(int n_h, int B, int G, in
   // element r of lane (g, l32): row 8 (r / 4) + 4 g + r % 4, column l32
   const int b = b0 + l32;
   if (b < B) {
-    float* dst = o + (int64_t)b * n_h * DH + (int64_t)i * DH + 32 * w + 4 * g;
+    uint16_t* dst = o + (int64_t)b * n_h * DH + (int64_t)i * DH + 32 * w + 4 * g;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      *(f32x4*)(dst + 8 * r4) = f32x4{D[4 * r4], D[4 * r4 + 1], D[4 * r4 + 2], D[4 * r4 + 3]};
+      *(u32x2*)(dst + 8 * r4) = u32x2{pack_bf16x2(D[4 * r4], D[4 * r4 + 1]), pack_bf16x2(D[4 * r4 + 2], D[4 * r4 + 3])};
   }
 }
 
@@ -2426,7 +2427,7 @@ bool combine_uv_supported(const mla_dims& d, int G) {
   return d.d_c == cuv::DC && d.d_h == cuv::DH && G + cuv::SB - 1 <= cuv::MAXP;
 }
 
-hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, const void* W_uv, float* o, float* lse,
+hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, const void* W_uv, void* o, float* lse,
                              hipStream_t st) {
   if (!combine_uv_supported(d, G)) return hipErrorNotSupported;
   DecodeLayout L = decode_layout(d, B, G);
@@ -2435,7 +2436,7 @@ hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, co
   hipLaunchKernelGGL(k_combine_uv, dim3((unsigned)((ntiles + 7) & ~7)), dim3(256), 0, st, d.n_h, B, G, ntiles,
                      (const int64_t*)(base + L.off_cu), (const int32_t*)(base + L.off_fmt),
                      (const float*)(base + L.off_lse), (const float*)(base + L.off_sc), (const void*)(base + L.off_o),
-                     (const uint16_t*)W_uv, o, lse);
+                     (const uint16_t*)W_uv, (uint16_t*)o, lse);
   return hipGetLastError();
 }
 

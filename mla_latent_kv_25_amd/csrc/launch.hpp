@@ -89,10 +89,10 @@ hipError_t launch_output_proj(const mla_dims& d, int N, const void* o, bool o_bf
                               float* u, hipStream_t st);
 bool naive_supported(const mla_dims& d);
 
-// Combine fused with the W^UV product (k_decode.hip): o [B, n_h d_h] float32 from the decode
+// Combine fused with the W^UV product (k_decode.hip): o [B, n_h d_h] bf16 from the decode
 // workspace's pieces; V2 head shape (d_c = 512, d_h = 128), bf16 W^UV.
 bool combine_uv_supported(const mla_dims& d, int G);
-hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, const void* W_uv, float* o, float* lse,
+hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, const void* W_uv, void* o, float* lse,
                              hipStream_t st);
 
 int device_cu_count();

@@ -43,8 +43,15 @@ def test_fused_combine_absorb_out(key, B, T, layout, stress, splits):
     u1 = s1.run(case.h, case.weights, c1, case.seq_lens).clone()
     u2 = s2.run(case.h, case.weights, c2, case.seq_lens).clone()
     torch.cuda.synchronize()
-    # same decode workspace contents: the two orders of the same sums agree to float32 rounding
-    assert rel_l2(u2.double().cpu().numpy(), u1.double().cpu().numpy()) < 1e-5
+    # the per-head outputs o (start of the absorb_out workspace): float32 in the two-call path,
+    # bf16 in the fused one; the same sums in another order agree to the bf16 rounding
+    nho = B * case.dims.n_h * case.dims.d_h
+    o1 = s1.ws_o[: 4 * nho].view(torch.float32).double()
+    o2 = s2.ws_o[: 2 * nho].view(torch.bfloat16).double()
+    slack = 2.0 ** -8 * o1.abs() + 1e-5 * float(o1.abs().max())
+    assert bool(((o2 - o1).abs() <= slack).all()), float(((o2 - o1).abs() - slack).max())
+    # u then differs by that rounding only
+    assert rel_l2(u2.double().cpu().numpy(), u1.double().cpu().numpy()) < 2e-3
     assert float((s1.lse - s2.lse).abs().max()) <= 1e-6
     if B <= 4:
         ref = run_oracle(case)
