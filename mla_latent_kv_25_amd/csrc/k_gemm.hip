@@ -1201,12 +1201,12 @@ hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, cons
   sg.Y[1] = (float*)vv; sg.ldy[1] = nhdh;
   sg.m0[0] = 0; sg.m0[1] = nhdh; sg.m0[2] = 2 * nhdh; sg.nseg = 2;
   // 256 x 128 tiles, a 3-stage ring (K = d_c is only 16 stages of 32: a deeper ring hides more of
-  // each tile's load latency), two workgroups per CU; bands of 4 row tiles, so that the ~64 tiles in
-  // flight per XCD share ~1 MB of [W^UK; W^UV] and ~2 MB of latent rows in its L2 instead of
+  // each tile's load latency), two workgroups per CU; bands of 8 row tiles, so that the ~64 tiles in
+  // flight per XCD share ~2 MB of [W^UK; W^UV] and ~1 MB of latent rows in its L2 instead of
   // streaming every row tile's worth of latents from memory again
   const int Mtot = 2 * nhdh, ntn = cdiv(R, cgm::BN);
   dim3 g2((unsigned)((cdiv(Mtot, 256) * ntn + 7) & ~7), 1, 1);
-  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 3, true>), g2, dim3(256), 0, st, sg, R, ntn, 4, d.d_c, ctx,
+  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 3, true>), g2, dim3(256), 0, st, sg, R, ntn, 8, d.d_c, ctx,
                      (int64_t)(d.d_c + d.d_r), 1, (float*)nullptr, Mtot, (int64_t)0, (int64_t)0, (int64_t)0);
   return hipGetLastError();
 }

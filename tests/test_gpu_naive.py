@@ -96,3 +96,25 @@ def test_naive_benchmark_shape_sampled():
     u_a = pa.run(case.h_chunk, case.weights, c_a, case.p0)
     torch.cuda.synchronize()
     assert rel_l2(u.double().cpu().numpy(), u_a.double().cpu().numpy()) < 5e-3
+
+
+def test_naive_attention_contiguous_cache_equals_paged():
+    """mla_prefill_naive_attn on a contiguous copy of the paged cache (same rows, in order) gives
+    the same per-head outputs bit for bit: the gather is the only layout-dependent step."""
+    key, p0, C = "3", [150, 20], 40
+    case = make_prefill_case(get_config(key), p0, C, device="cuda")
+    B = len(p0)
+    pf, _, cache = _run_naive(case, C)
+    o_paged = pf.o.clone()
+    ps, t_cap = cache.page_size, cache.t_cap
+    j = torch.arange(t_cap, device="cuda")
+    rows = cache.rows.view(-1, case.dims.row)
+    # unassigned pages (-1) lie past every sequence's rows, which the gather never reads: page 0 there
+    pages = [cache.block_table[b, j // ps].long().clamp_min(0) for b in range(B)]
+    contig = torch.stack([rows[pages[b] * ps + j % ps] for b in range(B)]).contiguous()
+    cc = mla.LatentCache(contig, cache.dtype, t_cap)
+    o = torch.empty_like(o_paged)
+    mla.prefill_naive_attn(pf.dims, B, C, pf.q_c, pf.step.q_pe, cc, case.p0, pf.max_ctx, case.weights["W_uk"],
+                           case.weights["W_uv"], pf.ws_n, o)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_paged)
