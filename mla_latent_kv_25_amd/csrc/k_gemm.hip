@@ -639,10 +639,16 @@ __global__ __launch_bounds__(256) void k_absorb_uk(int n_h, int d_c, int N, cons
   __shared__ __attribute__((aligned(16))) float xs[NB * 32 * XP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int i = blockIdx.y;              // head
-  const int c0 = blockIdx.x * TC;        // column tile
-  // blockIdx.z: batch rows [32 NB z, 32 NB (z + 1)) (one launch covers any N)
-  const int nz = 32 * NB * (int)blockIdx.z;
+  // tile t = (head i * batch chunks + chunk zc) * column tiles + column tile; consecutive t go to
+  // one XCD (workgroups are dealt round-robin to the 8 XCDs), so a head's column tiles and batch
+  // chunks, which share its q^C rows and W^UK tiles, read them through one L2
+  const int nct = d_c / TC, nzc = (N + 32 * NB - 1) / (32 * NB);
+  const int t = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  if (t >= nct * nzc * n_h) return;  // padding workgroup (uniform)
+  const int i = t / (nct * nzc);         // head
+  const int c0 = (t % nct) * TC;         // column tile
+  // batch rows [32 NB zc, 32 NB (zc + 1)) (one launch covers any N)
+  const int nz = 32 * NB * ((t / nct) % nzc);
   N -= nz;
   qC += (int64_t)nz * n_h * DH;
   q_lat += (int64_t)nz * n_h * d_c;
@@ -1111,8 +1117,10 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     s2.Y[1] = q_pe; s2.ldy[1] = (int64_t)d.n_h * d.d_r;
     s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
     mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0, 3);
-    // stage 3: q_lat_i = (W^UK_i)^T q^C_i, batch rows in chunks of up to 128 along grid z
-    dim3 g3(d.d_c / absq::TC, d.n_h, cdiv(B, gm::MAXB));
+    // stage 3: q_lat_i = (W^UK_i)^T q^C_i, batch rows in chunks of 32 NB (one-dimensional grid of
+    // (head, chunk, column tile) tiles, padded to a multiple of 8)
+    const int nb_uk = B <= 32 ? 1 : (B <= 64 ? 2 : (B <= 96 ? 3 : 4));
+    dim3 g3((unsigned)(((d.d_c / absq::TC) * d.n_h * cdiv(B, 32 * nb_uk) + 7) & ~7));
     const uint16_t* wuk = (const uint16_t*)W_uk;
     if (B <= 32) hipLaunchKernelGGL(k_absorb_uk<1>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
     else if (B <= 64) hipLaunchKernelGGL(k_absorb_uk<2>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);

@@ -69,3 +69,32 @@ def test_fused_without_lse():
     mla.combine_absorb_out(s.dims, 3, s.ws_d, case.weights["W_uv"], case.weights["W_o"], s.ws_o, u, None)
     torch.cuda.synchronize()
     assert torch.equal(u, u_ref)
+
+
+def test_fused_zero_length_sequences():
+    """Sequences at length 0 (outside the contract, but defined): the fused call gives them u = 0 and
+    lse = -inf, as mla_combine + mla_absorb_out do, and the others the two-call results."""
+    T = [1, 300, 1, 77, 5, 1]
+    empty = [0, 2, 5]
+    case = make_case(get_config("2", stress=True), device="cuda", B=len(T), T=T, layout="paged")
+    cache = build_cache(case)
+    s1 = mla.DecodeStep(case.dims, len(T), 7)
+    s1.run(case.h, case.weights, cache, case.seq_lens)
+    lens = case.seq_lens.clone()
+    lens[empty] = 0
+    mla.decode_attn(s1.dims, s1.q_lat, s1.q_pe, cache, lens, 7, s1.ws_d)
+    u_f = torch.full_like(s1.u, 7.0)
+    lse_f = torch.full_like(s1.lse, 7.0)
+    mla.combine_absorb_out(s1.dims, 7, s1.ws_d, case.weights["W_uv"], case.weights["W_o"], s1.ws_o, u_f, lse_f)
+    o_lat = torch.empty_like(s1.o_lat)
+    lse_u = torch.empty_like(s1.lse)
+    u_u = torch.empty_like(s1.u)
+    mla.combine(s1.dims, 7, lens, s1.ws_d, o_lat, lse_u)
+    mla.absorb_out(s1.dims, o_lat, case.weights["W_uv"], case.weights["W_o"], s1.ws_o, u_u)
+    torch.cuda.synchronize()
+    for b in range(len(T)):
+        if b in empty:
+            assert torch.all(u_f[b] == 0) and torch.all(torch.isneginf(lse_f[b])), b
+        else:
+            assert rel_l2(u_f[b].double().cpu().numpy(), u_u[b].double().cpu().numpy()) < 2e-3, b
+            assert float((lse_f[b] - lse_u[b]).abs().max()) <= 1e-6, b
