@@ -1118,14 +1118,13 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     s2.m0[0] = 0; s2.m0[1] = nhdh; s2.m0[2] = nhdh + d.n_h * d.d_r; s2.nseg = 2;
     mfma_gemm<true>(st, s2, B, d.d_cq, cq, d.d_cq, 1, nullptr, 1, 0, 0, 0, 3);
     // stage 3: q_lat_i = (W^UK_i)^T q^C_i, batch rows in chunks of 32 NB (one-dimensional grid of
-    // (head, chunk, column tile) tiles, padded to a multiple of 8)
-    const int nb_uk = B <= 32 ? 1 : (B <= 64 ? 2 : (B <= 96 ? 3 : 4));
+    // (head, chunk, column tile) tiles, padded to a multiple of 8). Chunks of at most 64 rows keep
+    // the workgroup at 69 KB of LDS, two per CU, so that one's loads overlap the other's stores.
+    const int nb_uk = B <= 32 ? 1 : 2;
     dim3 g3((unsigned)(((d.d_c / absq::TC) * d.n_h * cdiv(B, 32 * nb_uk) + 7) & ~7));
     const uint16_t* wuk = (const uint16_t*)W_uk;
     if (B <= 32) hipLaunchKernelGGL(k_absorb_uk<1>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
-    else if (B <= 64) hipLaunchKernelGGL(k_absorb_uk<2>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
-    else if (B <= 96) hipLaunchKernelGGL(k_absorb_uk<3>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
-    else hipLaunchKernelGGL(k_absorb_uk<4>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
+    else hipLaunchKernelGGL(k_absorb_uk<2>, g3, dim3(256), 0, st, d.n_h, d.d_c, B, wuk, qc, q_lat);
     return hipGetLastError();
   }
   // VALU path (any dims, float32/float16/bf16 weights); W^DQ, W^DKV and W^KR share h: one launch
