@@ -436,7 +436,7 @@ __device__ __forceinline__ void g2l16_v(const void* src, uint32_t lds_addr) {
 }
 
 template <bool XF32, int WMB, int WNB, int NS, bool OB16 = false>
-__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : 2) void k_cgemm(Seg seg, int N, int ntn, int gm, int K, const void* __restrict__ Xv,
+__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : (OB16 ? 3 : 2)) void k_cgemm(Seg seg, int N, int ntn, int gm, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part, int Mtot,
                                                   int64_t zW, int64_t zX, int64_t zY) {
   using C = CgCfg<XF32, WMB, WNB, NS>;
@@ -1207,13 +1207,13 @@ hipError_t launch_materialize_kv(const mla_dims& d, int R, const void* ctx, cons
   sg.Y[0] = (float*)kc; sg.ldy[0] = nhdh;
   sg.Y[1] = (float*)vv; sg.ldy[1] = nhdh;
   sg.m0[0] = 0; sg.m0[1] = nhdh; sg.m0[2] = 2 * nhdh; sg.nseg = 2;
-  // 256 x 128 tiles, a 3-stage ring (K = d_c is only 16 stages of 32: a deeper ring hides more of
-  // each tile's load latency), two workgroups per CU; bands of 8 row tiles, so that the ~64 tiles in
-  // flight per XCD share ~2 MB of [W^UK; W^UV] and ~1 MB of latent rows in its L2 instead of
-  // streaming every row tile's worth of latents from memory again
+  // 256 x 128 tiles, a 2-stage ring, three workgroups per CU (K = d_c is only 16 stages of 32: more
+  // workgroups in flight hide more of each tile's load latency and epilogue than a deeper ring);
+  // bands of 8 row tiles, so that the ~96 tiles in flight per XCD share [W^UK; W^UV] rows and
+  // latent rows in its L2 instead of streaming every row tile's worth of latents from memory again
   const int Mtot = 2 * nhdh, ntn = cdiv(R, cgm::BN);
   dim3 g2((unsigned)((cdiv(Mtot, 256) * ntn + 7) & ~7), 1, 1);
-  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 3, true>), g2, dim3(256), 0, st, sg, R, ntn, 8, d.d_c, ctx,
+  hipLaunchKernelGGL((k_cgemm<false, 4, 2, 2, true>), g2, dim3(256), 0, st, sg, R, ntn, 8, d.d_c, ctx,
                      (int64_t)(d.d_c + d.d_r), 1, (float*)nullptr, Mtot, (int64_t)0, (int64_t)0, (int64_t)0);
   return hipGetLastError();
 }

@@ -46,9 +46,8 @@ __global__ __launch_bounds__(256) void k_gather_rows(CacheArgs c, int B, int C, 
 // tq0 + 32 w .. + 31, two waves per SIMD (two workgroups per CU). The keys come in 32-key tiles
 // shared by the four waves through a 3-slot LDS ring (global -> LDS copies; each wave issues 6 of
 // the 24 1-KB copies of a tile, one barrier per tile). A tile holds the keys' rows
-// [k^C (128) | k^R (64)] (25 chunks per row, an odd stride, so the row reads of 16 lanes hit 16
-// distinct bank groups) and their value rows (18 chunks per row, which makes the transposing
-// reads conflict-free).
+// [k^C (128) | k^R (64)] (25 chunks per row: an odd stride spreads the row reads of consecutive
+// lanes over the banks) and their value rows (18 chunks per row, for the transposing reads).
 //   scores: S^T[32 keys x 32 queries] on MFMA 32x32x16 (key rows as A, the wave's queries as B,
 //     12 k-steps over 192 dims, the scale folded into the bf16 query); lane (g, n) gets query n's
 //     scores of keys 8 (r / 4) + 4 g + r % 4, r = 0..15: values r = 0..7 and 8..15 are that lane's
