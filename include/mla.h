@@ -203,7 +203,10 @@ MLA_API mla_status mla_combine(const mla_dims* dims, int32_t B, int32_t num_spli
  * "DeepSeek-V2 from Scratch" section 5.2 (o_i = W^UV_i sum_j a_j c_j) and sections 1/6
  * (u = W^O [o_1; ...; o_nh]), applied in that two-step order.
  *   o_lat [B, n_h, d_c] float32; W_uv, W_o in `wdtype`; u [B, d] float32.
- *   workspace: at least mla_absorb_out_workspace_bytes(dims, B) bytes. */
+ *   workspace: at least mla_absorb_out_workspace_bytes(dims, B) bytes.
+ * The per-head outputs o_i stay float32 between the two products, except for bf16 weights at
+ * B >= 256 rows (the batches of a chunked prefill), where they are rounded to bf16 so that the
+ * W^O product runs on bf16 activations. */
 MLA_API size_t mla_absorb_out_workspace_bytes(const mla_dims* dims, int32_t B);
 MLA_API mla_status mla_absorb_out(const mla_dims* dims, int32_t B, int32_t wdtype, const float* o_lat,
                           const void* W_uv, const void* W_o, void* workspace, size_t ws_bytes,

@@ -436,7 +436,7 @@ __device__ __forceinline__ void g2l16_v(const void* src, uint32_t lds_addr) {
 }
 
 template <bool XF32, int WMB, int WNB, int NS, bool OB16 = false>
-__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : (OB16 ? 3 : 2)) void k_cgemm(Seg seg, int N, int ntn, int gm, int K, const void* __restrict__ Xv,
+__global__ __launch_bounds__(256, WMB * WNB > 8 ? 1 : (OB16 && !XF32 ? 3 : 2)) void k_cgemm(Seg seg, int N, int ntn, int gm, int K, const void* __restrict__ Xv,
                                                   int64_t ldx, int split_k, float* __restrict__ part, int Mtot,
                                                   int64_t zW, int64_t zX, int64_t zY) {
   using C = CgCfg<XF32, WMB, WNB, NS>;
@@ -1092,6 +1092,18 @@ static void mfma_gemm(hipStream_t st, const Seg& sg, int N, int K, const void* X
   }
 }
 
+// A wide product (N >= cgm::MIN_N) written as bf16, without a K split (the K-split partials are
+// float32): the prefill's W^UV product, whose output feeds W^O.
+template <bool XF32>
+static void wide_gemm_bf16_out(hipStream_t st, const Seg& sg, int N, int K, const void* X, int64_t ldx, int Z,
+                               int64_t zW, int64_t zX, int64_t zY) {
+  const int Mtot = sg.m0[sg.nseg];
+  const int bm = cg_bm(Mtot), ntn = cdiv(N, cgm::BN);
+  dim3 g2((unsigned)((cdiv(Mtot, bm) * ntn + 7) & ~7), 1, Z);
+  if (bm == 128) hipLaunchKernelGGL((k_cgemm<XF32, 2, 2, 2, true>), g2, dim3(256), 0, st, sg, N, ntn, 4, K, X, ldx, 1, (float*)nullptr, Mtot, zW, zX, zY);
+  else hipLaunchKernelGGL((k_cgemm<XF32, 4, 2, 2, true>), g2, dim3(256), 0, st, sg, N, ntn, 4, K, X, ldx, 1, (float*)nullptr, Mtot, zW, zX, zY);
+}
+
 hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, const void* W_dq, const void* W_uq,
                            const void* W_qr, const void* W_uk, const void* W_dkv, const void* W_kr, void* ws,
                            float* q_lat, float* q_pe, float* kv_new, hipStream_t st) {
@@ -1144,6 +1156,20 @@ hipError_t launch_absorb_out(const mla_dims& d, int B, int wdt, const float* o_l
   float* o = (float*)((char*)ws + L.off_o);
   float* part = (float*)((char*)ws + L.off_part);
   const int nhdh = d.n_h * d.d_h;
+  if (wdt == MLA_BF16 && mfma_dims_ok(d) && B >= cgm::MIN_N) {
+    // wide batches (chunked prefill): o_i = W^UV_i o_lat_i rounded to bf16, then W^O on the bf16
+    // per-head outputs (one MFMA per step instead of the float32 hi + lo pair)
+    Seg s4{};
+    s4.W[0] = W_uv; s4.Y[0] = o; s4.ldy[0] = nhdh;
+    s4.m0[0] = 0; s4.m0[1] = d.d_h; s4.nseg = 1;
+    wide_gemm_bf16_out<true>(st, s4, B, d.d_c, o_lat, (int64_t)d.n_h * d.d_c, d.n_h, (int64_t)d.d_h * d.d_c, d.d_c,
+                             d.d_h);
+    Seg s5{};
+    s5.W[0] = W_o; s5.Y[0] = u; s5.ldy[0] = d.d;
+    s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
+    mfma_gemm<false>(st, s5, B, nhdh, o, nhdh, o_splits(d, B).sk5, part, 1, 0, 0, 0, 4);
+    return hipGetLastError();
+  }
   if (wdt == MLA_BF16 && mfma_dims_ok(d)) {
     // o_i = W^UV_i o_lat_i, batched over heads (z): rows of W^UV_i are outputs
     Seg s4{};
