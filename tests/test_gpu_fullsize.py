@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times (one range per
 compute unit), on sampled outputs the oracle can compute one by one.
 
-Every config runs its whole decode step on the GPU through the C ABI. The oracle is then run, with
+Every config runs its whole decode step on the GPU through the C ABI (config 2 also with the fused
+combine + W^UV call the bench uses). The oracle is then run, with
 explicit K/V reconstruction and every head, on sampled sequences: the first, the last and one in
 between of config 2; the shortest, the longest and ten more seeded picks of the ragged config 3;
 two whole 131,072-token sequences of config 4 (bf16, fp8 and fp6 caches). Each sampled sequence is
@@ -51,6 +52,25 @@ def test_fullsize_config2(stress):
         ref = _oracle(case, b)
         check_u(step.u[b].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg2 b={b}")
         _check_heads(step, case, b, {"o_lat": ref["o_lat"], "lse": ref["lse"]}, list(range(case.dims.n_h)), "cfg2")
+
+
+@pytest.mark.parametrize("stress", [False, True], ids=["plain", "stress"])
+def test_fullsize_config2_fused(stress):
+    """The bench's own step at config 2 (mla_combine_absorb_out in place of the last two calls): u
+    of three sampled sequences against the oracle, and every sequence's u and lse against the
+    two-call step on the same decode workspace contents."""
+    import mla_latent_kv_25_amd as mla
+    from gpu_helpers import build_cache
+    case = make_case(get_config("2", stress=stress), device="cuda")
+    step, cache = run_gpu(case, 0)
+    fused = mla.DecodeStep(case.dims, case.B, 0, fused=True)
+    fused.run(case.h, case.weights, build_cache(case), case.seq_lens)
+    torch.cuda.synchronize()
+    assert rel_l2(fused.u.double().cpu().numpy(), step.u.double().cpu().numpy()) < 2e-3
+    assert float((fused.lse - step.lse).abs().max()) <= 1e-5
+    for b in (0, 37, case.B - 1):
+        ref = _oracle(case, b)
+        check_u(fused.u[b].double().cpu().numpy(), ref["u"], case.cfg.cdtype, f"cfg2 fused b={b}")
 
 
 def test_fullsize_config1():
