@@ -41,7 +41,8 @@ static int cdiv(int a, int b) { return (a + b - 1) / b; }
 static int col_tiles(int N) { return cdiv(N, gm::MAXB); }
 struct QSplits { int sk1; };
 static QSplits q_splits(const mla_dims& d, int B) {
-  return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, gm::MT) * col_tiles(B), d.d / gm::KC, 1)};
+  // the first projection runs on 64-row tiles (more workgroups, so a smaller K split)
+  return {split_for(cdiv(d.d_cq + d.d_c + d.d_r, 64) * col_tiles(B), d.d / gm::KC, 1)};
 }
 struct OSplits { int sk4, sk5; };
 // W^O runs on 256-row tiles when the batch is at most 64 rows
@@ -1121,7 +1122,7 @@ hipError_t launch_absorb_q(const mla_dims& d, int B, int wdt, const void* h, con
     s1.Y[1] = kv_new; s1.ldy[1] = rw;
     s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
     s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
-    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0, 2);
     // stage 2: [q^C | q^R raw] = [W^UQ; W^QR] c^Q
     Seg s2{};
     s2.W[0] = W_uq; s2.W[1] = W_qr;
@@ -1213,7 +1214,7 @@ hipError_t launch_absorb_q_naive(const mla_dims& d, int B, const void* h, const 
   s1.Y[1] = kv_new; s1.ldy[1] = rw;
   s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
   s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
-  mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+  mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0, 2);
   Seg s2{};
   s2.W[0] = W_uq; s2.W[1] = W_qr;
   s2.Y[0] = q_c; s2.ldy[0] = nhdh;
@@ -1381,7 +1382,7 @@ hipError_t launch_absorb_q_pre(const mla_dims& d, int B, int wdt, const void* h,
     s1.Y[1] = kv_new; s1.ldy[1] = rw;
     s1.Y[2] = kv_new + d.d_c; s1.ldy[2] = rw;
     s1.m0[0] = 0; s1.m0[1] = d.d_cq; s1.m0[2] = d.d_cq + d.d_c; s1.m0[3] = d.d_cq + rw; s1.nseg = 3;
-    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0);
+    mfma_gemm<false>(st, s1, B, d.d, h, d.d, q_splits(d, B).sk1, part, 1, 0, 0, 0, 2);
     // stage 2: [q~ | q^R raw] = [W~^Q; W^QR] c^Q, one product
     Seg s2{};
     s2.W[0] = Wq_pre; s2.W[1] = W_qr;
