@@ -1271,7 +1271,11 @@ hipError_t launch_output_proj(const mla_dims& d, int N, const void* o, bool o_bf
   Seg s5{};
   s5.W[0] = W_o; s5.Y[0] = u; s5.ldy[0] = d.d;
   s5.m0[0] = 0; s5.m0[1] = d.d; s5.nseg = 1;
-  if (o_bf16) mfma_gemm<false>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
+  // bf16 o: 128-row tiles (a 6-stage ring at this stage size) and the K split that fills the chip
+  // with them (at most o_splits' split, which sizes the partial area)
+  if (o_bf16)
+    mfma_gemm<false>(st, s5, N, nhdh, o, nhdh, split_for(cdiv(d.d, gm::MT) * col_tiles(N), nhdh / gm::KC, 1), part,
+                     1, 0, 0, 0, 4);
   else mfma_gemm<true>(st, s5, N, nhdh, o, nhdh, o_splits(d, N).sk5, part, 1, 0, 0, 0, o_wide(N) ? 8 : 4);
   return hipGetLastError();
 }
