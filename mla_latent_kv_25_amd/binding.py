@@ -393,25 +393,48 @@ class PrecombinedStep(DecodeStep):
         return self.u
 
 
+# Chunk length from which the naive form is the faster one (measured crossover at the DeepSeek-V2
+# shape, 16 sequences of 2048 stored rows, bf16: between C = 128 and C = 256)
+NAIVE_MIN_CHUNK = 160
+
+
+def naive_form_available(dims, weight_dtype, cache_dtype: str) -> bool:
+    """Whether the naive-form calls have kernels for these dims and types (mla_absorb_q_naive,
+    mla_prefill_naive_attn, mla_output_proj): d_h 128, d_c 512, d_r 64, the MFMA GEMM shapes
+    (d and d_cq multiples of 256, n_h d_h a multiple of 256), bf16 weights and a bf16 cache."""
+    return (dims.d_h == 128 and dims.d_c == 512 and dims.d_r == 64 and dims.d % 256 == 0 and dims.d_cq % 256 == 0
+            and (dims.n_h * dims.d_h) % 256 == 0 and weight_dtype == torch.bfloat16 and cache_dtype == "bf16")
+
+
+def choose_prefill_form(dims, C: int, weight_dtype, cache_dtype: str) -> bool:
+    """True for the naive form: from NAIVE_MIN_CHUNK chunk tokens on, where it has kernels."""
+    return C >= NAIVE_MIN_CHUNK and naive_form_available(dims, weight_dtype, cache_dtype)
+
+
 class PrefillStep:
     """Chunked prefill: C new tokens per sequence (positions p0[b] .. p0[b] + C - 1) as B * C causal
     pseudo-sequences sharing their sequence's pages (mla_prefill_tables). Every chunk token's row is
     appended, and each token gets its causal output u.
       absorbed form (naive=False): the five decode calls over the pseudo-sequences;
       naive form (naive=True): absorb_q_naive -> rope -> prefill_naive_attn -> output_proj, with
-      keys and values expanded for contexts of up to max_ctx rows (p0[b] + C <= max_ctx)."""
+      keys and values expanded for contexts of up to max_ctx rows (p0[b] + C <= max_ctx);
+      naive="auto": the naive form from NAIVE_MIN_CHUNK tokens on where it has kernels (weight and
+      cache types given as weight_dtype / cache_dtype), the absorbed form otherwise."""
 
     def __init__(self, dims, B: int, C: int, max_pages: int, num_splits: int = 0, device="cuda",
-                 sm_scale: float = 0.0, naive: bool = False, max_ctx: Optional[int] = None):
+                 sm_scale: float = 0.0, naive=False, max_ctx: Optional[int] = None,
+                 weight_dtype=torch.bfloat16, cache_dtype: str = "bf16"):
         self.B, self.C = B, C
-        self.naive = naive
+        if naive == "auto":
+            naive = max_ctx is not None and choose_prefill_form(dims, C, weight_dtype, cache_dtype)
+        self.naive = bool(naive)
         # separate combine and absorb_out: at B * C pseudo-sequences the fused call re-reads W^UV_i
         # per 32 of them and is no faster (C = 64: 571 against 560 us)
         self.step = DecodeStep(dims, B * C, num_splits, device, sm_scale)
         self.dims = self.step.dims
         self.seq_lens = torch.empty(B * C, dtype=torch.int32, device=device)
         self.block_table = torch.empty((B * C, max_pages), dtype=torch.int32, device=device)
-        if naive:
+        if self.naive:
             if max_ctx is None:
                 raise MLAError("the naive form needs max_ctx (bound on p0[b] + C)")
             self.max_ctx = max_ctx
