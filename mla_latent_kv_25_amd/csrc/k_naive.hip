@@ -219,6 +219,14 @@ __global__ __launch_bounds__(256, 2) void k_mha_prefill(int B, int C, int max_ct
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks)
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + 32 * ks), qf[ks], S, 0, 0, 0);
+    // key fragments requested four ahead of their MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // causal mask (tiles that reach past the wave's first query position)
     if (j0 + TT - 1 > wpos0) {
       const int lim = tpos - j0;
