@@ -146,38 +146,49 @@ def _blas_name():
 
 
 def decode_subrecord(mla, key, splits):
-    """decode_attn (and combine) of another DeepSeek-V2 workload, event-timed on its launch stream:
-    the latent-cache bytes over the decode_attn call as a fraction of the HBM peak."""
+    """Another DeepSeek-V2 workload, timed the way the main line is: whole decode steps (absorb_q,
+    rope, decode_attn, then the fused combine + output call) with HIP events around each call on its
+    launch stream. Reports the step and the decode_attn call; the latent-cache bytes over the
+    decode_attn call as a fraction of the HBM peak."""
     import numpy as np
     import torch
     from synth import get_config, make_case
     cfg = get_config(key)
     case = make_case(cfg, device="cuda")
+    # two copies (cycled) unless one alone outgrows the 256 MB MALL many times over (config 3: 2.5 GB)
     caches = [build_cache(mla, case) for _ in range(1 if key == "3" else 2)]
-    step = mla.DecodeStep(cfg.dims, case.B, splits)
-    d = step.dims
-    mla.absorb_q(d, case.h, case.weights, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
-    for c in caches:  # append the current rows (rotating copies, so q_pe itself is rotated once)
-        mla.rope(d, case.seq_lens, step.q_pe.clone(), step.kv_new.clone(), c)
-    mla.rope(d, case.seq_lens, step.q_pe, step.kv_new, None)
-    sigma_T = int(case.seq_lens.sum())
+    step = mla.DecodeStep(cfg.dims, case.B, splits, fused="auto")
+    d, W, h, seq_lens = step.dims, case.weights, case.h, case.seq_lens
+    sigma_T = int(seq_lens.sum())
     row_bytes = mla.row_bytes(cfg.cdtype, cfg.dims.row) + (4 if cfg.cdtype in ("fp8_e4m3", "fp6_e2m3") else 0)
-    n = 10
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n + 3)]
-    for i, e in enumerate(evs):
-        c = caches[i % len(caches)]
+
+    def one(c, e):
         e[0].record()
-        mla.decode_attn(d, step.q_lat, step.q_pe, c, case.seq_lens, splits, step.ws_d)
+        mla.absorb_q(d, h, W, step.ws_q, step.q_lat, step.q_pe, step.kv_new)
+        mla.rope(d, seq_lens, step.q_pe, step.kv_new, c)
         e[1].record()
-        mla.combine(d, splits, case.seq_lens, step.ws_d, step.o_lat, step.lse)
+        mla.decode_attn(d, step.q_lat, step.q_pe, c, seq_lens, splits, step.ws_d)
         e[2].record()
+        if step.fused:
+            mla.combine_absorb_out(d, splits, step.ws_d, W["W_uv"], W["W_o"], step.ws_o, step.u, step.lse)
+        else:
+            mla.combine(d, splits, seq_lens, step.ws_d, step.o_lat, step.lse)
+            mla.absorb_out(d, step.o_lat, W["W_uv"], W["W_o"], step.ws_o, step.u)
+        e[3].record()
+
+    warm, n = 20, 20
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(warm + n)]
+    for i, e in enumerate(evs):
+        one(caches[i % len(caches)], e)
     torch.cuda.synchronize()
-    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[3:]])) * 1e-3
-    t_comb = float(np.mean([e[1].elapsed_time(e[2]) for e in evs[3:]])) * 1e-3
+    t = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs[warm:]])) * 1e-3 for k in range(3)]
+    t_step = float(np.mean([e[0].elapsed_time(e[3]) for e in evs[warm:]])) * 1e-3
     cache_bytes = sigma_T * row_bytes
     out = {"workload": f"config {cfg.key}: {cfg.title}", "sum_context_tokens": sigma_T,
-           "decode_attn_us": t_dec * 1e6, "combine_us": t_comb * 1e6,
-           "achieved_gbps": cache_bytes / t_dec / 1e9, "frac": cache_bytes / t_dec / 1e9 / HBM_PEAK_GBPS,
+           "step_us": t_step * 1e6, "tokens_per_s": case.B / t_step,
+           "absorb_q_rope_us": t[0] * 1e6, "decode_attn_us": t[1] * 1e6, "combine_absorb_out_us": t[2] * 1e6,
+           "output_call": "mla_combine_absorb_out" if step.fused else "mla_combine + mla_absorb_out",
+           "achieved_gbps": cache_bytes / t[1] / 1e9, "frac": cache_bytes / t[1] / 1e9 / HBM_PEAK_GBPS,
            "traffic": DECODE_TRAFFIC_BYTES.get(key), "bytes_per_launch": cache_bytes,
            "per_unit": f"{row_bytes} B per cached token x {sigma_T} tokens"}
     del caches, case, step
@@ -322,7 +333,7 @@ def main():
     caches = [build_cache(mla, case) for _ in range(max(1, args.rotate))]
     # the fused combine + W^UV call where it has kernels (DeepSeek-V2 head shape, bf16 weights)
     fused = (not args.unfused and not args.precombined and dims.d_h == 128 and dims.d_c == 512 and dims.d_r == 64
-             and case.weights["W_uv"].dtype == torch.bfloat16)
+             and case.weights["W_uv"].dtype == torch.bfloat16 and mla.fused_output_suits(B, args.splits))
     if args.precombined:
         step = mla.PrecombinedStep(dims, B, args.splits, case.weights)
     else:

@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     absorb_q, absorb_q_pre, absorb_q_workspace_bytes, cache_store, combine, decode_attn, decode_workspace_bytes, lib,
     precombine, prefill_tables, rope, row_bytes,
     absorb_q_naive, output_proj, output_proj_workspace_bytes, prefill_naive_attn, prefill_naive_workspace_bytes,
-    NAIVE_MIN_CHUNK, choose_prefill_form, naive_form_available,
+    NAIVE_MIN_CHUNK, choose_prefill_form, naive_form_available, fused_output_suits,
     version,
 )

@@ -336,16 +336,27 @@ def version() -> str:
 
 
 # ------------------------------------------------------------------------------------------------
+def fused_output_suits(B: int, num_splits: int, device="cuda") -> bool:
+    """Whether mla_combine_absorb_out is the faster output call for B sequences over num_splits
+    ranges (0: the library's default of one range per CU at the DeepSeek-V2 shape). Its workgroups
+    (one head, 32 sequences) fetch up to six pieces of a sequence in one round trip and walk longer
+    piece lists one piece at a time; with more than about four ranges per sequence (long contexts
+    over a few sequences) mla_combine + mla_absorb_out are faster (B = 4 x 131072 tokens: 61 against
+    123 us)."""
+    G = num_splits or torch.cuda.get_device_properties(device).multi_processor_count
+    return G <= 4 * B
+
+
 class DecodeStep:
     """Buffers for the five calls of one decode step, allocated once (torch), reused per step.
     fused=True runs combine and absorb_out as the one call mla_combine_absorb_out (bf16 weights; other
-    weight types take the two calls)."""
+    weight types take the two calls); fused="auto" does so where fused_output_suits says it is faster."""
 
-    def __init__(self, dims, B: int, num_splits: int, device="cuda", sm_scale: float = 0.0, fused: bool = False):
+    def __init__(self, dims, B: int, num_splits: int, device="cuda", sm_scale: float = 0.0, fused=False):
         self.dims = Dims.of(dims, sm_scale)
         self.B = B
         self.num_splits = num_splits
-        self.fused = fused
+        self.fused = fused_output_suits(B, num_splits, device) if fused == "auto" else bool(fused)
         f32 = dict(dtype=torch.float32, device=device)
         self.q_lat = torch.empty((B, dims.n_h, dims.d_c), **f32)
         self.q_pe = torch.empty((B, dims.n_h, dims.d_r), **f32)

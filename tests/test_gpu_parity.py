@@ -465,3 +465,17 @@ def test_page_sizes(key, ps):
     ref = run_oracle(case)
     u_ref = np.stack([ref[b]["u"] for b in range(3)])
     check_u(step.u.double().cpu().numpy(), u_ref, case.cfg.cdtype, f"paged ps={ps} cfg{key}")
+
+
+@pytest.mark.parametrize("key", ["2", "4f8", "4f6", "1"])
+def test_paged_long_ranges(key):
+    """Ranges that span more than 64 pages: with 32-token pages and two ranges over the 6800 tokens, each
+    range covers about 106 pages, whose ids the kernels look up tile by tile as the range crosses
+    page after page."""
+    cfg = get_config(key, stress=True).with_(page_size=32)
+    case = make_case(cfg, device="cuda", B=2, T=[4500, 2300], layout="paged")
+    print(f"case cfg={key} page_size=32 B=2 T=[4500, 2300] splits=2", flush=True)
+    step, _ = run_gpu(case, 2)
+    ref = run_oracle(case)
+    u_ref = np.stack([ref[b]["u"] for b in range(2)])
+    check_u(step.u.double().cpu().numpy(), u_ref, case.cfg.cdtype, f"paged long range cfg{key}")
