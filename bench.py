@@ -77,6 +77,26 @@ def copy_calibration():
                                            "launches": 5}}), flush=True)
 
 
+def stream_read_ceiling(mla, nbytes=1 << 30, reps=10):
+    """HBM read ceiling measured on this GPU: mla_stream_read (a plain read-only streaming kernel)
+    over a buffer four times the last-level cache, timed with HIP events on its launch stream."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(mla.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        mla.stream_read(src, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mla.stream_read(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src
+    torch.cuda.empty_cache()
+    return nbytes / t / 1e9
+
+
 def build_cache(mla, case):
     import torch
     cfg, dims = case.cfg, case.dims
@@ -468,12 +488,17 @@ def main():
                      "per_unit": f"{row_bytes} B per cached token x {sigma_T} tokens"},
         "wall_s": wall,
     }
+    ceiling = stream_read_ceiling(mla)
+    out["stream_read_ceiling_gbps"] = ceiling
+    out["latent_cache_pct_stream_ceiling"] = 100.0 * out["latent_cache_gbps"] / ceiling
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     if cfg.key == "2" and not args.no_other_workloads and not args.precombined:
         del caches
         torch.cuda.empty_cache()
         out["other_workloads"] = {k: decode_subrecord(mla, k, args.splits) for k in ("3", "4", "4f8", "4f6")}
+        for rec in out["other_workloads"].values():
+            rec["pct_stream_ceiling"] = 100.0 * rec["achieved_gbps"] / ceiling
     print(json.dumps(out), flush=True)
 
 

@@ -357,6 +357,19 @@ MLA_API mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache,
                            const int32_t* n_rows, int32_t max_rows, const float* src,
                            int64_t src_stride, hipStream_t stream);
 
+/*
+ * mla_stream_read — measurement helper, not a step of the path: a plain read-only streaming
+ * kernel over `bytes` bytes at `src`, the HBM read ceiling that the latent-cache read of
+ * mla_decode_attn is reported against. Every 16-byte word is loaded once and
+ * folded into an XOR; word k of sink (k < the launch's workgroup count, at most
+ * MLA_STREAM_SINK_WORDS) receives the XOR of the 32-bit words its workgroup read, so the XOR of
+ * all sink words written equals the XOR of every 32-bit word of the buffer.
+ * src: device, 16-byte aligned, bytes a multiple of 16 (> 0). sink: device uint32
+ * [MLA_STREAM_SINK_WORDS], zero it first when comparing the XOR. Returns MLA_E_ARG otherwise.
+ */
+#define MLA_STREAM_SINK_WORDS 4096
+MLA_API mla_status mla_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Status text, and the last error message of the calling thread ("" if none). */
 MLA_API const char* mla_status_str(mla_status s);
 MLA_API const char* mla_last_error(void);

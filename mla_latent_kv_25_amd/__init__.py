@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     precombine, prefill_tables, rope, row_bytes,
     absorb_q_naive, output_proj, output_proj_workspace_bytes, prefill_naive_attn, prefill_naive_workspace_bytes,
     NAIVE_MIN_CHUNK, choose_prefill_form, naive_form_available, fused_output_suits,
-    version,
+    stream_read, STREAM_SINK_WORDS, version,
 )

@@ -85,6 +85,7 @@ def lib():
         "mla_prefill_naive_attn": (I32, [D, I32, I32, I32, P, P, C, P, I32, P, P, P, SZ, P, ST]),
         "mla_output_proj_workspace_bytes": (SZ, [D, I32]),
         "mla_output_proj": (I32, [D, I32, I32, I32, P, P, P, SZ, P, ST]),
+        "mla_stream_read": (I32, [P, SZ, P, ST]),
         "mla_status_str": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
         "mla_version": (ctypes.c_char_p, []),
@@ -102,7 +103,7 @@ EXPORTS = ("mla_absorb_q_workspace_bytes", "mla_absorb_q", "mla_rope", "mla_deco
            "mla_absorb_out_noalloc",
            "mla_prefill_tables", "mla_precombine", "mla_absorb_q_pre", "mla_absorb_out_pre_workspace_bytes",
            "mla_absorb_out_pre", "mla_cache_store", "mla_combine_absorb_out", "mla_absorb_q_naive", "mla_prefill_naive_workspace_bytes",
-           "mla_prefill_naive_attn", "mla_output_proj_workspace_bytes", "mla_output_proj",
+           "mla_prefill_naive_attn", "mla_output_proj_workspace_bytes", "mla_output_proj", "mla_stream_read",
            "mla_status_str", "mla_last_error", "mla_version")
 
 
@@ -329,6 +330,18 @@ def output_proj(dims: Dims, o, W_o, workspace, u):
                                  _ptr(W_o, name="W_o"), _ptr(workspace, name="workspace") if workspace is not None
                                  else None, 0 if workspace is None else workspace.numel(),
                                  _ptr(u, torch.float32, "u"), _stream()))
+
+
+STREAM_SINK_WORDS = 4096  # MLA_STREAM_SINK_WORDS
+
+
+def stream_read(src, sink):
+    """mla_stream_read: read every byte of the device tensor `src` once (the read-stream ceiling
+    measurement); `sink` is a device int32/uint32 tensor of STREAM_SINK_WORDS words."""
+    if sink.numel() < STREAM_SINK_WORDS or sink.element_size() != 4:
+        raise MLAError(f"sink must hold {STREAM_SINK_WORDS} 32-bit words")
+    _check(lib().mla_stream_read(_ptr(src, None, "src"), src.numel() * src.element_size(),
+                                 _ptr(sink, None, "sink"), _stream()))
 
 
 def version() -> str:

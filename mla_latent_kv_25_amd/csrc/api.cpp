@@ -505,4 +505,12 @@ mla_status mla_cache_store(const mla_dims* dims, const mla_cache* cache, int32_t
   return hip_status(mla::launch_cache_store(*dims, c, B, n_rows, max_rows, src, src_stride, stream), fn);
 }
 
+mla_status mla_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  const char* fn = "mla_stream_read";
+  if (!src || !sink) return fail(MLA_E_ARG, "%s: NULL pointer", fn);
+  if (bytes == 0 || bytes % 16) return fail(MLA_E_ARG, "%s: bytes must be a positive multiple of 16", fn);
+  if (misaligned(src) || misaligned4(sink)) return fail(MLA_E_ARG, "%s: src must be 16-byte aligned, sink 4-byte", fn);
+  return hip_status(mla::launch_stream_read(src, bytes, sink, stream), fn);
+}
+
 }  // extern "C"

@@ -97,4 +97,7 @@ hipError_t launch_combine_uv(const mla_dims& d, int B, int G, const void* ws, co
 
 int device_cu_count();
 
+// Read-only streaming ceiling (k_stream.hip).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+
 }  // namespace mla

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
     from mla_latent_kv_25_amd.binding import EXPORTS
@@ -259,3 +259,13 @@ def test_alignment_validation(L):
     need = L.mla_absorb_out_workspace_bytes(ctypes.byref(d), 2)
     assert L.mla_absorb_out(ctypes.byref(d), 2, 0, FAKE, FAKE, FAKE, odd, need, FAKE, None) == 1
     assert b"aligned" in L.mla_last_error()
+
+
+def test_stream_read_validation(L):
+    sink = ctypes.c_void_p(0x2000)
+    assert L.mla_stream_read(None, 16, sink, None) == 1
+    assert L.mla_stream_read(FAKE, 0, sink, None) == 1
+    assert L.mla_stream_read(FAKE, 24, sink, None) == 1
+    assert b"multiple of 16" in L.mla_last_error()
+    assert L.mla_stream_read(ctypes.c_void_p(0x1008), 32, sink, None) == 1
+    assert L.mla_stream_read(FAKE, 32, None, None) == 1
