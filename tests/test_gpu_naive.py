@@ -3,7 +3,7 @@ keys and values expanded per head from the latent rows, attention per head on th
 oracle's chunk prefill, and against the absorbed form on the same inputs.
 
 Cases: DeepSeek-V2 shape, bf16 weights and paged bf16 cache; empty, ragged and page-crossing
-prefixes; chunks of 1 to 130 tokens (one and two 64-query blocks per workgroup, ragged tails).
+prefixes; chunks of 1 to 260 tokens (one to three 128-query blocks per (sequence, head), ragged tails).
 """
 import numpy as np
 import pytest
@@ -27,6 +27,8 @@ CASES = [
     ("3", [70, 129], 65, False),
     ("3", [0], 1, False),
     ("2", [5], 130, True),
+    # three 128-query blocks, the last one ragged (4 queries)
+    ("2", [3, 40], 260, False),
 ]
 
 
