@@ -329,8 +329,9 @@ def prefill_bench(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "single-GPU build: this benchmark measures one GPU; see the design notes "
-                                   "for how the path shards across GPUs"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; across GPUs the path would shard "
+                                   "decode over sequences and token ranges (one log-sum-exp all-gather per "
+                                   "sequence before the combine), which is not built"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

@@ -9,8 +9,7 @@ attention with the decoupled rotary part, exactly as the pages write the method 
   [Visual]  = "DeepSeek-V2" (sghael visual-learn), "Why position needs separate handling";
   [Summary] = noblerworks summary of the DeepSeek-V2 paper, "The matrix-absorption trick".
 
-Where the pages are silent the oracle takes these readings (each is listed with its reason in
-the design notes of the repository):
+Where the pages are silent the oracle takes these readings:
   * rotary embedding: consecutive pairs (x_2m, x_2m+1) rotated by pos * base^(-2m/d_r), base
     10000; applied to every head's d_h^R slice of the rotary query and to the shared rotary key;
   * positions are 0-based, cache row j holds position j, the current token sits at T_b - 1 and

@@ -379,14 +379,14 @@ def test_appended_row_storage():
 
 
 def spike_budget(case, ref, mult, rel=2.0 ** -7):
-    """Error budget of the late-spike case (reading R10 of the design notes), from the oracle's own
+    """Error budget of the late-spike case, from the oracle's own
     query and stored rows. The V2-shape MFMA kernels hold the query as bf16 (or as two e4m3 parts
     with the same 8 significant bits) and the probabilities as bf16: each is rounded with a relative
     error of at most 2^-8, so
       score s_ij:  |ds_ij| <= 2^-8 * scale * sum_k |q_ik c_jk|, and lse_i moves by at most max_j |ds_ij|;
       u:           one dominating row carries its rounded weight into every output, |du| <= 2^-8 |u|,
                    plus 2^-11 for the float16 partial rows.
-    The bars are the benchmark spec's absolute ones plus twice these terms (rel = 2^-7), and they grow with
+    The bars are the absolute bf16 bars (max-abs 2e-2) plus twice these terms (rel = 2^-7), and they grow with
     the spike: 8x more from x8 to x64. The few-head kernel over an fp16 cache rounds the query and
     the probabilities to fp16 (unit roundoff 2^-11): rel = 2^-10."""
     import numpy as np
