@@ -28,9 +28,9 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # profiles/decode_attn_config2_hbm_counters.md and profiles/decode_attn_config4_hbm_counters.md for
 # the kernels as they stand. Workloads without a recorded measurement report null.
 DECODE_TRAFFIC_BYTES = {
-    "2": 153658 * 1024 * 2 + 38145 * 1024,
-    "4": 297084 * 1024 * 2 + 38144 * 1024,
-    "4f8": 151014 * 1024 * 2 + 37120 * 1024,
+    "2": 153666 * 1024 * 2 + 38145 * 1024,
+    "4": 297090 * 1024 * 2 + 38144 * 1024,
+    "4f8": 150874 * 1024 * 2 + 36864 * 1024,
 }
 
 

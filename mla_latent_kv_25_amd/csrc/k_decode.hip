@@ -467,14 +467,13 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const uint8_t* __restrict_
         for (int par = 0; par < 2; ++par) vq[kk][ab][par] = t * ROWB + sub + (((4 * par + cst) ^ key) << 4);
       }
   }
-  uint32_t doff2[(LOADS + 1) / 2];
-#pragma unroll
-  for (int i = 0; i < (LOADS + 1) / 2; ++i) doff2[i] = 0;
+  // byte offset of the lane's i-th 16-byte chunk in a tile, one register each: unpacking two
+  // 16-bit offsets per register cost two VALU instructions per copy inside the score chain
+  uint32_t doff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int f = i * 256 + tid, t = f / CHUNKS;
-    const uint32_t o = (uint32_t)(t * ROWB + (swz(t, f - t * CHUNKS) << 4));
-    doff2[i >> 1] |= o << (16 * (i & 1));
+    doff[i] = (uint32_t)(t * ROWB + (swz(t, f - t * CHUNKS) << 4));
   }
 
   while (start < end) {
@@ -524,9 +523,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_v3(const uint8_t* __restrict_
     // `partial`: the tile may end before its 32nd row (only a segment's last tile does); callers
     // pass a constant so that full tiles carry no branch
     auto copy = [&](const CopyPlan& cp, int i, bool partial) __attribute__((always_inline)) {
-      uint32_t d2 = doff2[i >> 1];
-      asm volatile("" : "+v"(d2));
-      uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
+      uint32_t off = doff[i];
       if (partial && cp.last < TT - 1) {
         const int t = (int)(off / ROWB);
         if (t > cp.last) off -= (uint32_t)(t - cp.last) * ROWB;
@@ -982,27 +979,27 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
   // Copies: wave w moves row chunks R = w + 4i (i < 4) and, for w < 2, R = 16 + w; waves 2 and 3
   // copy the 32 token scales (each into its own slot, so that every wave issues 5 copies per
   // tile). Row chunk R, lane L fills LDS chunk 64R + L = row t, position pos: source chunk
-  // (pos & ~3) | ((pos & 3) ^ key8(t)) of row t. Offsets are < 2^16: two per register.
+  // (pos & ~3) | ((pos & 3) ^ key8(t)) of row t. One offset per register (unpacking two 16-bit
+  // offsets per register cost two VALU instructions per copy inside the score chain).
   // fp6: the packed rows are copied as they are (LDS chunk 64R + L from source chunk 64R + L):
   // wave w moves R = w + 4i (i < 3) and, for w < 2, R = 12 + w; waves 2 and 3 copy the scales, so
   // every wave issues 4 copies. The 32 lanes of R = 13 past the 864 chunks of the rows re-read the
   // last chunk into the slot's 512-byte pad.
-  uint32_t doff2[3] = {0u, 0u, 0u};
+  uint32_t doff[LOADS8];
 #pragma unroll
   for (int i = 0; i < LOADS8; ++i) {
+    doff[i] = 0u;
     if constexpr (FP6) {
       const int R = i < 3 ? w + 4 * i : 12 + w;
       if (R < 14) {
         const int f = 64 * R + lane;
-        const uint32_t o = (uint32_t)((f < 864 ? f : 863) << 4);
-        doff2[i >> 1] |= o << (16 * (i & 1));
+        doff[i] = (uint32_t)((f < 864 ? f : 863) << 4);
       }
     } else {
       const int R = i < 4 ? w + 4 * i : 16 + w;
       if (R < 18) {
         const int f = 64 * R + lane, t = f / f8::CH, pos = f - t * f8::CH;
-        const uint32_t o = (uint32_t)(t * RB + (((pos & ~3) | ((pos & 3) ^ key8(t))) << 4));
-        doff2[i >> 1] |= o << (16 * (i & 1));
+        doff[i] = (uint32_t)(t * RB + (((pos & ~3) | ((pos & 3) ^ key8(t))) << 4));
       }
     }
   }
@@ -1059,9 +1056,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_fp8(const uint8_t* __restrict
     constexpr int NROWCP = FP6 ? 3 : 4;  // row copies every wave issues; waves 0 and 1 add one more
     auto copy = [&](const CopyPlan& cp, int i, bool partial) __attribute__((always_inline)) {
       if (i < NROWCP || wu < 2) {
-        uint32_t d2 = doff2[i >> 1];
-        asm volatile("" : "+v"(d2));
-        uint32_t off = (i & 1) ? d2 >> 16 : d2 & 0xffffu;
+        uint32_t off = doff[i];
         if (partial && cp.last < TT - 1) {
           const int t = (int)(off / HRB);
           if (t > cp.last) off -= (uint32_t)(t - cp.last) * HRB;
